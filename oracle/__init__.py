@@ -1,0 +1,10 @@
+"""CPU oracle for the FP8 scaled matrix multiply.
+
+TEST INFRASTRUCTURE ONLY: imported by the test suite, the smoke check and the
+benchmark's CPU-baseline leg.  The GPU library and its Python binding never
+import it.
+"""
+from .fp8_scaled_mm_ref import (  # noqa: F401
+    PER_TENSOR, ROWWISE, e4m3fn_value, e4m3fn_decode_table, decode,
+    bf16_bits_to_f64, f64_to_bf16_rne, scaled_mm,
+)

@@ -1,0 +1,157 @@
+"""Plain CPU oracle for the FP8 (e4m3fn) scaled matrix multiply.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+benchmark's CPU-baseline leg may import this module.  The GPU library never
+calls it and shares no code with it.
+
+What it computes (the plain definition of the method):
+
+    out[m, n] = RNE_bf16( s[m, n] * sum_k dec(A[m, k]) * dec(B[n, k])  (+ bias[n]) )
+
+  * A is M x K and B is N x K, both e4m3fn codes with K fastest.  B is the
+    K x N column-major right operand of the pages ("TN"): the gist
+    "matmul_fp8.py", function `benchmark`, makes b column-major before the
+    call, and the row-wise kernel PR (pytorch #125204, Summary) supports only
+    TN and scales B along its fast dimension.
+  * s[m, n] = scale_a * scale_b (per-tensor, gist `matmul_fp8_kernel`, the
+    scalar scale branch) or scale_a[m] * scale_b[n] (row-wise, same kernel's
+    per-row branch; PR #125204 Summary: scale of x has length M, scale of y
+    length N).
+  * The products are accumulated in fp32 on the GPU (gist: the accumulator is
+    float32 and every `tl.dot` asks for float32 output); here they are
+    accumulated in fp64, which is exact (see `scaled_mm`).
+  * The scale multiplies the accumulated sum once, after the K loop, and the
+    result is cast to the output dtype (gist `matmul_fp8_kernel`, after the K
+    loop).  The bias is added after scaling, unscaled (PR #142045 Summary: the
+    plan is to apply scaling and bias as epilogues; reading: bias is not
+    multiplied by the scale).
+  * The bf16 cast is round-to-nearest-even, done once, directly from fp64.
+
+Every piece is pinned by tests against closed forms, brute force with exact
+rationals, invariants and torch's CPU casts (as an outside library).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+PER_TENSOR = 0
+ROWWISE = 1
+
+
+def e4m3fn_value(code: int) -> float:
+    """Closed-form value of one OCP float8 e4m3fn byte.
+
+    Bit layout s eeee mmm, exponent bias 7.  Exponent field 15 with mantissa
+    7 is NaN (there is no infinity); exponent field 0 is subnormal,
+    m * 2^-9; otherwise (1 + m/8) * 2^(e-7).  The largest finite magnitude is
+    448 (the gist quantises to torch.finfo(float8_e4m3fn).max, which is 448).
+    """
+    s = (code >> 7) & 1
+    e = (code >> 3) & 0xF
+    m = code & 0x7
+    sign = -1.0 if s else 1.0
+    if e == 0xF and m == 0x7:
+        return float("nan")
+    if e == 0:
+        return sign * m * 2.0 ** -9
+    return sign * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+
+
+def e4m3fn_decode_table() -> np.ndarray:
+    """fp64 value of every byte code 0..255."""
+    return np.array([e4m3fn_value(c) for c in range(256)], dtype=np.float64)
+
+
+_DECODE = e4m3fn_decode_table()
+
+
+def decode(codes: np.ndarray) -> np.ndarray:
+    return _DECODE[np.asarray(codes, dtype=np.uint8)]
+
+
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """A bf16 pattern is the top half of the fp32 pattern with the same value."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32).astype(np.float64)
+
+
+def f64_to_bf16_rne(y: np.ndarray) -> np.ndarray:
+    """Round fp64 values to bf16 (8 significant bits, exponent range of fp32)
+    with round-to-nearest, ties-to-even, in one step; return bit patterns.
+
+    For |y| in [2^e, 2^(e+1)) the bf16 spacing is 2^(e-7); below the smallest
+    normal 2^-126 the spacing stays 2^-133 (subnormals).  Dividing by the
+    spacing is exact (a power of two), np.rint rounds half to even, and the
+    multiply back is exact.  A result of 2^128 or more is an overflow to
+    infinity (that is where RNE sends values from (2 - 2^-8) * 2^127 up).
+    NaN becomes the quiet NaN 0x7FC0.
+    """
+    y = np.asarray(y, dtype=np.float64)
+    a = np.abs(y)
+    _, e = np.frexp(a)                     # a = f * 2^e with f in [0.5, 1)
+    exp = np.maximum(e.astype(np.int64) - 1, -126)
+    spacing = np.ldexp(1.0, exp - 7)
+    with np.errstate(over="ignore", invalid="ignore"):
+        r = np.rint(a / spacing) * spacing
+        r32 = r.astype(np.float32)          # exact below 2^128, inf at 2^128
+    bits = (r32.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+    bits = np.where(np.signbit(y), bits | np.uint16(0x8000), bits)
+    bits = np.where(np.isnan(y), np.uint16(0x7FC0), bits)
+    return bits.astype(np.uint16)
+
+
+def scaled_mm(a, b, scale_a, scale_b, bias=None, mode=PER_TENSOR, rows=None, cols=None):
+    """Reference result for out[rows][:, cols] (all rows/cols by default).
+
+    a: uint8 [M, K] codes; b: uint8 [N, K] codes; scale_a/scale_b: float32
+    arrays of length 1 (per-tensor) or M / N (row-wise); bias: uint16 [N] bf16
+    bits or None.
+
+    Returns a dict with
+      bits : uint16 [m, n]  the bf16 output
+      y    : float64 [m, n] the value before the bf16 rounding
+      acc  : float64 [m, n] sum_k dec(a) dec(b)          (exact)
+      mag  : float64 [m, n] sum_k |dec(a)| |dec(b)|      (exact)
+      s    : float64 [m, n] the scale applied to acc
+
+    Exactness of acc: every finite e4m3fn value is an integer multiple of
+    2^-9 with magnitude at most 448 = 229376 * 2^-9, so each product is an
+    integer multiple of 2^-18 below 2^36 units, and any partial sum over
+    K <= 2^16 terms stays below 2^52 units.  All of them are fp64 numbers, so
+    the fp64 sum is exact in any order; the matrix product below is just a
+    convenient way to form it.
+    """
+    a = np.asarray(a, dtype=np.uint8)
+    b = np.asarray(b, dtype=np.uint8)
+    if a.ndim != 2 or b.ndim != 2 or a.shape[1] != b.shape[1]:
+        raise ValueError("a must be M x K and b N x K")
+    M, K = a.shape
+    N = b.shape[0]
+    if K > 65536:
+        raise ValueError("exact fp64 accumulation is only argued for K <= 65536")
+    rows = np.arange(M) if rows is None else np.asarray(rows, dtype=np.int64)
+    cols = np.arange(N) if cols is None else np.asarray(cols, dtype=np.int64)
+
+    da = decode(a[rows])                     # [m, K]
+    db = decode(b[cols])                     # [n, K]
+    acc = da @ db.T
+    mag = np.abs(da) @ np.abs(db).T
+
+    sa = np.asarray(scale_a, dtype=np.float32).astype(np.float64).reshape(-1)
+    sb = np.asarray(scale_b, dtype=np.float32).astype(np.float64).reshape(-1)
+    if mode == PER_TENSOR:
+        if sa.size != 1 or sb.size != 1:
+            raise ValueError("per-tensor scales must have one element each")
+        s = np.full(acc.shape, sa[0] * sb[0])
+    elif mode == ROWWISE:
+        if sa.size != M or sb.size != N:
+            raise ValueError("row-wise scales must have M and N elements")
+        # The product of two fp32 numbers is exact in fp64.
+        s = sa[rows][:, None] * sb[cols][None, :]
+    else:
+        raise ValueError(f"unknown scaling mode {mode}")
+
+    y = s * acc
+    if bias is not None:
+        y = y + bf16_bits_to_f64(np.asarray(bias, dtype=np.uint16)[cols])[None, :]
+    return {"bits": f64_to_bf16_rne(y), "y": y, "acc": acc, "mag": mag, "s": s}

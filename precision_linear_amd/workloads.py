@@ -1,0 +1,196 @@
+"""Seeded synthetic inputs for the FP8 scaled matrix multiply.
+
+This module is the only code shared by the GPU path's tests/bench and the CPU
+oracle.  It draws random numbers and prepares operand bytes; it holds none of
+the multiply's arithmetic (no decoding, no accumulation, no scaling of
+products, no output rounding).  Conversions to bf16 and to float8_e4m3fn are
+done with torch's CPU casts, exactly as the input recipe of the gist
+"matmul_fp8.py" (a-r-r-o-w), functions `get_scale` and `benchmark`, prepares
+its operands: amax -> scale = amax / 448 -> x / scale -> clamp to +-448 ->
+cast to e4m3fn.  The clamp matters because torch's e4m3fn cast does not
+saturate (anything at or above 464 in magnitude becomes NaN).
+
+Layouts produced (all C-contiguous numpy arrays):
+  a        uint8  [M, K]   e4m3fn codes, K fastest
+  b        uint8  [N, K]   e4m3fn codes, K fastest (the "TN" layout: the
+                           K x N column-major operand of the pages, stored
+                           as its N x K transpose)
+  scale_a  float32 [1] (per-tensor) or [M] (row-wise)
+  scale_b  float32 [1] (per-tensor) or [N] (row-wise)
+  bias     uint16  [N] bf16 bit patterns, or None
+
+Seeds: numpy PCG64 streams keyed by SeedSequence([42, workload_id, tensor_id]);
+42 is the gist's seed (function `benchmark`).
+"""
+from __future__ import annotations
+
+import dataclasses
+import hashlib
+import zlib
+from typing import Optional
+
+import numpy as np
+
+PER_TENSOR = 0
+ROWWISE = 1
+MODE_NAMES = {PER_TENSOR: "per_tensor", ROWWISE: "rowwise"}
+E4M3_MAX = 448.0
+BASE_SEED = 42
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    M: int
+    N: int
+    K: int
+    mode: int            # PER_TENSOR or ROWWISE
+    recipe: str          # "normal", "skinny", "codes"
+    bias: bool = False
+
+    @property
+    def flops(self) -> int:
+        return 2 * self.M * self.N * self.K
+
+    @property
+    def algorithmic_bytes(self) -> int:
+        """Bytes the multiply must move at least once: both fp8 operands,
+        the fp32 scales, the bf16 bias and the bf16 output."""
+        sa = 4 * (self.M if self.mode == ROWWISE else 1)
+        sb = 4 * (self.N if self.mode == ROWWISE else 1)
+        bias = 2 * self.N if self.bias else 0
+        return self.M * self.K + self.N * self.K + sa + sb + bias + 2 * self.M * self.N
+
+
+def _wl(name, M, N, K, mode, recipe, bias=False):
+    return Workload(name, M, N, K, mode, recipe, bias)
+
+
+# The synthetic workloads: square shapes with N(0,1) inputs quantised by amax,
+# skinny inference shapes (activations N(0,1), weights N(0,0.02), bf16 bias),
+# and ragged shapes whose operands are raw e4m3fn codes.
+WORKLOADS = {w.name: w for w in [
+    _wl("sq256_pt", 256, 256, 256, PER_TENSOR, "normal"),
+    _wl("sq2048_rw", 2048, 2048, 2048, ROWWISE, "normal"),
+    _wl("sq8192_pt", 8192, 8192, 8192, PER_TENSOR, "normal"),
+    _wl("sq8192_rw", 8192, 8192, 8192, ROWWISE, "normal"),
+] + [
+    _wl(f"skinny_m{m}_k{k}_n{n}", m, n, k, ROWWISE, "skinny", True)
+    for (k, n) in ((8192, 28672), (28672, 8192)) for m in (16, 64, 128)
+] + [
+    _wl(f"ragged_{m}x{n}x{k}_{MODE_NAMES[mode]}", m, n, k, mode, "codes")
+    for (m, n, k) in ((4096, 4096, 32), (4095, 4097, 96), (8191, 1000, 4160),
+                      (16384, 16384, 8192))
+    for mode in (PER_TENSOR, ROWWISE)
+]}
+
+
+@dataclasses.dataclass
+class Inputs:
+    a: np.ndarray
+    b: np.ndarray
+    scale_a: np.ndarray
+    scale_b: np.ndarray
+    bias: Optional[np.ndarray]
+    mode: int
+
+    @property
+    def shape(self):
+        return self.a.shape[0], self.b.shape[0], self.a.shape[1]
+
+    def sha256(self) -> dict:
+        out = {}
+        for k in ("a", "b", "scale_a", "scale_b", "bias"):
+            v = getattr(self, k)
+            if v is not None:
+                out[k] = hashlib.sha256(np.ascontiguousarray(v).tobytes()).hexdigest()[:16]
+        return out
+
+
+def _rng(workload_key: int, tensor_id: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(
+        np.random.SeedSequence([BASE_SEED, workload_key, tensor_id])))
+
+
+def _torch():
+    import torch  # local import: torch is only a casting library here
+    return torch
+
+
+def _bf16_normal(rng, shape, std=1.0) -> np.ndarray:
+    """float32 N(0, std) draws passed through torch's bf16 cast; returned as
+    float32 holding bf16-representable values."""
+    torch = _torch()
+    x = rng.standard_normal(shape, dtype=np.float32)
+    if std != 1.0:
+        x *= np.float32(std)
+    return torch.from_numpy(x).to(torch.bfloat16).to(torch.float32).numpy()
+
+
+def _quantise(x: np.ndarray, rowwise: bool):
+    """amax/448 scale (whole tensor or per row of the K-fastest layout),
+    then x/scale clamped to +-448 and cast to e4m3fn by torch."""
+    torch = _torch()
+    t = torch.from_numpy(x)
+    if rowwise:
+        amax = t.abs().amax(dim=1)
+    else:
+        amax = t.abs().amax().reshape(1)
+    amax = torch.where(amax > 0, amax, torch.ones_like(amax))
+    scale = amax / torch.tensor(E4M3_MAX, dtype=torch.float32)
+    q = (t / (scale[:, None] if rowwise else scale)).clamp(-E4M3_MAX, E4M3_MAX)
+    codes = q.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    return np.ascontiguousarray(codes), scale.numpy().astype(np.float32)
+
+
+# The 254 byte codes of e4m3fn that are not NaN (0x7F and 0xFF are NaN).
+_NON_NAN_CODES = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+
+
+def _codes(rng, shape, zero_frac=0.01) -> np.ndarray:
+    idx = rng.integers(0, _NON_NAN_CODES.size, size=shape, dtype=np.int64)
+    c = _NON_NAN_CODES[idx]
+    c[rng.random(shape) < zero_frac] = 0
+    return np.ascontiguousarray(c)
+
+
+def _log_uniform_scales(rng, n) -> np.ndarray:
+    return np.exp2(rng.uniform(-8.0, 4.0, size=n)).astype(np.float32)
+
+
+def make_inputs(M: int, N: int, K: int, mode: int, recipe: str, bias: bool = False,
+                key: int = 0) -> Inputs:
+    """Seeded inputs for an (M, N, K) problem.  `key` selects the stream."""
+    rowwise = mode == ROWWISE
+    if recipe in ("normal", "skinny"):
+        a_f = _bf16_normal(_rng(key, 0), (M, K))
+        b_f = _bf16_normal(_rng(key, 1), (N, K), std=0.02 if recipe == "skinny" else 1.0)
+        a, sa = _quantise(a_f, rowwise)
+        b, sb = _quantise(b_f, rowwise)
+        del a_f, b_f
+    elif recipe == "codes":
+        a = _codes(_rng(key, 0), (M, K))
+        b = _codes(_rng(key, 1), (N, K))
+        sa = _log_uniform_scales(_rng(key, 2), M if rowwise else 1)
+        sb = _log_uniform_scales(_rng(key, 3), N if rowwise else 1)
+    else:
+        raise ValueError(f"unknown recipe {recipe!r}")
+    bias_bits = None
+    if bias:
+        bias_bits = _bf16_bits_normal(_rng(key, 4), N)
+    return Inputs(a, b, sa, sb, bias_bits, mode)
+
+
+def _bf16_bits_normal(rng, n) -> np.ndarray:
+    torch = _torch()
+    x = rng.standard_normal(n, dtype=np.float32)
+    return torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16).copy()
+
+
+def workload_key(name: str) -> int:
+    return zlib.crc32(name.encode()) & 0x7FFFFFFF
+
+
+def make_workload(name: str) -> Inputs:
+    w = WORKLOADS[name]
+    return make_inputs(w.M, w.N, w.K, w.mode, w.recipe, w.bias, key=workload_key(name))
