@@ -1,0 +1,217 @@
+"""Benchmark of the FP8 scaled GEMM on one MI355X.
+
+One step = the whole hot path on the headline workload: the M=N=K=8192
+e4m3fn multiply once with per-tensor scales and once with row-wise scales
+(inputs N(0,1) -> bf16 -> amax/448 quantised to e4m3fn, B stored N x K,
+bf16 out), both already resident in HBM.  `value` is FP8 TFLOP/s over the
+timed steps (2*M*N*K per multiply).
+
+The JSON line also carries
+  roofline      the GEMM kernel's own throughput (algorithmic flops per launch
+                over its average launch time, from HIP events on the launch
+                stream) against the dense-FP8 MFMA peak of MI355X;
+  cpu_baseline  the CPU oracle timed on a bounded sample (a block of output
+                rows of the same problem) on this host's cores;
+  secondary     the skinny inference shapes (row-wise + bias, HBM-bound) with
+                the MALL flushed before every launch, reported in HBM GB/s.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "FP8 scaled-GEMM TFLOP/s and % of dense-FP8 MFMA peak (per-tensor, row-wise)"
+PEAK_FP8_TFLOPS = 5000.0      # MI355X dense FP8 MFMA (no sparsity)
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+KERNEL_SRC = os.path.join(ROOT, "precision_linear_amd", "csrc", "fp8_scaled_mm.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_sq8192.json")
+
+
+def kernel_sha():
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def to_dev(x, dev):
+    import torch
+    if x is None:
+        return None
+    t = torch.from_numpy(np.ascontiguousarray(x))
+    if x.dtype == np.uint16:
+        t = t.view(torch.int16).view(torch.bfloat16)
+    return t.to(dev)
+
+
+class Problem:
+    def __init__(self, name, dev):
+        from precision_linear_amd import workloads as wl
+        self.name = name
+        self.w = wl.WORKLOADS[name]
+        self.inp = wl.make_workload(name)
+        i = self.inp
+        self.a, self.b = to_dev(i.a, dev), to_dev(i.b, dev)
+        self.sa, self.sb = to_dev(i.scale_a, dev), to_dev(i.scale_b, dev)
+        self.bias = to_dev(i.bias, dev)
+        import torch
+        self.out = torch.empty((self.w.M, self.w.N), dtype=torch.bfloat16, device=dev)
+
+    def launch(self):
+        from precision_linear_amd import binding
+        binding.fp8_scaled_mm(self.a, self.b, self.sa, self.sb, self.bias, out=self.out,
+                              mode=self.w.mode)
+
+
+def cpu_baseline(problem, target_s=12.0):
+    """The oracle, as it stands, on a block of output rows of the same problem."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max((d.get("num_threads", 1) for d in threadpool_info()
+                     if d.get("user_api") == "blas"), default=1)
+    except Exception:
+        cores = os.cpu_count() or 1
+    i = problem.inp
+    M, N, K = i.shape
+    rows = 16
+    while True:
+        t0 = time.perf_counter()
+        oracle.scaled_mm(i.a, i.b, i.scale_a, i.scale_b, i.bias, i.mode, rows=np.arange(rows))
+        dt = time.perf_counter() - t0
+        if dt * 4 > target_s or rows >= M:
+            break
+        rows = min(M, int(rows * max(2.0, min(8.0, target_s / max(dt, 1e-3) / 2))))
+    tflops = 2.0 * rows * N * K / dt / 1e12
+    return {"value": round(tflops, 6), "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{problem.name}: output rows 0..{rows - 1} of {M} (all {N} columns, "
+                      f"K={K}), fp64 exact accumulation + bf16 RNE, {dt:.1f} s"}
+
+
+def time_launches(problem, n, flush=None):
+    """Per-launch HIP events on the launch stream; returns durations in ms."""
+    import torch
+    evs = []
+    for _ in range(n):
+        if flush is not None:
+            flush.zero_()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        problem.launch()
+        e.record()
+        evs.append((s, e))
+    torch.cuda.synchronize()
+    return [s.elapsed_time(e) for s, e in evs]
+
+
+def skinny_results(dev, reps=20):
+    import torch
+    from precision_linear_amd import workloads as wl
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)   # > 256 MB MALL
+    res = []
+    for name in [n for n in wl.WORKLOADS if n.startswith("skinny")]:
+        p = Problem(name, dev)
+        time_launches(p, 3, flush)
+        ts = sorted(time_launches(p, reps, flush))
+        t50 = ts[len(ts) // 2] * 1e-3
+        gbs = p.w.algorithmic_bytes / t50 / 1e9
+        res.append({"workload": name, "M": p.w.M, "N": p.w.N, "K": p.w.K,
+                    "us_p50": round(t50 * 1e6, 2), "hbm_gbs": round(gbs, 1),
+                    "frac_hbm": round(gbs / PEAK_HBM_GBS, 4),
+                    "tflops": round(p.w.flops / t50 / 1e12, 1)})
+        del p
+        torch.cuda.empty_cache()
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-secondary", action="store_true", help="skip the skinny shapes")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the multiply shards by output columns with no exchange; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from precision_linear_amd import binding
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    binding.lib()
+    probs = [Problem("sq8192_pt", dev), Problem("sq8192_rw", dev)]
+    flops_step = sum(p.w.flops for p in probs)
+
+    for _ in range(args.warmup):
+        for p in probs:
+            p.launch()
+    torch.cuda.synchronize()
+
+    durations = {p.name: [] for p in probs}
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        for p in probs:
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record()
+            p.launch()
+            e.record()
+            durations[p.name].append((s, e))
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    elapsed = t1 - t0
+    per_kernel = {k: [s.elapsed_time(e) for s, e in v] for k, v in durations.items()}
+    avg_ms = {k: sum(v) / len(v) for k, v in per_kernel.items()}
+    all_ms = [x for v in per_kernel.values() for x in v]
+    kernel_avg_s = sum(all_ms) / len(all_ms) * 1e-3
+    achieved = probs[0].w.flops / kernel_avg_s / 1e12
+
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+        if tr.get("kernel_sha") == kernel_sha():
+            traffic = tr.get("bytes_per_launch")
+
+    value = flops_step * args.steps / elapsed / 1e12
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3fn x fp8_e4m3fn -> fp32 acc -> bf16",
+        "data": "synthetic (seeded N(0,1) -> bf16 -> amax/448 e4m3fn quantisation)",
+        "config": {"workload": "fp8_scaled_mm M=N=K=8192, per-tensor then row-wise, TN, bf16 out",
+                   "M": 8192, "N": 8192, "K": 8192, "modes": ["per_tensor", "rowwise"],
+                   "tile_config": binding.config_names()[binding.select_config(8192, 8192, 8192, 0)],
+                   "frac_of_peak": round(value / PEAK_FP8_TFLOPS, 4),
+                   "kernel_ms": {k: round(v, 4) for k, v in avg_ms.items()}},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP8_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP8_TFLOPS, 4),
+                     "traffic": traffic},
+    }
+    if not args.no_secondary:
+        line["secondary"] = skinny_results(dev)
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(probs[0])
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

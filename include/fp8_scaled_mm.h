@@ -1,0 +1,109 @@
+/*
+ * fp8_scaled_mm.h -- C ABI of the MI355X (gfx950) FP8 scaled matrix multiply.
+ *
+ * The operation (the scaled-mm semantics of the gist "matmul_fp8.py"
+ * (a-r-r-o-w), kernel `matmul_fp8_kernel`, and of pytorch PR #125204
+ * "rowwise scaling kernel", Summary):
+ *
+ *     out[m][n] = bf16_rne( s[m][n] * sum_{k<K} A[m][k] * B[n][k]  (+ bias[n]) )
+ *
+ *   A    M x K float8 e4m3fn (OCP), row-major, row stride K bytes.
+ *   B    N x K float8 e4m3fn, row-major, row stride K bytes.  This is the
+ *        "TN" right operand: the K x N column-major matrix of the pages,
+ *        handed over as its N x K transpose (PR #125204 Summary: only TN is
+ *        supported and the scale of B runs along its fast dimension).
+ *   s    FP8MM_PER_TENSOR: scale_a[0] * scale_b[0]   (one fp32 each)
+ *        FP8MM_ROWWISE:    scale_a[m] * scale_b[n]   (M and N fp32 values;
+ *        PR #125204 Summary: the scale of x has length M, that of y length N).
+ *        The product of the two scales is formed in fp32 in both modes.
+ *   The products are accumulated in fp32 (the gist's accumulator is fp32).
+ *   bias optional bf16 vector of length N, added after scaling and not
+ *        scaled (PR #142045 Summary: scaling and bias are to be applied as
+ *        epilogues).
+ *   out  M x N bf16, row-major, row stride N elements, rounded to nearest
+ *        even.  Every element is written; `out` is never read.
+ *
+ * Pointers: A, B, scale_a, scale_b, bias and out are DEVICE pointers on the
+ * current HIP device.  The library never dereferences them on the host, so
+ * scales may be produced by an earlier kernel on the same stream.  The
+ * caller owns every buffer; the library allocates nothing, keeps no pointer
+ * after the call returns and may be called from several host threads.
+ *
+ * Execution: asynchronous on `stream` (a hipStream_t; NULL = the default
+ * stream).  The call returns after the launch, without synchronising.
+ *
+ * Preconditions (checked on the host, before anything is enqueued):
+ *   - 0 <= M, N <= 2^31 - 1; 16 <= K <= 2^23 and K % 16 == 0 (whole 16-byte
+ *     row chunks: the pages' TMA path likewise needs K * itemsize to be a
+ *     multiple of 16, PR #142101 review discussion).  M == 0 or N == 0 is a
+ *     successful no-op that touches no pointer (any of them may be NULL).
+ *   - Otherwise A, B, scale_a, scale_b, out non-NULL; bias may be NULL.
+ *   - A and B 16-byte aligned; scales 4-byte aligned; bias and out 2-byte
+ *     aligned.  out must not overlap any input.
+ * Errors: the return value is FP8MM_OK (0) or one of the FP8MM_ERR_* codes;
+ * on a validation error nothing is enqueued and `out` is untouched.  A
+ * launch failure reported by the runtime gives FP8MM_ERR_LAUNCH.
+ */
+#ifndef FP8_SCALED_MM_H
+#define FP8_SCALED_MM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+struct ihipStream_t; /* hipStream_t is `struct ihipStream_t*` */
+
+enum fp8mm_scaling_mode {
+    FP8MM_PER_TENSOR = 0,
+    FP8MM_ROWWISE = 1
+};
+
+enum fp8mm_status {
+    FP8MM_OK = 0,
+    FP8MM_ERR_NULL = 1,    /* a required pointer is NULL */
+    FP8MM_ERR_SHAPE = 2,   /* M, N or K out of range, or K % 16 != 0 */
+    FP8MM_ERR_ALIGN = 3,   /* a pointer is not aligned as required */
+    FP8MM_ERR_MODE = 4,    /* unknown scaling_mode */
+    FP8MM_ERR_DEVICE = 5,  /* no usable HIP device, or not a gfx950 */
+    FP8MM_ERR_LAUNCH = 6,  /* the kernel launch failed */
+    FP8MM_ERR_CONFIG = 7   /* unknown tile configuration id */
+};
+
+/* The scaled multiply described above, with the tile configuration chosen
+ * from (M, N, K, scaling_mode, bias present). */
+int fp8_scaled_mm(const void* A, const void* B, const float* scale_a, const float* scale_b,
+                  const void* bias_or_null, void* out, int64_t M, int64_t N, int64_t K,
+                  int scaling_mode, struct ihipStream_t* stream);
+
+/* The same, with an explicit tile configuration (0 <= config_id <
+ * fp8_scaled_mm_num_configs()), or the automatic choice for config_id < 0.
+ * Every configuration computes the same function; they differ in speed. */
+int fp8_scaled_mm_with_config(const void* A, const void* B, const float* scale_a,
+                              const float* scale_b, const void* bias_or_null, void* out,
+                              int64_t M, int64_t N, int64_t K, int scaling_mode,
+                              struct ihipStream_t* stream, int config_id);
+
+/* Number of tile configurations compiled into the library. */
+int fp8_scaled_mm_num_configs(void);
+
+/* Static, NUL-terminated description of a configuration ("" if unknown). */
+const char* fp8_scaled_mm_config_name(int config_id);
+
+/* The configuration fp8_scaled_mm would use for this problem (pure host
+ * logic: no device access).  Returns -1 for an invalid problem. */
+int fp8_scaled_mm_select_config(int64_t M, int64_t N, int64_t K, int scaling_mode, int has_bias);
+
+/* Grid size (workgroups) a launch of `config_id` uses on a device with
+ * `num_cus` compute units for an M x N output (host logic only). */
+int64_t fp8_scaled_mm_grid_size(int config_id, int64_t M, int64_t N, int num_cus);
+
+/* Static, NUL-terminated text for a status code. */
+const char* fp8_scaled_mm_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8_SCALED_MM_H */

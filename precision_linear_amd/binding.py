@@ -1,0 +1,139 @@
+"""ctypes binding of libfp8_scaled_mm.so: argument marshalling only.
+
+Every step of the multiply runs in the HIP library; this module turns torch
+tensors into device pointers, sizes and the current stream, and turns
+status codes into exceptions.  A missing library is an error (there is no
+fallback path).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(HERE, "libfp8_scaled_mm.so")
+
+PER_TENSOR = 0
+ROWWISE = 1
+_MODES = {"per_tensor": PER_TENSOR, "tensorwise": PER_TENSOR, "rowwise": ROWWISE,
+          PER_TENSOR: PER_TENSOR, ROWWISE: ROWWISE}
+
+# status codes from include/fp8_scaled_mm.h
+OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_MODE, ERR_DEVICE, ERR_LAUNCH, ERR_CONFIG = range(8)
+_ARG_ERRORS = {ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_MODE, ERR_CONFIG}
+
+EXPORTS = ("fp8_scaled_mm", "fp8_scaled_mm_with_config", "fp8_scaled_mm_num_configs",
+           "fp8_scaled_mm_config_name", "fp8_scaled_mm_select_config",
+           "fp8_scaled_mm_grid_size", "fp8_scaled_mm_status_string")
+
+
+class Fp8MMError(RuntimeError):
+    def __init__(self, status: int):
+        self.status = status
+        super().__init__(f"fp8_scaled_mm failed: {status_string(status)} (status {status})")
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(library_path):
+            raise RuntimeError(
+                f"{library_path} is missing: build it with "
+                "`python -m precision_linear_amd.build` (there is no non-HIP fallback)")
+        L = ctypes.CDLL(library_path)
+        vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+        L.fp8_scaled_mm.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, vp]
+        L.fp8_scaled_mm.restype = i32
+        L.fp8_scaled_mm_with_config.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, vp, i32]
+        L.fp8_scaled_mm_with_config.restype = i32
+        L.fp8_scaled_mm_num_configs.argtypes = []
+        L.fp8_scaled_mm_num_configs.restype = i32
+        L.fp8_scaled_mm_config_name.argtypes = [i32]
+        L.fp8_scaled_mm_config_name.restype = ctypes.c_char_p
+        L.fp8_scaled_mm_select_config.argtypes = [i64, i64, i64, i32, i32]
+        L.fp8_scaled_mm_select_config.restype = i32
+        L.fp8_scaled_mm_grid_size.argtypes = [i32, i64, i64, i32]
+        L.fp8_scaled_mm_grid_size.restype = i64
+        L.fp8_scaled_mm_status_string.argtypes = [i32]
+        L.fp8_scaled_mm_status_string.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().fp8_scaled_mm_status_string(int(status)).decode()
+
+
+def config_names() -> list:
+    L = lib()
+    return [L.fp8_scaled_mm_config_name(i).decode() for i in range(L.fp8_scaled_mm_num_configs())]
+
+
+def select_config(M, N, K, mode, has_bias=False) -> int:
+    return int(lib().fp8_scaled_mm_select_config(M, N, K, _MODES[mode], int(bool(has_bias))))
+
+
+def _as_codes(t: torch.Tensor, name: str) -> torch.Tensor:
+    if t.dtype == torch.float8_e4m3fn:
+        return t.view(torch.uint8)
+    if t.dtype == torch.uint8:
+        return t
+    raise ValueError(f"{name} must be float8_e4m3fn (or uint8 codes), got {t.dtype}")
+
+
+def fp8_scaled_mm(a: torch.Tensor, b: torch.Tensor, scale_a: torch.Tensor, scale_b: torch.Tensor,
+                  bias: torch.Tensor | None = None, out: torch.Tensor | None = None,
+                  mode="per_tensor", config: int = -1) -> torch.Tensor:
+    """out = bf16(scale_a * scale_b * (a @ b^T) + bias) with a: M x K and b: N x K
+    (e4m3fn, K contiguous).  b may also be given as a K x N column-major view
+    (stride (1, K)), which is the same memory."""
+    if mode not in _MODES:
+        raise ValueError(f"mode must be 'per_tensor' or 'rowwise', got {mode!r}")
+    m = _MODES[mode]
+    a = _as_codes(a, "a")
+    b = _as_codes(b, "b")
+    if a.dim() != 2 or b.dim() != 2:
+        raise ValueError("a and b must be 2-D")
+    M, K = a.shape
+    if b.shape[1] == K and b.is_contiguous():
+        N = b.shape[0]
+    elif b.shape[0] == K and b.stride() == (1, K):
+        b = b.t()
+        N = b.shape[0]
+    else:
+        raise ValueError(f"b must be N x K contiguous or K x N column-major, got {tuple(b.shape)} "
+                         f"strides {b.stride()} for K={K}")
+    if not a.is_contiguous():
+        raise ValueError("a must be contiguous (row-major M x K)")
+    if not (a.is_cuda and b.is_cuda and scale_a.is_cuda and scale_b.is_cuda):
+        raise ValueError("all tensors must be on the GPU")
+    for name, s in (("scale_a", scale_a), ("scale_b", scale_b)):
+        if s.dtype != torch.float32 or not s.is_contiguous():
+            raise ValueError(f"{name} must be contiguous float32")
+    want_a, want_b = (1, 1) if m == PER_TENSOR else (M, N)
+    if scale_a.numel() != want_a or scale_b.numel() != want_b:
+        raise ValueError(f"{'per-tensor' if m == PER_TENSOR else 'row-wise'} scales need "
+                         f"{want_a} and {want_b} elements, got {scale_a.numel()} and {scale_b.numel()}")
+    if bias is not None:
+        if bias.dtype != torch.bfloat16 or bias.numel() != N or not bias.is_contiguous() or not bias.is_cuda:
+            raise ValueError("bias must be a contiguous bf16 GPU vector of length N")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
+    elif out.dtype != torch.bfloat16 or tuple(out.shape) != (M, N) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous bf16 M x N tensor")
+    stream = torch.cuda.current_stream(a.device).cuda_stream
+    with torch.cuda.device(a.device):
+        st = lib().fp8_scaled_mm_with_config(
+            a.data_ptr(), b.data_ptr(), scale_a.data_ptr(), scale_b.data_ptr(),
+            bias.data_ptr() if bias is not None else None, out.data_ptr(),
+            M, N, K, m, stream, int(config))
+    if st != OK:
+        if st in _ARG_ERRORS:
+            raise ValueError(f"fp8_scaled_mm: {status_string(st)} (status {st})")
+        raise Fp8MMError(st)
+    return out

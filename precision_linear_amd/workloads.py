@@ -19,8 +19,8 @@ Layouts produced (all C-contiguous numpy arrays):
   scale_b  float32 [1] (per-tensor) or [N] (row-wise)
   bias     uint16  [N] bf16 bit patterns, or None
 
-Seeds: numpy PCG64 streams keyed by SeedSequence([42, workload_id, tensor_id]);
-42 is the gist's seed (function `benchmark`).
+Seeds: numpy PCG64 streams keyed by SeedSequence([42, workload_id,
+tensor_id, row_block]); 42 is the gist's seed (function `benchmark`).
 """
 from __future__ import annotations
 
@@ -107,9 +107,27 @@ class Inputs:
         return out
 
 
-def _rng(workload_key: int, tensor_id: int) -> np.random.Generator:
-    return np.random.Generator(np.random.PCG64(
-        np.random.SeedSequence([BASE_SEED, workload_key, tensor_id])))
+def _rng(workload_key: int, tensor_id: int, block: int = -1) -> np.random.Generator:
+    key = [BASE_SEED, workload_key, tensor_id] + ([block] if block >= 0 else [])
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence(key)))
+
+
+def _blocked(shape, fill, nblk_max=64):
+    """Fill a 2-D array in row blocks, each from its own seeded stream (the
+    block layout depends on the shape only, so results do not depend on the
+    thread count)."""
+    from concurrent.futures import ThreadPoolExecutor
+    rows = shape[0]
+    nblk = max(1, min(nblk_max, rows))
+    bounds = [rows * i // nblk for i in range(nblk + 1)]
+    out = [None] * nblk
+
+    def job(i):
+        out[i] = fill(i, (bounds[i + 1] - bounds[i],) + tuple(shape[1:]))
+
+    with ThreadPoolExecutor(max_workers=min(8, nblk)) as ex:
+        list(ex.map(job, range(nblk)))
+    return np.ascontiguousarray(np.concatenate(out, axis=0))
 
 
 def _torch():
@@ -117,11 +135,11 @@ def _torch():
     return torch
 
 
-def _bf16_normal(rng, shape, std=1.0) -> np.ndarray:
+def _bf16_normal(key, tensor_id, shape, std=1.0) -> np.ndarray:
     """float32 N(0, std) draws passed through torch's bf16 cast; returned as
     float32 holding bf16-representable values."""
     torch = _torch()
-    x = rng.standard_normal(shape, dtype=np.float32)
+    x = _blocked(shape, lambda i, shp: _rng(key, tensor_id, i).standard_normal(shp, dtype=np.float32))
     if std != 1.0:
         x *= np.float32(std)
     return torch.from_numpy(x).to(torch.bfloat16).to(torch.float32).numpy()
@@ -147,11 +165,13 @@ def _quantise(x: np.ndarray, rowwise: bool):
 _NON_NAN_CODES = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
 
 
-def _codes(rng, shape, zero_frac=0.01) -> np.ndarray:
-    idx = rng.integers(0, _NON_NAN_CODES.size, size=shape, dtype=np.int64)
-    c = _NON_NAN_CODES[idx]
-    c[rng.random(shape) < zero_frac] = 0
-    return np.ascontiguousarray(c)
+def _codes(key, tensor_id, shape, zero_frac=0.01) -> np.ndarray:
+    def fill(i, shp):
+        rng = _rng(key, tensor_id, i)
+        c = _NON_NAN_CODES[rng.integers(0, _NON_NAN_CODES.size, size=shp, dtype=np.int64)]
+        c[rng.random(shp, dtype=np.float32) < zero_frac] = 0
+        return c
+    return _blocked(shape, fill)
 
 
 def _log_uniform_scales(rng, n) -> np.ndarray:
@@ -163,14 +183,14 @@ def make_inputs(M: int, N: int, K: int, mode: int, recipe: str, bias: bool = Fal
     """Seeded inputs for an (M, N, K) problem.  `key` selects the stream."""
     rowwise = mode == ROWWISE
     if recipe in ("normal", "skinny"):
-        a_f = _bf16_normal(_rng(key, 0), (M, K))
-        b_f = _bf16_normal(_rng(key, 1), (N, K), std=0.02 if recipe == "skinny" else 1.0)
+        a_f = _bf16_normal(key, 0, (M, K))
+        b_f = _bf16_normal(key, 1, (N, K), std=0.02 if recipe == "skinny" else 1.0)
         a, sa = _quantise(a_f, rowwise)
         b, sb = _quantise(b_f, rowwise)
         del a_f, b_f
     elif recipe == "codes":
-        a = _codes(_rng(key, 0), (M, K))
-        b = _codes(_rng(key, 1), (N, K))
+        a = _codes(key, 0, (M, K))
+        b = _codes(key, 1, (N, K))
         sa = _log_uniform_scales(_rng(key, 2), M if rowwise else 1)
         sb = _log_uniform_scales(_rng(key, 3), N if rowwise else 1)
     else:

@@ -1,0 +1,118 @@
+"""Host-side checks of the C ABI: the library loads without a GPU, exports
+every function the header declares, and rejects bad arguments before
+touching the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from precision_linear_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp8_scaled_mm.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(binding.library_path):
+        from precision_linear_amd import build
+        build.build()
+    return binding.lib()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fp8_scaled_mm\w*)\s*\(", text)))
+
+
+def test_exports_every_declared_function(L):
+    names = _declared_functions()
+    assert len(names) >= 7
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(binding.EXPORTS)
+
+
+def test_status_strings(L):
+    for s in range(8):
+        assert binding.status_string(s)
+    assert binding.status_string(99) == "unknown status"
+
+
+def test_configs_listed(L):
+    names = binding.config_names()
+    assert len(names) >= 3 and all(names)
+    assert L.fp8_scaled_mm_config_name(len(names)) == b""
+    assert L.fp8_scaled_mm_config_name(-1) == b""
+
+
+P = 0x10000          # a 64 KiB-aligned fake device address, never dereferenced
+
+
+def call(L, A=P, B=P, sa=P, sb=P, bias=None, out=P, M=64, N=64, K=64, mode=0, cfg=-1):
+    return L.fp8_scaled_mm_with_config(A, B, sa, sb, bias, out, M, N, K, mode, None, cfg)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(A=None), binding.ERR_NULL), (dict(B=None), binding.ERR_NULL),
+    (dict(sa=None), binding.ERR_NULL), (dict(sb=None), binding.ERR_NULL),
+    (dict(out=None), binding.ERR_NULL),
+    (dict(mode=2), binding.ERR_MODE), (dict(mode=-1), binding.ERR_MODE),
+    (dict(M=-1), binding.ERR_SHAPE), (dict(N=-5), binding.ERR_SHAPE),
+    (dict(M=2 ** 31), binding.ERR_SHAPE), (dict(K=8), binding.ERR_SHAPE),
+    (dict(K=0), binding.ERR_SHAPE), (dict(K=40), binding.ERR_SHAPE),
+    (dict(K=2 ** 23 + 16), binding.ERR_SHAPE),
+    (dict(A=P + 8), binding.ERR_ALIGN), (dict(B=P + 4), binding.ERR_ALIGN),
+    (dict(sa=P + 2), binding.ERR_ALIGN), (dict(sb=P + 1), binding.ERR_ALIGN),
+    (dict(out=P + 1), binding.ERR_ALIGN), (dict(bias=P + 1), binding.ERR_ALIGN),
+    (dict(cfg=10 ** 6), binding.ERR_CONFIG),
+])
+def test_validation_errors(L, kw, code):
+    assert call(L, **kw) == code
+
+
+def test_empty_output_is_a_noop(L):
+    # M == 0 or N == 0 returns before any device call
+    assert call(L, M=0) == binding.OK
+    assert call(L, N=0) == binding.OK
+    assert call(L, A=None, B=None, sa=None, sb=None, out=None, M=0) == binding.OK
+    assert call(L, M=0, K=24) == binding.ERR_SHAPE
+
+
+def test_no_device_reported():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present: this case would launch on fake pointers")
+    L = binding.lib()
+    assert call(L) == binding.ERR_DEVICE
+
+
+def test_select_config_host_logic(L):
+    n = L.fp8_scaled_mm_num_configs()
+    for shape in [(8192, 8192, 8192), (2048, 2048, 2048), (256, 256, 256), (16, 28672, 8192),
+                  (64, 8192, 28672), (128, 28672, 8192), (4095, 4097, 96), (1, 1, 16)]:
+        for mode in (0, 1):
+            c = L.fp8_scaled_mm_select_config(*shape, mode, 1)
+            assert 0 <= c < n
+    assert L.fp8_scaled_mm_select_config(16, 16, 16, 3, 0) == -1
+    assert L.fp8_scaled_mm_select_config(16, 16, 24, 0, 0) == -1
+
+
+def test_grid_size_is_persistent(L):
+    n = L.fp8_scaled_mm_num_configs()
+    for c in range(n):
+        g = L.fp8_scaled_mm_grid_size(c, 8192, 8192, 256)
+        assert 1 <= g <= 256
+        assert L.fp8_scaled_mm_grid_size(c, 1, 1, 256) == 1
+    assert L.fp8_scaled_mm_grid_size(0, 0, 5, 256) == 0
+
+
+def test_python_binding_rejects_bad_tensors():
+    import torch
+    a = torch.zeros(4, 32, dtype=torch.float32)
+    with pytest.raises(ValueError):
+        binding.fp8_scaled_mm(a, a, a, a)
+    with pytest.raises(ValueError):
+        binding.fp8_scaled_mm(a, a, a, a, mode="columnwise")

@@ -1,0 +1,238 @@
+"""GPU parity: the HIP library against the CPU oracle, element by element,
+on seeded inputs, through the C ABI (via the thin ctypes binding).
+
+Small and ragged shapes are compared in full; the full-size workloads are
+compared on sampled rows and columns that the oracle computes one by one.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from precision_linear_amd import binding
+from precision_linear_amd import workloads as wl
+from parity import bf16_bits_to_f64, compare
+
+pytestmark = pytest.mark.gpu
+PT, RW = wl.PER_TENSOR, wl.ROWWISE
+DEV = "cuda:0"
+
+
+def _to_dev(x):
+    if x is None:
+        return None
+    t = torch.from_numpy(np.ascontiguousarray(x))
+    if x.dtype == np.uint16:
+        t = t.view(torch.int16).view(torch.bfloat16)
+    return t.to(DEV)
+
+
+def run_gpu(inp, config=-1, out=None):
+    a, b = _to_dev(inp.a), _to_dev(inp.b)
+    sa, sb = _to_dev(inp.scale_a), _to_dev(inp.scale_b)
+    bias = _to_dev(inp.bias)
+    out = binding.fp8_scaled_mm(a, b, sa, sb, bias, out=out, mode=inp.mode, config=config)
+    torch.cuda.synchronize()
+    return out
+
+
+def out_bits(t):
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def check_full(inp, config=-1):
+    print(f"[parity] shape={inp.shape} mode={inp.mode} bias={inp.bias is not None} "
+          f"config={config}", flush=True)
+    got = out_bits(run_gpu(inp, config))
+    ref = oracle.scaled_mm(inp.a, inp.b, inp.scale_a, inp.scale_b, inp.bias, inp.mode)
+    nbad, worst, first = compare(got, ref)
+    assert nbad == 0, f"{nbad} elements out of bound, worst ratio {worst:.3g}, first {first}"
+    return got, ref
+
+
+def check_sampled(inp, out, n_rows=24, n_cols=24, seed=0):
+    """Compare whole sampled rows and whole sampled columns (every tile of the
+    grid is hit by both), including the first and last of each."""
+    M, N, K = inp.shape
+    rng = np.random.Generator(np.random.PCG64(seed))
+    rows = np.unique(np.concatenate([[0, M - 1], rng.integers(0, M, n_rows)]))
+    cols = np.unique(np.concatenate([[0, N - 1], rng.integers(0, N, n_cols)]))
+    rows_t = torch.from_numpy(rows).to(out.device)
+    cols_t = torch.from_numpy(cols).to(out.device)
+    g_rows = out_bits(out.index_select(0, rows_t))
+    g_cols = out_bits(out.index_select(1, cols_t))
+    r_rows = oracle.scaled_mm(inp.a, inp.b, inp.scale_a, inp.scale_b, inp.bias, inp.mode, rows=rows)
+    r_cols = oracle.scaled_mm(inp.a, inp.b, inp.scale_a, inp.scale_b, inp.bias, inp.mode, cols=cols)
+    for g, r, what in ((g_rows, r_rows, "rows"), (g_cols, r_cols, "cols")):
+        nbad, worst, first = compare(g, r)
+        assert nbad == 0, f"{what}: {nbad} out of bound, worst {worst:.3g}, first {first}"
+
+
+# ------------------------------------------------------------ small / ragged ---
+
+SMALL_SHAPES = [
+    (1, 1, 16), (1, 7, 32), (5, 1, 48), (32, 32, 64), (64, 64, 128),
+    (100, 70, 160), (257, 129, 272), (300, 513, 256), (128, 96, 4096 + 48),
+    (513, 260, 96), (33, 1000, 528),
+]
+
+
+@pytest.mark.parametrize("mode", [PT, RW])
+@pytest.mark.parametrize("shape", SMALL_SHAPES)
+def test_small_shapes_auto_config(shape, mode):
+    M, N, K = shape
+    inp = wl.make_inputs(M, N, K, mode, "codes", bias=(M + N) % 2 == 0, key=M * 7 + N * 13 + K)
+    check_full(inp)
+
+
+def _configs():
+    return list(range(len(binding.config_names())))
+
+
+@pytest.mark.parametrize("config", _configs())
+@pytest.mark.parametrize("mode", [PT, RW])
+@pytest.mark.parametrize("bias", [False, True])
+@pytest.mark.parametrize("shape", [(300, 200, 160), (257, 515, 400), (64, 128, 1024), (16, 300, 2080)])
+def test_every_config_ragged(config, mode, bias, shape):
+    M, N, K = shape
+    inp = wl.make_inputs(M, N, K, mode, "codes", bias=bias, key=config * 101 + M + N + K)
+    check_full(inp, config)
+
+
+@pytest.mark.parametrize("recipe", ["normal", "skinny"])
+def test_normal_inputs_small(recipe):
+    inp = wl.make_inputs(192, 320, 512, RW, recipe, bias=recipe == "skinny", key=77)
+    check_full(inp)
+
+
+# ------------------------------------------------------- bitwise invariants ---
+
+def _small(mode=PT, bias=False, key=5, shape=(130, 200, 288)):
+    return wl.make_inputs(*shape, mode, "codes", bias=bias, key=key)
+
+
+def test_deterministic():
+    inp = _small(RW, True)
+    a = out_bits(run_gpu(inp))
+    b = out_bits(run_gpu(inp))
+    assert np.array_equal(a, b)
+
+
+def test_power_of_two_scale_is_exact():
+    inp = _small(PT)
+    base = bf16_bits_to_f64(out_bits(run_gpu(inp)))
+    inp.scale_a = (inp.scale_a * np.float32(8.0)).astype(np.float32)
+    scaled = bf16_bits_to_f64(out_bits(run_gpu(inp)))
+    ok = np.abs(base) > 2.0 ** -120
+    assert np.array_equal(scaled[ok], 8.0 * base[ok])
+
+
+def test_rowwise_constant_equals_per_tensor_bitwise():
+    inp = _small(PT, True)
+    pt = out_bits(run_gpu(inp))
+    M, N, _ = inp.shape
+    inp_rw = wl.Inputs(inp.a, inp.b, np.repeat(inp.scale_a, M), np.repeat(inp.scale_b, N),
+                       inp.bias, RW)
+    rw = out_bits(run_gpu(inp_rw))
+    assert np.array_equal(pt, rw)
+
+
+def test_sign_flip_negates_bitwise():
+    inp = _small(RW)
+    a = out_bits(run_gpu(inp))
+    inp_neg = wl.Inputs(inp.a ^ np.uint8(0x80), inp.b, inp.scale_a, inp.scale_b, None, RW)
+    b = out_bits(run_gpu(inp_neg))
+    nz = (a & 0x7FFF) != 0
+    assert np.array_equal(b[nz], a[nz] ^ np.uint16(0x8000))
+
+
+def test_zero_k_padding_bitwise():
+    inp = _small(RW, True, shape=(96, 80, 96))
+    a = out_bits(run_gpu(inp))
+    M, N, K = inp.shape
+    pad = 160
+    inp_p = wl.Inputs(np.concatenate([inp.a, np.zeros((M, pad), np.uint8)], 1),
+                      np.concatenate([inp.b, np.zeros((N, pad), np.uint8)], 1),
+                      inp.scale_a, inp.scale_b, inp.bias, RW)
+    b = out_bits(run_gpu(inp_p))
+    assert np.array_equal(a, b)
+
+
+def test_identity_is_exact():
+    K = 256
+    a = np.zeros((K, K), np.uint8)
+    a[np.arange(K), np.arange(K)] = 0x38
+    bsrc = _small(PT, shape=(8, 200, K))
+    inp = wl.Inputs(a, bsrc.b, np.array([0.5], np.float32), np.array([4.0], np.float32), None, PT)
+    got = out_bits(run_gpu(inp))
+    dec = torch.from_numpy(bsrc.b.copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    want = oracle.f64_to_bf16_rne(2.0 * dec.T)
+    want = np.where(want == 0x8000, np.uint16(0), want)
+    got = np.where(got == 0x8000, np.uint16(0), got)
+    assert np.array_equal(got, want)
+
+
+def test_every_element_written():
+    inp = _small(RW, True, shape=(259, 131, 64))
+    M, N, _ = inp.shape
+    out = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=DEV)
+    run_gpu(inp, out=out)
+    assert not torch.isnan(out).any()
+
+
+def test_empty_is_noop():
+    inp = _small(PT, shape=(16, 16, 32))
+    a, b = _to_dev(inp.a), _to_dev(inp.b)
+    sa, sb = _to_dev(inp.scale_a), _to_dev(inp.scale_b)
+    out = torch.full((0, 16), 1.0, dtype=torch.bfloat16, device=DEV)
+    binding.fp8_scaled_mm(a[:0], b, sa, sb, out=out)
+    torch.cuda.synchronize()
+
+
+def test_unaligned_output_rows_fall_back():
+    """N odd and an output base that is only 2-byte aligned: the kernel must
+    not use its 8-byte stores."""
+    inp = _small(RW, True, shape=(70, 131, 128))
+    M, N, _ = inp.shape
+    buf = torch.full((M * N + 1,), float("nan"), dtype=torch.bfloat16, device=DEV)
+    out = buf[1:].view(M, N)
+    run_gpu(inp, out=out)
+    ref = oracle.scaled_mm(inp.a, inp.b, inp.scale_a, inp.scale_b, inp.bias, RW)
+    nbad, worst, first = compare(out_bits(out), ref)
+    assert nbad == 0, (nbad, worst, first)
+
+
+def test_column_major_b_view():
+    inp = _small(PT, shape=(64, 96, 128))
+    a, b = _to_dev(inp.a), _to_dev(inp.b)
+    b_kn = b.t()                                   # K x N, stride (1, K)
+    sa, sb = _to_dev(inp.scale_a), _to_dev(inp.scale_b)
+    o1 = binding.fp8_scaled_mm(a, b, sa, sb)
+    o2 = binding.fp8_scaled_mm(a, b_kn, sa, sb)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+
+
+# ------------------------------------------- full-size workloads (sampled) ---
+
+@pytest.mark.parametrize("name", [n for n in wl.WORKLOADS if not n.startswith("ragged_16384")])
+def test_workload(name):
+    inp = wl.make_workload(name)
+    print(f"[parity] workload {name} shape={inp.shape}", flush=True)
+    out = run_gpu(inp)
+    M, N, K = inp.shape
+    if M * N * K <= 2048 ** 3:
+        ref = oracle.scaled_mm(inp.a, inp.b, inp.scale_a, inp.scale_b, inp.bias, inp.mode)
+        nbad, worst, first = compare(out_bits(out), ref)
+        assert nbad == 0, (nbad, worst, first)
+    else:
+        check_sampled(inp, out)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name", [n for n in wl.WORKLOADS if n.startswith("ragged_16384")])
+def test_workload_largest(name):
+    inp = wl.make_workload(name)
+    print(f"[parity] workload {name} shape={inp.shape}", flush=True)
+    out = run_gpu(inp)
+    check_sampled(inp, out, n_rows=8, n_cols=8)
