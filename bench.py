@@ -136,6 +136,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-secondary", action="store_true", help="skip the skinny shapes")
+    ap.add_argument("--profile-gemm", type=int, default=0, metavar="N",
+                    help="only launch the M=N=K=8192 per-tensor multiply N times (counter runs)")
+    ap.add_argument("--profile-copy-mib", type=int, default=0, metavar="MIB",
+                    help="only run one device-to-device copy of MIB MiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -149,6 +153,21 @@ def main():
     dev = "cuda:0"
     torch.cuda.set_device(0)
     binding.lib()
+    if args.profile_copy_mib:
+        src = torch.ones(args.profile_copy_mib << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": src.numel()}))
+        return
+    if args.profile_gemm:
+        p = Problem("sq8192_pt", dev)
+        for _ in range(args.profile_gemm):
+            p.launch()
+        torch.cuda.synchronize()
+        print(json.dumps({"launches": args.profile_gemm, "workload": p.name}))
+        return
     probs = [Problem("sq8192_pt", dev), Problem("sq8192_rw", dev)]
     flops_step = sum(p.w.flops for p in probs)
 

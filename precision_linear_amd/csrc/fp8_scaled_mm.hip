@@ -67,12 +67,16 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
     return u >> 16;
 }
 
+// Position of 16-byte chunk c of LDS row r is c ^ chunk_swizzle(r).  The MFMA
+// operand reads have 8 (or 16) consecutive lanes read the same logical chunk
+// of 8 (16) consecutive rows; the mask makes those land in distinct banks
+// whether the LDS serves 128 or 256 bytes per cycle.  It uses row bits 0..3
+// only, so every 16-row-aligned block of rows shares one pattern.
 template <int CPR>
 __device__ __forceinline__ int chunk_swizzle(int r) {
-    // CPR = 16-byte chunks per LDS row (a power of two).  Consecutive rows get
-    // distinct XOR masks over every aligned run of CPR rows.
-    constexpr int LOG = CPR == 4 ? 2 : CPR == 8 ? 3 : CPR == 16 ? 4 : 5;
-    return (r ^ (r >> LOG)) & (CPR - 1);
+    if constexpr (CPR == 4) return ((r >> 1) ^ (r >> 2)) & 3;   // 4 rows per 256 B
+    if constexpr (CPR == 8) return (r & 7) ^ ((r >> 3) & 1);    // 2 rows per 256 B
+    return r & 15;                                              // >= 256-byte rows
 }
 
 template <int MI>
@@ -123,14 +127,25 @@ struct Cfg {
     static constexpr int A_BYTES = BM * BK;
     static constexpr int B_BYTES = BN * BK;
     static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
-    static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
+    static constexpr int MAIN_BYTES = STAGES * STAGE_BYTES;
+    // Epilogue parameters of the current tile: BM row scales, BN column
+    // scales (fp32) and BN bias values (bf16).
+    static constexpr int EPI_BYTES = BM * 4 + BN * 4 + BN * 2;
+    static constexpr int LDS_BYTES = MAIN_BYTES + ((EPI_BYTES + 15) / 16) * 16;
+    static constexpr int NSA = (BM + THREADS - 1) / THREADS;   // staged per thread
+    static constexpr int NSB = (BN + THREADS - 1) / THREADS;
     static constexpr int A_BLOCKS = A_BYTES / 1024;  // 1 KiB = one wave-wide 16-byte load
     static constexpr int B_BLOCKS = B_BYTES / 1024;
     static constexpr int A_LOADS = A_BLOCKS / WAVES; // per wave per stage
     static constexpr int B_LOADS = B_BLOCKS / WAVES;
     static constexpr int LOADS = A_LOADS + B_LOADS;
     static constexpr int KSTEP = Mfma<MI>::KSTEP;
+    static constexpr int NKS = BK / KSTEP;        // MFMA K steps per stage
+    static constexpr int MI_ = MI;
+    static constexpr int BK_ = BK;
+    static constexpr int STAGES_ = STAGES;
     static_assert(WTM % MI == 0 && WTN % MI == 0, "wave tile must hold whole MFMA tiles");
+    static_assert(MI % 16 == 0, "fragment row blocks must be 16-row aligned for the swizzle");
     static_assert(BK % KSTEP == 0, "BK must be a multiple of the MFMA K step");
     static_assert(CPR == 4 || CPR == 8 || CPR == 16 || CPR == 32, "BK must be 64..512");
     static_assert(A_BLOCKS % WAVES == 0 && B_BLOCKS % WAVES == 0, "loads must split evenly");
@@ -145,8 +160,12 @@ __device__ __forceinline__ void load_stage(uint8_t* lds_stage, __amdgpu_buffer_r
                                            __amdgpu_buffer_rsrc_t rb, int K, int k0, int wave,
                                            int lane) {
     constexpr int RPB = 1024 / (C::CPR * 16);    // LDS rows per 1 KiB block
-    const int rr = lane / C::CPR;
-    const int pos = lane % C::CPR;
+    // The lane-dependent offsets are cheap to recompute; keeping them live
+    // across the K loop would only cost registers the MFMA pipeline needs.
+    int l = lane;
+    asm volatile("" : "+v"(l));
+    const int rr = l / C::CPR;
+    const int pos = l % C::CPR;
 #pragma unroll
     for (int i = 0; i < C::A_LOADS; ++i) {
         const int blk = wave + i * C::WAVES;
@@ -169,12 +188,13 @@ __device__ __forceinline__ void load_stage(uint8_t* lds_stage, __amdgpu_buffer_r
     }
 }
 
-// 32 operand bytes for one MFMA: row `r` of an LDS operand tile, logical
-// chunks c0 and c0+1.
+// 32 operand bytes for one MFMA: row base + l of an LDS operand tile
+// (base a multiple of 16, so the swizzle depends on l only), logical chunks c0
+// and c0+1.
 template <int CPR>
-__device__ __forceinline__ v8i read_frag(const uint8_t* tile, int r, int c0) {
-    const int sw = chunk_swizzle<CPR>(r);
-    const uint8_t* row = tile + r * (CPR * 16);
+__device__ __forceinline__ v8i read_frag(const uint8_t* tile, int base, int l, int c0) {
+    const int sw = chunk_swizzle<CPR>(l);
+    const uint8_t* row = tile + (base + l) * (CPR * 16);
     v4i lo = *reinterpret_cast<const v4i*>(row + ((c0 ^ sw) << 4));
     v4i hi = *reinterpret_cast<const v4i*>(row + (((c0 + 1) ^ sw) << 4));
     v8i f;
@@ -190,12 +210,76 @@ __device__ __forceinline__ void barrier_lds() {
     __builtin_amdgcn_s_barrier();
 }
 
+// Operand fragments of K step `ks` of one stage for this wave: FM row blocks
+// of A and FN row blocks of B.  Lanes 0..MI-1 take rows, the lane group
+// (lane / MI) takes chunk pair 2*(lane/MI) of the step (for MI=32 lanes
+// 32..63 take chunks 2,3; for MI=16 four lane groups take pairs 0..3).  A and
+// B use the same lane -> k assignment, which is all the MFMA contraction needs.
+template <class C>
+__device__ __forceinline__ void read_frags(v8i (&fa)[C::FM], v8i (&fb)[C::FN], const uint8_t* st,
+                                           int ks, int wm, int wn, int lane) {
+    constexpr int MI = C::MI_;
+    const int c0 = ks * (C::KSTEP / 16) + (lane / MI) * 2;
+    const int l = lane % MI;
+#pragma unroll
+    for (int j = 0; j < C::FM; ++j)
+        fa[j] = read_frag<C::CPR>(st, wm * C::WTM + j * MI, l, c0);
+#pragma unroll
+    for (int i = 0; i < C::FN; ++i)
+        fb[i] = read_frag<C::CPR>(st + C::A_BYTES, wn * C::WTN + i * MI, l, c0);
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
     // s_waitcnt encoding on gfx9: vmcnt low bits [3:0], high bits [15:14];
     // expcnt [6:4] and lgkmcnt [11:8] left at their maxima (no wait).
     static_assert(N >= 0 && N <= 63, "vmcnt range");
     __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// One K stage (BK bytes of K) of the software pipeline.  The fragments of
+// the stage's first K step are already in buffer CUR0.  Each step first
+// issues the LDS reads of the next step into the other buffer, then the MFMAs
+// of this step.  At the last step, if another stage follows (HAS_NEXT), the
+// wave waits for its own loads of that stage, joins the barrier (after which
+// every wave's reads of this stage are done and every wave's loads of the next
+// stage have landed), refills this stage's buffer with the slice STAGES ahead,
+// and reads the next stage's first fragments.
+template <class C, int CUR0, bool HAS_NEXT>
+__device__ __forceinline__ void run_stage(typename Mfma<C::MI_>::acc_t (&acc)[C::FN][C::FM],
+                                          v8i (&fa)[2][C::FM], v8i (&fb)[2][C::FN], uint8_t* smem,
+                                          int kt, int k_iters, __amdgpu_buffer_rsrc_t ra,
+                                          __amdgpu_buffer_rsrc_t rb, int K, int wave, int wm, int wn,
+                                          int lane) {
+    using F = Mfma<C::MI_>;
+    constexpr int S = C::STAGES_;
+    const uint8_t* st = smem + (kt % S) * C::STAGE_BYTES;
+#pragma unroll
+    for (int ks = 0; ks < C::NKS; ++ks) {
+        const int cur = (CUR0 + ks) & 1;
+        if (ks + 1 < C::NKS) {
+            read_frags<C>(fa[cur ^ 1], fb[cur ^ 1], st, ks + 1, wm, wn, lane);
+        } else if (HAS_NEXT) {
+            // Loads issued so far cover slices 0 .. min(kt+S-1, k_iters-1);
+            // slice kt+1 has landed once the S-2 newest slices remain.
+            if (kt + S - 1 < k_iters) wait_vmcnt<C::LOADS * (S - 2)>();
+            else wait_vmcnt<0>();
+            barrier_lds();
+            if (kt + S < k_iters)
+                load_stage<C>(smem + (kt % S) * C::STAGE_BYTES, ra, rb, K, (kt + S) * C::BK_, wave,
+                              lane);
+            read_frags<C>(fa[cur ^ 1], fb[cur ^ 1], smem + ((kt + 1) % S) * C::STAGE_BYTES, 0, wm,
+                          wn, lane);
+        }
+        // Keep the compiler from sinking the LDS reads below the MFMAs: they
+        // must be in flight while the MFMAs of this step run.
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < C::FN; ++i)
+#pragma unroll
+            for (int j = 0; j < C::FM; ++j) acc[i][j] = F::run(fb[cur][i], fa[cur][j], acc[i][j]);
+        __builtin_amdgcn_sched_barrier(0);
+    }
 }
 
 template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int STAGES, int MI, int GROUP_M>
@@ -217,6 +301,10 @@ fp8_gemm_kernel(Params p) {
     if (G % kXcds == 0) wg = (blockIdx.x % kXcds) * (G / kXcds) + blockIdx.x / kXcds;
 
     const float s_pt = p.rowwise ? 0.f : p.scale_a[0] * p.scale_b[0];
+    float* epi_sa = reinterpret_cast<float*>(smem + C::MAIN_BYTES);
+    float* epi_sb = epi_sa + BM;
+    uint16_t* epi_bias = reinterpret_cast<uint16_t*>(epi_sb + BN);
+    const bool has_bias = p.bias != nullptr;
 
     for (int t = wg; t < p.num_tiles; t += G) {
         int pm, pn;
@@ -230,6 +318,28 @@ fp8_gemm_kernel(Params p) {
         const __amdgpu_buffer_rsrc_t rb =
             make_rsrc(p.B + (size_t)col0 * p.K, rows_b * (uint32_t)p.K);
 
+        // Every wave must be done with the LDS of the previous tile (and its
+        // own epilogue stores must have left) before this tile's loads start.
+        wait_vmcnt<0>();
+        barrier_lds();
+
+        // This tile's scales and bias, fetched now into registers and moved to
+        // LDS after the K loop (their latency hides under the loop).
+        float sa_v[C::NSA], sb_v[C::NSB];
+        uint16_t bias_v[C::NSB];
+#pragma unroll
+        for (int i = 0; i < C::NSA; ++i) {
+            const int r = tid + i * C::THREADS;
+            sa_v[i] = (p.rowwise && r < BM && row0 + r < p.M) ? p.scale_a[row0 + r] : 0.f;
+        }
+#pragma unroll
+        for (int i = 0; i < C::NSB; ++i) {
+            const int c = tid + i * C::THREADS;
+            const bool ok = c < BN && col0 + c < p.N;
+            sb_v[i] = (p.rowwise && ok) ? p.scale_b[col0 + c] : 0.f;
+            bias_v[i] = (has_bias && ok) ? p.bias[col0 + c] : (uint16_t)0;
+        }
+
         typename F::acc_t acc[C::FN][C::FM];
 #pragma unroll
         for (int i = 0; i < C::FN; ++i)
@@ -238,42 +348,62 @@ fp8_gemm_kernel(Params p) {
 #pragma unroll
                 for (int v = 0; v < F::NACC; ++v) acc[i][j][v] = 0.f;
 
-        // Every wave must be done with the LDS of the previous tile (and its
-        // own epilogue stores must have left) before this tile's loads start.
-        wait_vmcnt<0>();
-        barrier_lds();
+        // Fill every stage buffer; the buffer of stage kt is refilled with
+        // slice kt + STAGES once stage kt has been read.
 #pragma unroll
-        for (int s = 0; s < STAGES - 1; ++s)
+        for (int s = 0; s < STAGES; ++s)
             if (s < p.k_iters) load_stage<C>(smem + s * C::STAGE_BYTES, ra, rb, p.K, s * BK, wave, lane);
 
-        for (int kt = 0; kt < p.k_iters; ++kt) {
-            // Stage kt is complete once at most (loads issued after it) remain.
-            if (kt + STAGES - 2 < p.k_iters) wait_vmcnt<C::LOADS * (STAGES - 2)>();
-            else wait_vmcnt<0>();
-            barrier_lds();
-            const int nk = kt + STAGES - 1;
-            if (nk < p.k_iters)
-                load_stage<C>(smem + (nk % STAGES) * C::STAGE_BYTES, ra, rb, p.K, nk * BK, wave,
-                              lane);
-            const uint8_t* sa_t = smem + (kt % STAGES) * C::STAGE_BYTES;
-            const uint8_t* sb_t = sa_t + C::A_BYTES;
-#pragma unroll
-            for (int ks = 0; ks < BK / C::KSTEP; ++ks) {
-                // operand k chunks: MI=32 -> lanes 0-31 chunks {0,1}, 32-63 {2,3};
-                // MI=16 -> four lane groups of 16 take chunk pairs 0..3.
-                const int c0 = ks * (C::KSTEP / 16) + (lane / MI) * 2;
-                v8i af[C::FM], bfr[C::FN];
-#pragma unroll
-                for (int j = 0; j < C::FM; ++j)
-                    af[j] = read_frag<C::CPR>(sa_t, wm * C::WTM + j * MI + lane % MI, c0);
-#pragma unroll
-                for (int i = 0; i < C::FN; ++i)
-                    bfr[i] = read_frag<C::CPR>(sb_t, wn * C::WTN + i * MI + lane % MI, c0);
-#pragma unroll
-                for (int i = 0; i < C::FN; ++i)
-#pragma unroll
-                    for (int j = 0; j < C::FM; ++j) acc[i][j] = F::run(bfr[i], af[j], acc[i][j]);
+        // Software pipeline over K steps: the operand fragments of step q+1 are
+        // read from LDS while the MFMAs of step q run.  At the last step of a
+        // stage the wave first makes the next stage visible (own loads landed,
+        // barrier), recycles the stage it has just finished reading for the
+        // loads STAGES slices ahead, and reads the next stage's first fragments;
+        // the barrier therefore sits under the tail of the previous MFMAs.
+        v8i fa[2][C::FM], fb[2][C::FN];
+        if (STAGES - 1 < p.k_iters) wait_vmcnt<C::LOADS * (STAGES - 1)>();   // stage 0 landed
+        else wait_vmcnt<0>();
+        barrier_lds();
+        read_frags<C>(fa[0], fb[0], smem, 0, wm, wn, lane);
+
+        // Every stage but the last hands over to the next one; the fragment
+        // parity of each stage is a compile-time constant.
+        int kt = 0;
+        if constexpr (C::NKS % 2 == 0) {
+            for (; kt + 1 < p.k_iters; ++kt)
+                run_stage<C, 0, true>(acc, fa, fb, smem, kt, p.k_iters, ra, rb, p.K, wave, wm, wn, lane);
+            run_stage<C, 0, false>(acc, fa, fb, smem, kt, p.k_iters, ra, rb, p.K, wave, wm, wn, lane);
+        } else {
+            for (; kt + 2 < p.k_iters; kt += 2) {
+                run_stage<C, 0, true>(acc, fa, fb, smem, kt, p.k_iters, ra, rb, p.K, wave, wm, wn, lane);
+                run_stage<C, 1, true>(acc, fa, fb, smem, kt + 1, p.k_iters, ra, rb, p.K, wave, wm, wn,
+                                      lane);
             }
+            if (kt + 1 < p.k_iters) {
+                run_stage<C, 0, true>(acc, fa, fb, smem, kt, p.k_iters, ra, rb, p.K, wave, wm, wn, lane);
+                run_stage<C, 1, false>(acc, fa, fb, smem, kt + 1, p.k_iters, ra, rb, p.K, wave, wm, wn,
+                                       lane);
+            } else {
+                run_stage<C, 0, false>(acc, fa, fb, smem, kt, p.k_iters, ra, rb, p.K, wave, wm, wn, lane);
+            }
+        }
+
+        // Epilogue parameters into LDS (the stage buffers are not touched).
+        if (p.rowwise || has_bias) {
+#pragma unroll
+            for (int i = 0; i < C::NSA; ++i) {
+                const int r = tid + i * C::THREADS;
+                if (r < BM) epi_sa[r] = sa_v[i];
+            }
+#pragma unroll
+            for (int i = 0; i < C::NSB; ++i) {
+                const int c = tid + i * C::THREADS;
+                if (c < BN) {
+                    epi_sb[c] = sb_v[i];
+                    epi_bias[c] = bias_v[i];
+                }
+            }
+            barrier_lds();
         }
 
         // Epilogue.  The MFMA was fed B as its first operand, so lane l holds
@@ -281,30 +411,41 @@ fp8_gemm_kernel(Params p) {
         // columns n.
 #pragma unroll
         for (int j = 0; j < C::FM; ++j) {
-            const int m = row0 + wm * C::WTM + j * MI + lane % MI;
+            const int ml = wm * C::WTM + j * MI + lane % MI;
+            const int m = row0 + ml;
             if (m >= p.M) continue;
-            const float sa_m = p.rowwise ? p.scale_a[m] : 0.f;
+            const float sa_m = p.rowwise ? epi_sa[ml] : 0.f;
             uint16_t* orow = p.out + (size_t)m * p.N;
 #pragma unroll
             for (int i = 0; i < C::FN; ++i) {
 #pragma unroll
                 for (int g = 0; g < F::NACC / 4; ++g) {
-                    const int n = col0 + wn * C::WTN + i * MI +
-                                  (MI == 32 ? 8 * g + 4 * (lane / 32) : 4 * (lane / 16));
+                    const int nl = wn * C::WTN + i * MI +
+                                   (MI == 32 ? 8 * g + 4 * (lane / 32) : 4 * (lane / 16));
+                    const int n = col0 + nl;
                     if (n >= p.N) continue;
+                    float s4[4], b4[4];
+                    if (p.rowwise) {
+                        const v4f sb4 = *reinterpret_cast<const v4f*>(epi_sb + nl);
+#pragma unroll
+                        for (int c = 0; c < 4; ++c) s4[c] = sa_m * sb4[c];
+                    } else {
+#pragma unroll
+                        for (int c = 0; c < 4; ++c) s4[c] = s_pt;
+                    }
+                    if (has_bias) {
+                        const uint2 bb = *reinterpret_cast<const uint2*>(epi_bias + nl);
+                        b4[0] = __uint_as_float(bb.x << 16);
+                        b4[1] = __uint_as_float(bb.x & 0xffff0000u);
+                        b4[2] = __uint_as_float(bb.y << 16);
+                        b4[3] = __uint_as_float(bb.y & 0xffff0000u);
+                    }
                     uint32_t h[4];
 #pragma unroll
                     for (int c = 0; c < 4; ++c) {
-                        const int nc = min(n + c, p.N - 1);
-                        const float s = p.rowwise ? sa_m * p.scale_b[nc] : s_pt;
-                        float y = acc[i][j][4 * g + c];
-                        if (p.bias) {
-                            const float b = __uint_as_float((uint32_t)p.bias[nc] << 16);
-                            y = __builtin_fmaf(y, s, b);
-                        } else {
-                            y = y * s;
-                        }
-                        h[c] = f32_to_bf16_rne(y);
+                        const float y = acc[i][j][4 * g + c];
+                        h[c] = f32_to_bf16_rne(has_bias ? __builtin_fmaf(y, s4[c], b4[c])
+                                                        : y * s4[c]);
                     }
                     if (p.vec_store && n + 3 < p.N) {
                         uint2 w;
@@ -352,6 +493,10 @@ const ConfigInfo kConfigs[] = {
     FP8MM_CFG("bm128_bn128_bk128_w2x2_s3_mfma32", 128, 128, 128, 2, 2, 3, 32, 8),
     FP8MM_CFG("bm32_bn64_bk256_w1x2_s4_mfma32", 32, 64, 256, 1, 2, 4, 32, 8),
     FP8MM_CFG("bm16_bn64_bk256_w1x4_s4_mfma16", 16, 64, 256, 1, 4, 4, 16, 8),
+    FP8MM_CFG("bm256_bn256_bk64_w2x4_s4_mfma32", 256, 256, 64, 2, 4, 4, 32, 8),
+    FP8MM_CFG("bm256_bn256_bk128_w2x4_s2_mfma32", 256, 256, 128, 2, 4, 2, 32, 8),
+    FP8MM_CFG("bm256_bn256_bk64_w2x2_s4_mfma32", 256, 256, 64, 2, 2, 4, 32, 8),
+    FP8MM_CFG("bm256_bn256_bk64_w4x2_s4_mfma32", 256, 256, 64, 4, 2, 4, 32, 8),
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 
@@ -361,8 +506,9 @@ int choose_config(int64_t M, int64_t N, int64_t K, int mode, int has_bias) {
     (void)K; (void)mode; (void)has_bias;
     if (M <= 16) return 3;
     if (M <= 64) return 2;
+    // 256 x 256 tiles (8 waves) once they fill most of the 256 CUs; else 128 x 128.
     const int64_t big_tiles = cdiv(M, 256) * cdiv(N, 256);
-    if (big_tiles >= 256) return 0;
+    if (big_tiles >= 192) return 5;
     return 1;
 }
 
