@@ -31,7 +31,7 @@ METRIC = "FP8 scaled-GEMM TFLOP/s and % of dense-FP8 MFMA peak (per-tensor, row-
 PEAK_FP8_TFLOPS = 5000.0      # MI355X dense FP8 MFMA (no sparsity)
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 KERNEL_SRC = os.path.join(ROOT, "precision_linear_amd", "csrc", "fp8_scaled_mm.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_sq8192.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_sq8192.txt")
 
 
 def kernel_sha():
@@ -197,10 +197,14 @@ def main():
 
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
+        tr = {}
         with open(TRAFFIC_FILE) as f:
-            tr = json.load(f)
-        if tr.get("kernel_sha") == kernel_sha():
-            traffic = tr.get("bytes_per_launch")
+            for line in f:
+                if ":" in line and not line.startswith("#"):
+                    k, v = line.split(":", 1)
+                    tr[k.strip()] = v.strip()
+        if tr.get("kernel_sha") == kernel_sha():     # counters taken on this very kernel
+            traffic = int(tr["bytes_per_launch"])
 
     value = flops_step * args.steps / elapsed / 1e12
     line = {
