@@ -93,13 +93,25 @@ def cpu_baseline(problem, target_s=12.0):
                       f"K={K}), fp64 exact accumulation + bf16 RNE, {dt:.1f} s"}
 
 
+def evict_caches(flush):
+    """Read (not write) a buffer larger than the 256 MB MALL so the next launch
+    finds its operands in HBM.  Writing would leave dirty lines whose write-back
+    would then be charged to the measured kernel."""
+    flush.sum(dtype=torch_int64())
+
+
+def torch_int64():
+    import torch
+    return torch.int64
+
+
 def time_launches(problem, n, flush=None):
     """Per-launch HIP events on the launch stream; returns durations in ms."""
     import torch
     evs = []
     for _ in range(n):
         if flush is not None:
-            flush.zero_()
+            evict_caches(flush)
         s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         s.record()
         problem.launch()
@@ -112,7 +124,7 @@ def time_launches(problem, n, flush=None):
 def skinny_results(dev, reps=20):
     import torch
     from precision_linear_amd import workloads as wl
-    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)   # > 256 MB MALL
+    flush = torch.ones(1 << 30, dtype=torch.uint8, device=dev)    # > 256 MB MALL
     res = []
     for name in [n for n in wl.WORKLOADS if n.startswith("skinny")]:
         p = Problem(name, dev)

@@ -26,8 +26,19 @@
  * Pointers: A, B, scale_a, scale_b, bias and out are DEVICE pointers on the
  * current HIP device.  The library never dereferences them on the host, so
  * scales may be produced by an earlier kernel on the same stream.  The
- * caller owns every buffer; the library allocates nothing, keeps no pointer
- * after the call returns and may be called from several host threads.
+ * caller owns every buffer and the library keeps no pointer to them after the
+ * call returns; it may be called from several host threads.
+ *
+ * Workspace: when the output has too few tiles to occupy the GPU, the K
+ * reduction is split over several workgroups whose fp32 partial tiles meet in
+ * a workspace (the split-K of the gist "matmul_fp8.py", autotune parameter
+ * SPLIT_K, done with a deterministic in-order sum instead of atomics).  The
+ * plain entry points then use a workspace owned by the library, one per
+ * (device, stream), allocated and zero-filled by the first such call and
+ * grown (after synchronising that stream) when a larger one is needed; it is
+ * freed only at process exit.  fp8_scaled_mm_with_plan accepts a caller
+ * workspace instead and then allocates nothing.  Calls on different streams
+ * never share a workspace.
  *
  * Execution: asynchronous on `stream` (a hipStream_t; NULL = the default
  * stream).  The call returns after the launch, without synchronising.
@@ -68,7 +79,8 @@ enum fp8mm_status {
     FP8MM_ERR_MODE = 4,    /* unknown scaling_mode */
     FP8MM_ERR_DEVICE = 5,  /* no usable HIP device, or not a gfx950 */
     FP8MM_ERR_LAUNCH = 6,  /* the kernel launch failed */
-    FP8MM_ERR_CONFIG = 7   /* unknown tile configuration id */
+    FP8MM_ERR_CONFIG = 7,  /* unknown tile configuration id or split count */
+    FP8MM_ERR_WORKSPACE = 8 /* caller workspace smaller than required */
 };
 
 /* The scaled multiply described above, with the tile configuration chosen
@@ -85,6 +97,32 @@ int fp8_scaled_mm_with_config(const void* A, const void* B, const float* scale_a
                               int64_t M, int64_t N, int64_t K, int scaling_mode,
                               struct ihipStream_t* stream, int config_id);
 
+/* The most general form: explicit tile configuration (config_id < 0: chosen
+ * from the shape), split-K factor (splits == 0: chosen; 1: no split; at most
+ * 64, clamped to the number of K slices), and workspace.  With a non-NULL
+ * `workspace` (256-byte aligned, at least fp8_scaled_mm_workspace_size()
+ * bytes, zero-filled before its first use; every call leaves it zero-filled
+ * again) the library allocates nothing; with NULL it uses its own (see the
+ * workspace note above).  A caller workspace must not be used by two calls
+ * that can run at the same time.  Results do not depend on which workgroup
+ * finishes first: partial tiles are summed in split order. */
+int fp8_scaled_mm_with_plan(const void* A, const void* B, const float* scale_a,
+                            const float* scale_b, const void* bias_or_null, void* out,
+                            int64_t M, int64_t N, int64_t K, int scaling_mode,
+                            struct ihipStream_t* stream, int config_id, int splits,
+                            void* workspace, int64_t workspace_bytes);
+
+/* Workspace bytes the plan (config_id, splits; negative/zero = automatic)
+ * needs for this problem; 0 when it does not split K, -1 for a bad mode.
+ * Host logic only. */
+int64_t fp8_scaled_mm_workspace_size(int64_t M, int64_t N, int64_t K, int scaling_mode,
+                                     int has_bias, int config_id, int splits);
+
+/* The split-K factor the automatic plan uses (host logic only; -1 for an
+ * invalid problem). */
+int fp8_scaled_mm_select_splits(int64_t M, int64_t N, int64_t K, int scaling_mode, int has_bias,
+                                int config_id);
+
 /* Number of tile configurations compiled into the library. */
 int fp8_scaled_mm_num_configs(void);
 
@@ -95,8 +133,8 @@ const char* fp8_scaled_mm_config_name(int config_id);
  * logic: no device access).  Returns -1 for an invalid problem. */
 int fp8_scaled_mm_select_config(int64_t M, int64_t N, int64_t K, int scaling_mode, int has_bias);
 
-/* Grid size (workgroups) a launch of `config_id` uses on a device with
- * `num_cus` compute units for an M x N output (host logic only). */
+/* Grid size (workgroups) a launch of `config_id` without split-K uses on a
+ * device with `num_cus` compute units for an M x N output (host logic only). */
 int64_t fp8_scaled_mm_grid_size(int config_id, int64_t M, int64_t N, int num_cus);
 
 /* Static, NUL-terminated text for a status code. */

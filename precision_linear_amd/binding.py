@@ -21,11 +21,12 @@ _MODES = {"per_tensor": PER_TENSOR, "tensorwise": PER_TENSOR, "rowwise": ROWWISE
           PER_TENSOR: PER_TENSOR, ROWWISE: ROWWISE}
 
 # status codes from include/fp8_scaled_mm.h
-OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_MODE, ERR_DEVICE, ERR_LAUNCH, ERR_CONFIG = range(8)
-_ARG_ERRORS = {ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_MODE, ERR_CONFIG}
+OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_MODE, ERR_DEVICE, ERR_LAUNCH, ERR_CONFIG, ERR_WORKSPACE = range(9)
+_ARG_ERRORS = {ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_MODE, ERR_CONFIG, ERR_WORKSPACE}
 
-EXPORTS = ("fp8_scaled_mm", "fp8_scaled_mm_with_config", "fp8_scaled_mm_num_configs",
-           "fp8_scaled_mm_config_name", "fp8_scaled_mm_select_config",
+EXPORTS = ("fp8_scaled_mm", "fp8_scaled_mm_with_config", "fp8_scaled_mm_with_plan",
+           "fp8_scaled_mm_workspace_size", "fp8_scaled_mm_select_splits",
+           "fp8_scaled_mm_num_configs", "fp8_scaled_mm_config_name", "fp8_scaled_mm_select_config",
            "fp8_scaled_mm_grid_size", "fp8_scaled_mm_status_string")
 
 
@@ -51,6 +52,13 @@ def lib() -> ctypes.CDLL:
         L.fp8_scaled_mm.restype = i32
         L.fp8_scaled_mm_with_config.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, vp, i32]
         L.fp8_scaled_mm_with_config.restype = i32
+        L.fp8_scaled_mm_with_plan.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, vp, i32,
+                                              i32, vp, i64]
+        L.fp8_scaled_mm_with_plan.restype = i32
+        L.fp8_scaled_mm_workspace_size.argtypes = [i64, i64, i64, i32, i32, i32, i32]
+        L.fp8_scaled_mm_workspace_size.restype = i64
+        L.fp8_scaled_mm_select_splits.argtypes = [i64, i64, i64, i32, i32, i32]
+        L.fp8_scaled_mm_select_splits.restype = i32
         L.fp8_scaled_mm_num_configs.argtypes = []
         L.fp8_scaled_mm_num_configs.restype = i32
         L.fp8_scaled_mm_config_name.argtypes = [i32]
@@ -78,6 +86,16 @@ def select_config(M, N, K, mode, has_bias=False) -> int:
     return int(lib().fp8_scaled_mm_select_config(M, N, K, _MODES[mode], int(bool(has_bias))))
 
 
+def select_splits(M, N, K, mode, has_bias=False, config=-1) -> int:
+    return int(lib().fp8_scaled_mm_select_splits(M, N, K, _MODES[mode], int(bool(has_bias)),
+                                                 int(config)))
+
+
+def workspace_size(M, N, K, mode, has_bias=False, config=-1, splits=0) -> int:
+    return int(lib().fp8_scaled_mm_workspace_size(M, N, K, _MODES[mode], int(bool(has_bias)),
+                                                  int(config), int(splits)))
+
+
 def _as_codes(t: torch.Tensor, name: str) -> torch.Tensor:
     if t.dtype == torch.float8_e4m3fn:
         return t.view(torch.uint8)
@@ -88,10 +106,13 @@ def _as_codes(t: torch.Tensor, name: str) -> torch.Tensor:
 
 def fp8_scaled_mm(a: torch.Tensor, b: torch.Tensor, scale_a: torch.Tensor, scale_b: torch.Tensor,
                   bias: torch.Tensor | None = None, out: torch.Tensor | None = None,
-                  mode="per_tensor", config: int = -1) -> torch.Tensor:
+                  mode="per_tensor", config: int = -1, splits: int = 0,
+                  workspace: torch.Tensor | None = None) -> torch.Tensor:
     """out = bf16(scale_a * scale_b * (a @ b^T) + bias) with a: M x K and b: N x K
     (e4m3fn, K contiguous).  b may also be given as a K x N column-major view
-    (stride (1, K)), which is the same memory."""
+    (stride (1, K)), which is the same memory.  `config` (-1: automatic) and
+    `splits` (0: automatic) select the plan; `workspace` (a GPU byte tensor,
+    zero-filled before first use) replaces the library-owned split-K workspace."""
     if mode not in _MODES:
         raise ValueError(f"mode must be 'per_tensor' or 'rowwise', got {mode!r}")
     m = _MODES[mode]
@@ -126,12 +147,17 @@ def fp8_scaled_mm(a: torch.Tensor, b: torch.Tensor, scale_a: torch.Tensor, scale
         out = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
     elif out.dtype != torch.bfloat16 or tuple(out.shape) != (M, N) or not out.is_contiguous():
         raise ValueError("out must be a contiguous bf16 M x N tensor")
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        if not workspace.is_cuda or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous GPU tensor")
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
     stream = torch.cuda.current_stream(a.device).cuda_stream
     with torch.cuda.device(a.device):
-        st = lib().fp8_scaled_mm_with_config(
+        st = lib().fp8_scaled_mm_with_plan(
             a.data_ptr(), b.data_ptr(), scale_a.data_ptr(), scale_b.data_ptr(),
             bias.data_ptr() if bias is not None else None, out.data_ptr(),
-            M, N, K, m, stream, int(config))
+            M, N, K, m, stream, int(config), int(splits), ws_ptr, ws_bytes)
     if st != OK:
         if st in _ARG_ERRORS:
             raise ValueError(f"fp8_scaled_mm: {status_string(st)} (status {st})")

@@ -26,6 +26,10 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <map>
+#include <mutex>
+#include <utility>
+
 #include "../../include/fp8_scaled_mm.h"
 
 namespace {
@@ -52,6 +56,13 @@ struct Params {
     int tiles_m, tiles_n, num_tiles, k_iters;
     int rowwise;
     int vec_store;         // N % 4 == 0 and out 8-byte aligned
+    // Split-K: each output tile is computed by `splits` work units, unit s
+    // covering K slices [s*k_chunk, (s+1)*k_chunk).  With splits > 1 the fp32
+    // partial tiles go to `partials` and the unit that arrives last at the
+    // tile's counter adds them up in split order and runs the epilogue.
+    int splits, k_chunk;
+    float* partials;       // num_tiles * splits * BM * BN floats (splits > 1)
+    unsigned* counters;    // num_tiles arrival counters (splits > 1)
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
@@ -136,19 +147,27 @@ struct Cfg {
     static constexpr int NSB = (BN + THREADS - 1) / THREADS;
     static constexpr int A_BLOCKS = A_BYTES / 1024;  // 1 KiB = one wave-wide 16-byte load
     static constexpr int B_BLOCKS = B_BYTES / 1024;
-    static constexpr int A_LOADS = A_BLOCKS / WAVES; // per wave per stage
-    static constexpr int B_LOADS = B_BLOCKS / WAVES;
+    // Loads per wave per stage.  When the blocks do not split evenly over the
+    // waves, the surplus loads repeat the last block: the same bytes land at
+    // the same LDS address twice, and every wave keeps the same load count
+    // (which the vmcnt arithmetic relies on).
+    static constexpr int A_LOADS = (A_BLOCKS + WAVES - 1) / WAVES;
+    static constexpr int B_LOADS = (B_BLOCKS + WAVES - 1) / WAVES;
     static constexpr int LOADS = A_LOADS + B_LOADS;
     static constexpr int KSTEP = Mfma<MI>::KSTEP;
     static constexpr int NKS = BK / KSTEP;        // MFMA K steps per stage
     static constexpr int MI_ = MI;
+    // Split-K keeps a second copy of the accumulators while it sums the
+    // partials, so it is compiled only where both fit in registers.
+    static constexpr int PER_LANE_ACC = FM * FN * (MI == 32 ? 16 : 4);
+    static constexpr bool SPLIT_OK = PER_LANE_ACC <= 64;
     static constexpr int BK_ = BK;
     static constexpr int STAGES_ = STAGES;
     static_assert(WTM % MI == 0 && WTN % MI == 0, "wave tile must hold whole MFMA tiles");
     static_assert(MI % 16 == 0, "fragment row blocks must be 16-row aligned for the swizzle");
     static_assert(BK % KSTEP == 0, "BK must be a multiple of the MFMA K step");
     static_assert(CPR == 4 || CPR == 8 || CPR == 16 || CPR == 32, "BK must be 64..512");
-    static_assert(A_BLOCKS % WAVES == 0 && B_BLOCKS % WAVES == 0, "loads must split evenly");
+    static_assert(A_BYTES % 1024 == 0 && B_BYTES % 1024 == 0, "stages are whole 1 KiB blocks");
     static_assert(LDS_BYTES <= 160 * 1024, "gfx950 LDS is 160 KiB per workgroup");
     static_assert(STAGES >= 2, "at least double buffering");
     static_assert(LOADS * (STAGES - 1) <= 63, "vmcnt counts up to 63");
@@ -157,8 +176,8 @@ struct Cfg {
 // Issue the direct-to-LDS loads of one K slice (k0) for this wave.
 template <class C>
 __device__ __forceinline__ void load_stage(uint8_t* lds_stage, __amdgpu_buffer_rsrc_t ra,
-                                           __amdgpu_buffer_rsrc_t rb, int K, int k0, int wave,
-                                           int lane) {
+                                           __amdgpu_buffer_rsrc_t rb, int ld, int klim, int k0,
+                                           int wave, int lane) {
     constexpr int RPB = 1024 / (C::CPR * 16);    // LDS rows per 1 KiB block
     // The lane-dependent offsets are cheap to recompute; keeping them live
     // across the K loop would only cost registers the MFMA pipeline needs.
@@ -168,21 +187,21 @@ __device__ __forceinline__ void load_stage(uint8_t* lds_stage, __amdgpu_buffer_r
     const int pos = l % C::CPR;
 #pragma unroll
     for (int i = 0; i < C::A_LOADS; ++i) {
-        const int blk = wave + i * C::WAVES;
+        const int blk = min(wave + i * C::WAVES, C::A_BLOCKS - 1);
         const int r = blk * RPB + rr;
         const int c = pos ^ chunk_swizzle<C::CPR>(r);
         const int k = k0 + c * 16;
-        const uint32_t off = k < K ? (uint32_t)(r * K + k) : kOutOfRange;
+        const uint32_t off = k < klim ? (uint32_t)(r * ld + k) : kOutOfRange;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             ra, (lds_void_t*)(lds_stage + blk * 1024), 16, off, 0, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < C::B_LOADS; ++i) {
-        const int blk = wave + i * C::WAVES;
+        const int blk = min(wave + i * C::WAVES, C::B_BLOCKS - 1);
         const int r = blk * RPB + rr;
         const int c = pos ^ chunk_swizzle<C::CPR>(r);
         const int k = k0 + c * 16;
-        const uint32_t off = k < K ? (uint32_t)(r * K + k) : kOutOfRange;
+        const uint32_t off = k < klim ? (uint32_t)(r * ld + k) : kOutOfRange;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             rb, (lds_void_t*)(lds_stage + C::A_BYTES + blk * 1024), 16, off, 0, 0, 0);
     }
@@ -249,8 +268,8 @@ template <class C, int CUR0, bool HAS_NEXT>
 __device__ __forceinline__ void run_stage(typename Mfma<C::MI_>::acc_t (&acc)[C::FN][C::FM],
                                           v8i (&fa)[2][C::FM], v8i (&fb)[2][C::FN], uint8_t* smem,
                                           int kt, int k_iters, __amdgpu_buffer_rsrc_t ra,
-                                          __amdgpu_buffer_rsrc_t rb, int K, int wave, int wm, int wn,
-                                          int lane) {
+                                          __amdgpu_buffer_rsrc_t rb, int ld, int klim, int wave,
+                                          int wm, int wn, int lane) {
     using F = Mfma<C::MI_>;
     constexpr int S = C::STAGES_;
     const uint8_t* st = smem + (kt % S) * C::STAGE_BYTES;
@@ -266,8 +285,8 @@ __device__ __forceinline__ void run_stage(typename Mfma<C::MI_>::acc_t (&acc)[C:
             else wait_vmcnt<0>();
             barrier_lds();
             if (kt + S < k_iters)
-                load_stage<C>(smem + (kt % S) * C::STAGE_BYTES, ra, rb, K, (kt + S) * C::BK_, wave,
-                              lane);
+                load_stage<C>(smem + (kt % S) * C::STAGE_BYTES, ra, rb, ld, klim, (kt + S) * C::BK_,
+                              wave, lane);
             read_frags<C>(fa[cur ^ 1], fb[cur ^ 1], smem + ((kt + 1) % S) * C::STAGE_BYTES, 0, wm,
                           wn, lane);
         }
@@ -306,17 +325,27 @@ fp8_gemm_kernel(Params p) {
     uint16_t* epi_bias = reinterpret_cast<uint16_t*>(epi_sb + BN);
     const bool has_bias = p.bias != nullptr;
 
-    for (int t = wg; t < p.num_tiles; t += G) {
+    __shared__ unsigned arrival;
+    const int num_units = p.num_tiles * p.splits;
+    for (int u = wg; u < num_units; u += G) {
+        const int t = u / p.splits;             // the splits of a tile are neighbours
+        const int split = u - t * p.splits;
         int pm, pn;
         tile_coords(t, p.tiles_m, p.tiles_n, GROUP_M, pm, pn);
         const int row0 = pm * BM;
         const int col0 = pn * BN;
+        // This unit's K range, as whole BK slices; the buffer resources start at
+        // its first byte so the stage code sees a K range beginning at 0.
+        const int kb = split * p.k_chunk;
+        const int k_iters = max(0, min(p.k_chunk, p.k_iters - kb));
+        const int kskip = kb * BK;
+        const int klim = p.K - kskip;
         const uint32_t rows_a = (uint32_t)min(BM, p.M - row0);
         const uint32_t rows_b = (uint32_t)min(BN, p.N - col0);
         const __amdgpu_buffer_rsrc_t ra =
-            make_rsrc(p.A + (size_t)row0 * p.K, rows_a * (uint32_t)p.K);
+            make_rsrc(p.A + (size_t)row0 * p.K + kskip, rows_a * (uint32_t)p.K - (uint32_t)kskip);
         const __amdgpu_buffer_rsrc_t rb =
-            make_rsrc(p.B + (size_t)col0 * p.K, rows_b * (uint32_t)p.K);
+            make_rsrc(p.B + (size_t)col0 * p.K + kskip, rows_b * (uint32_t)p.K - (uint32_t)kskip);
 
         // Every wave must be done with the LDS of the previous tile (and its
         // own epilogue stores must have left) before this tile's loads start.
@@ -352,7 +381,8 @@ fp8_gemm_kernel(Params p) {
         // slice kt + STAGES once stage kt has been read.
 #pragma unroll
         for (int s = 0; s < STAGES; ++s)
-            if (s < p.k_iters) load_stage<C>(smem + s * C::STAGE_BYTES, ra, rb, p.K, s * BK, wave, lane);
+            if (s < k_iters)
+                load_stage<C>(smem + s * C::STAGE_BYTES, ra, rb, p.K, klim, s * BK, wave, lane);
 
         // Software pipeline over K steps: the operand fragments of step q+1 are
         // read from LDS while the MFMAs of step q run.  At the last step of a
@@ -361,31 +391,97 @@ fp8_gemm_kernel(Params p) {
         // loads STAGES slices ahead, and reads the next stage's first fragments;
         // the barrier therefore sits under the tail of the previous MFMAs.
         v8i fa[2][C::FM], fb[2][C::FN];
-        if (STAGES - 1 < p.k_iters) wait_vmcnt<C::LOADS * (STAGES - 1)>();   // stage 0 landed
+        if (STAGES - 1 < k_iters) wait_vmcnt<C::LOADS * (STAGES - 1)>();   // stage 0 landed
         else wait_vmcnt<0>();
         barrier_lds();
-        read_frags<C>(fa[0], fb[0], smem, 0, wm, wn, lane);
+        if (k_iters > 0) read_frags<C>(fa[0], fb[0], smem, 0, wm, wn, lane);
 
         // Every stage but the last hands over to the next one; the fragment
         // parity of each stage is a compile-time constant.
         int kt = 0;
-        if constexpr (C::NKS % 2 == 0) {
-            for (; kt + 1 < p.k_iters; ++kt)
-                run_stage<C, 0, true>(acc, fa, fb, smem, kt, p.k_iters, ra, rb, p.K, wave, wm, wn, lane);
-            run_stage<C, 0, false>(acc, fa, fb, smem, kt, p.k_iters, ra, rb, p.K, wave, wm, wn, lane);
-        } else {
-            for (; kt + 2 < p.k_iters; kt += 2) {
-                run_stage<C, 0, true>(acc, fa, fb, smem, kt, p.k_iters, ra, rb, p.K, wave, wm, wn, lane);
-                run_stage<C, 1, true>(acc, fa, fb, smem, kt + 1, p.k_iters, ra, rb, p.K, wave, wm, wn,
-                                      lane);
-            }
-            if (kt + 1 < p.k_iters) {
-                run_stage<C, 0, true>(acc, fa, fb, smem, kt, p.k_iters, ra, rb, p.K, wave, wm, wn, lane);
-                run_stage<C, 1, false>(acc, fa, fb, smem, kt + 1, p.k_iters, ra, rb, p.K, wave, wm, wn,
+        if (k_iters > 0) {
+            if constexpr (C::NKS % 2 == 0) {
+                for (; kt + 1 < k_iters; ++kt)
+                    run_stage<C, 0, true>(acc, fa, fb, smem, kt, k_iters, ra, rb, p.K, klim, wave, wm,
+                                          wn, lane);
+                run_stage<C, 0, false>(acc, fa, fb, smem, kt, k_iters, ra, rb, p.K, klim, wave, wm, wn,
                                        lane);
             } else {
-                run_stage<C, 0, false>(acc, fa, fb, smem, kt, p.k_iters, ra, rb, p.K, wave, wm, wn, lane);
+                for (; kt + 2 < k_iters; kt += 2) {
+                    run_stage<C, 0, true>(acc, fa, fb, smem, kt, k_iters, ra, rb, p.K, klim, wave, wm,
+                                          wn, lane);
+                    run_stage<C, 1, true>(acc, fa, fb, smem, kt + 1, k_iters, ra, rb, p.K, klim, wave,
+                                          wm, wn, lane);
+                }
+                if (kt + 1 < k_iters) {
+                    run_stage<C, 0, true>(acc, fa, fb, smem, kt, k_iters, ra, rb, p.K, klim, wave, wm,
+                                          wn, lane);
+                    run_stage<C, 1, false>(acc, fa, fb, smem, kt + 1, k_iters, ra, rb, p.K, klim, wave,
+                                           wm, wn, lane);
+                } else {
+                    run_stage<C, 0, false>(acc, fa, fb, smem, kt, k_iters, ra, rb, p.K, klim, wave, wm,
+                                           wn, lane);
+                }
             }
+        }
+
+        if constexpr (C::SPLIT_OK) if (p.splits > 1) {
+            // Publish this unit's partial tile (lane-major, so each store and
+            // load below is a 256-byte run per wave) and count the arrival.
+            // Partials travel with agent-coherent stores and loads (written
+            // through the XCD's L2, read past it), so a unit on one XCD sees
+            // another XCD's partials without writing back or invalidating
+            // whole L2s; the stores have completed (vmcnt 0) before the
+            // arrival is counted.
+            float* mine = p.partials + (size_t)u * (BM * BN);
+#pragma unroll
+            for (int i = 0; i < C::FN; ++i)
+#pragma unroll
+                for (int j = 0; j < C::FM; ++j)
+#pragma unroll
+                    for (int v = 0; v < F::NACC; ++v)
+                        __hip_atomic_store(mine + ((i * C::FM + j) * F::NACC + v) * C::THREADS + tid,
+                                           acc[i][j][v], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            wait_vmcnt<0>();
+            __syncthreads();
+            if (tid == 0)
+                arrival = __hip_atomic_fetch_add(&p.counters[t], 1u, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+            __syncthreads();
+            // Only the last of the tile's units goes on; it adds the partials in
+            // split order (deterministic whatever the arrival order).
+            if (arrival != (unsigned)(p.splits - 1)) continue;
+            if (tid == 0)
+                __hip_atomic_store(&p.counters[t], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            typename F::acc_t sum[C::FN][C::FM];
+#pragma unroll
+            for (int i = 0; i < C::FN; ++i)
+#pragma unroll
+                for (int j = 0; j < C::FM; ++j)
+#pragma unroll
+                    for (int v = 0; v < F::NACC; ++v) sum[i][j][v] = 0.f;
+            const float* tile_parts = p.partials + (size_t)t * p.splits * (BM * BN);
+            for (int q = 0; q < p.splits; ++q) {
+                const float* part = tile_parts + (size_t)q * (BM * BN);
+#pragma unroll
+                for (int i = 0; i < C::FN; ++i)
+#pragma unroll
+                    for (int j = 0; j < C::FM; ++j)
+#pragma unroll
+                        for (int v = 0; v < F::NACC; ++v) {
+                            const float x =
+                                q == split
+                                    ? acc[i][j][v]
+                                    : __hip_atomic_load(
+                                          part + ((i * C::FM + j) * F::NACC + v) * C::THREADS + tid,
+                                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                            sum[i][j][v] += x;
+                        }
+            }
+#pragma unroll
+            for (int i = 0; i < C::FN; ++i)
+#pragma unroll
+                for (int j = 0; j < C::FM; ++j) acc[i][j] = sum[i][j];
         }
 
         // Epilogue parameters into LDS (the stage buffers are not touched).
@@ -468,6 +564,7 @@ fp8_gemm_kernel(Params p) {
 struct ConfigInfo {
     const char* name;
     int bm, bn, bk;
+    bool split_ok;
     int threads;
     int lds_bytes;
     int occupancy;   // workgroups per CU the persistent grid assumes
@@ -483,7 +580,8 @@ void launch_cfg(const Params& p, dim3 grid, hipStream_t stream) {
 
 #define FP8MM_CFG(name, BM, BN, BK, WMW, WNW, ST, MI, GM)                                      \
     ConfigInfo {                                                                               \
-        name, BM, BN, BK, Cfg<BM, BN, BK, WMW, WNW, ST, MI, GM>::THREADS,                          \
+        name, BM, BN, BK, Cfg<BM, BN, BK, WMW, WNW, ST, MI, GM>::SPLIT_OK,                         \
+            Cfg<BM, BN, BK, WMW, WNW, ST, MI, GM>::THREADS,                                    \
             Cfg<BM, BN, BK, WMW, WNW, ST, MI, GM>::LDS_BYTES, 1,                               \
             &launch_cfg<BM, BN, BK, WMW, WNW, ST, MI, GM>                                      \
     }
@@ -497,15 +595,28 @@ const ConfigInfo kConfigs[] = {
     FP8MM_CFG("bm256_bn256_bk128_w2x4_s2_mfma32", 256, 256, 128, 2, 4, 2, 32, 8),
     FP8MM_CFG("bm256_bn256_bk64_w2x2_s4_mfma32", 256, 256, 64, 2, 2, 4, 32, 8),
     FP8MM_CFG("bm256_bn256_bk64_w4x2_s4_mfma32", 256, 256, 64, 4, 2, 4, 32, 8),
+    FP8MM_CFG("bm16_bn112_bk256_w1x7_s4_mfma16", 16, 112, 256, 1, 7, 4, 16, 8),
+    FP8MM_CFG("bm16_bn32_bk512_w1x2_s6_mfma16", 16, 32, 512, 1, 2, 6, 16, 8),
+    FP8MM_CFG("bm64_bn112_bk128_w4x1_s7_mfma16", 64, 112, 128, 4, 1, 7, 16, 8),
+    FP8MM_CFG("bm128_bn112_bk128_w4x1_s5_mfma16", 128, 112, 128, 4, 1, 5, 16, 8),
+    FP8MM_CFG("bm128_bn64_bk128_w4x1_s6_mfma16", 128, 64, 128, 4, 1, 6, 16, 8),
+    FP8MM_CFG("bm64_bn64_bk128_w4x1_s8_mfma16", 64, 64, 128, 4, 1, 8, 16, 8),
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+int choose_splits(int cfg, int64_t M, int64_t N, int64_t K);
+
 int choose_config(int64_t M, int64_t N, int64_t K, int mode, int has_bias) {
     (void)K; (void)mode; (void)has_bias;
+    // Skinny problems (M <= 128) are HBM-bound on B: tiles as tall as M with
+    // deep B prefetch; when such tiles leave CUs idle the K reduction is split
+    // (choose_splits).  Chosen from measurements on MI355X of the six skinny
+    // inference shapes.
     if (M <= 16) return 3;
-    if (M <= 64) return 2;
+    if (M <= 64) return 13;
+    if (M <= 128) return 1;
     // 256 x 256 tiles (8 waves) once they fill most of the 256 CUs; else 128 x 128.
     const int64_t big_tiles = cdiv(M, 256) * cdiv(N, 256);
     if (big_tiles >= 192) return 5;
@@ -540,11 +651,75 @@ int validate(const void* A, const void* B, const float* sa, const float* sb, con
     return FP8MM_OK;
 }
 
-int64_t grid_for(int cfg, int64_t M, int64_t N, int cus) {
+// Split-K factor for a configuration: only when the tile grid leaves most of
+// the 256 CUs idle, and never below 8 K slices per split.
+int choose_splits(int cfg, int64_t M, int64_t N, int64_t K) {
+    const ConfigInfo& c = kConfigs[cfg];
+    if (!c.split_ok) return 1;
+    const int64_t tiles = cdiv(M, c.bm) * cdiv(N, c.bn);
+    const int64_t k_iters = cdiv(K, c.bk);
+    if (tiles >= 160) return 1;
+    int64_t s = 256 / tiles;
+    if (s > k_iters / 8) s = k_iters / 8;
+    if (s > 16) s = 16;
+    return s < 1 ? 1 : (int)s;
+}
+
+int64_t grid_for(int cfg, int64_t M, int64_t N, int splits, int cus) {
+    const ConfigInfo& c = kConfigs[cfg];
+    const int64_t units = cdiv(M, c.bm) * cdiv(N, c.bn) * splits;
+    const int64_t slots = (int64_t)cus * c.occupancy;
+    return units < slots ? units : slots;
+}
+
+// Workspace layout of a split plan: a fixed block of arrival counters (one per
+// tile, room for kMaxSplitTiles) followed by one fp32 partial tile per work
+// unit.  The counter block sits at the same place for every plan, so a
+// workspace reused by plans of different shapes never finds stale partials
+// where it expects zero counters.
+constexpr int64_t kMaxSplitTiles = 65536;
+constexpr int64_t kCounterBytes = kMaxSplitTiles * 4;
+
+int64_t workspace_bytes(int cfg, int64_t M, int64_t N, int splits) {
+    if (splits <= 1) return 0;
     const ConfigInfo& c = kConfigs[cfg];
     const int64_t tiles = cdiv(M, c.bm) * cdiv(N, c.bn);
-    const int64_t slots = (int64_t)cus * c.occupancy;
-    return tiles < slots ? tiles : slots;
+    return kCounterBytes + tiles * splits * (int64_t)c.bm * c.bn * 4;
+}
+
+// Library-owned split-K workspaces, one per (device, stream): calls on one
+// stream are ordered, so a stream's workspace is never used by two launches at
+// once.  Created on the first split call (zero-filled), grown when needed,
+// kept until the process ends.
+struct OwnedWorkspace {
+    void* ptr = nullptr;
+    int64_t bytes = 0;
+};
+std::mutex g_ws_mutex;
+std::map<std::pair<int, hipStream_t>, OwnedWorkspace> g_ws;
+
+int owned_workspace(int dev, hipStream_t stream, int64_t bytes, void** out) {
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    OwnedWorkspace& w = g_ws[std::make_pair(dev, stream)];
+    if (w.bytes < bytes) {
+        if (w.ptr) {
+            if (hipStreamSynchronize(stream) != hipSuccess) return FP8MM_ERR_LAUNCH;
+            (void)hipFree(w.ptr);
+            w.ptr = nullptr;
+            w.bytes = 0;
+        }
+        void* p = nullptr;
+        if (hipMalloc(&p, (size_t)bytes) != hipSuccess) return FP8MM_ERR_DEVICE;
+        // Counters must start at zero; every launch leaves them at zero.
+        if (hipMemset(p, 0, (size_t)bytes) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
+            (void)hipFree(p);
+            return FP8MM_ERR_DEVICE;
+        }
+        w.ptr = p;
+        w.bytes = bytes;
+    }
+    *out = w.ptr;
+    return FP8MM_OK;
 }
 
 }  // namespace
@@ -565,7 +740,7 @@ int fp8_scaled_mm_select_config(int64_t M, int64_t N, int64_t K, int mode, int h
 
 int64_t fp8_scaled_mm_grid_size(int id, int64_t M, int64_t N, int num_cus) {
     if (id < 0 || id >= kNumConfigs || M <= 0 || N <= 0 || num_cus <= 0) return 0;
-    return grid_for(id, M, N, num_cus);
+    return grid_for(id, M, N, 1, num_cus);
 }
 
 const char* fp8_scaled_mm_status_string(int s) {
@@ -577,25 +752,44 @@ const char* fp8_scaled_mm_status_string(int s) {
         case FP8MM_ERR_MODE: return "unknown scaling mode";
         case FP8MM_ERR_DEVICE: return "no usable gfx950 device";
         case FP8MM_ERR_LAUNCH: return "kernel launch failed";
-        case FP8MM_ERR_CONFIG: return "unknown tile configuration";
+        case FP8MM_ERR_CONFIG: return "unknown tile configuration or split count";
+        case FP8MM_ERR_WORKSPACE: return "workspace smaller than fp8_scaled_mm_workspace_size()";
         default: return "unknown status";
     }
 }
 
-int fp8_scaled_mm_with_config(const void* A, const void* B, const float* scale_a,
-                              const float* scale_b, const void* bias, void* out, int64_t M,
-                              int64_t N, int64_t K, int mode, struct ihipStream_t* stream,
-                              int config_id) {
+int fp8_scaled_mm_with_plan(const void* A, const void* B, const float* scale_a,
+                            const float* scale_b, const void* bias, void* out, int64_t M, int64_t N,
+                            int64_t K, int mode, struct ihipStream_t* stream, int config_id,
+                            int splits, void* workspace, int64_t workspace_size) {
     int st = validate(A, B, scale_a, scale_b, bias, out, M, N, K, mode);
     if (st != FP8MM_OK) return st;
     if (config_id >= kNumConfigs) return FP8MM_ERR_CONFIG;
+    if (splits < 0 || splits > 64) return FP8MM_ERR_CONFIG;
     if (M == 0 || N == 0) return FP8MM_OK;
     const int cfg = config_id >= 0 ? config_id : choose_config(M, N, K, mode, bias != nullptr);
+    const ConfigInfo& c = kConfigs[cfg];
+    const int64_t k_iters = cdiv(K, c.bk);
+    int sp = splits > 0 ? splits : choose_splits(cfg, M, N, K);
+    if (sp > k_iters) sp = (int)k_iters;
+    const int64_t tiles = cdiv(M, c.bm) * cdiv(N, c.bn);
+    if (tiles > kMaxSplitTiles || !c.split_ok) sp = 1;
+    if (tiles * sp > INT32_MAX) return FP8MM_ERR_SHAPE;
+    const int64_t ws_need = workspace_bytes(cfg, M, N, sp);
+    if (workspace && workspace_size < ws_need) return FP8MM_ERR_WORKSPACE;
+    if (workspace && ((uintptr_t)workspace & 255)) return FP8MM_ERR_ALIGN;
 
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess) return FP8MM_ERR_DEVICE;
     const int cus = device_cus(dev);
     if (cus <= 0) return FP8MM_ERR_DEVICE;
+    const hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+
+    void* ws = workspace;
+    if (ws_need > 0 && !ws) {
+        st = owned_workspace(dev, hs, ws_need, &ws);
+        if (st != FP8MM_OK) return st;
+    }
 
     Params p;
     p.A = static_cast<const uint8_t*>(A);
@@ -607,27 +801,65 @@ int fp8_scaled_mm_with_config(const void* A, const void* B, const float* scale_a
     p.M = (int)M;
     p.N = (int)N;
     p.K = (int)K;
-    const ConfigInfo& c = kConfigs[cfg];
     p.tiles_m = (int)cdiv(M, c.bm);
     p.tiles_n = (int)cdiv(N, c.bn);
-    const int64_t tiles = (int64_t)p.tiles_m * p.tiles_n;
-    if (tiles > INT32_MAX) return FP8MM_ERR_SHAPE;
     p.num_tiles = (int)tiles;
-    p.k_iters = (int)cdiv(K, c.bk);
+    p.k_iters = (int)k_iters;
     p.rowwise = mode == FP8MM_ROWWISE;
     p.vec_store = (N % 4 == 0) && aligned(out, 8);
+    p.splits = sp;
+    p.k_chunk = (int)cdiv(k_iters, sp);
+    p.counters = nullptr;
+    p.partials = nullptr;
+    if (sp > 1) {
+        p.counters = static_cast<unsigned*>(ws);
+        p.partials = reinterpret_cast<float*>(static_cast<char*>(ws) + kCounterBytes);
+    }
 
-    const dim3 grid((unsigned)grid_for(cfg, M, N, cus));
+    const dim3 grid((unsigned)grid_for(cfg, M, N, sp, cus));
     (void)hipGetLastError();  // clear a stale error from earlier, unrelated calls
-    c.launch(p, grid, reinterpret_cast<hipStream_t>(stream));
+    c.launch(p, grid, hs);
     if (hipGetLastError() != hipSuccess) return FP8MM_ERR_LAUNCH;
     return FP8MM_OK;
+}
+
+int fp8_scaled_mm_with_config(const void* A, const void* B, const float* scale_a,
+                              const float* scale_b, const void* bias, void* out, int64_t M,
+                              int64_t N, int64_t K, int mode, struct ihipStream_t* stream,
+                              int config_id) {
+    return fp8_scaled_mm_with_plan(A, B, scale_a, scale_b, bias, out, M, N, K, mode, stream,
+                                   config_id, 0, nullptr, 0);
 }
 
 int fp8_scaled_mm(const void* A, const void* B, const float* scale_a, const float* scale_b,
                   const void* bias, void* out, int64_t M, int64_t N, int64_t K, int mode,
                   struct ihipStream_t* stream) {
-    return fp8_scaled_mm_with_config(A, B, scale_a, scale_b, bias, out, M, N, K, mode, stream, -1);
+    return fp8_scaled_mm_with_plan(A, B, scale_a, scale_b, bias, out, M, N, K, mode, stream, -1, 0,
+                                   nullptr, 0);
+}
+
+int fp8_scaled_mm_select_splits(int64_t M, int64_t N, int64_t K, int mode, int has_bias,
+                                int config_id) {
+    if (mode != FP8MM_PER_TENSOR && mode != FP8MM_ROWWISE) return -1;
+    if (M <= 0 || N <= 0 || K < 16 || K % 16 != 0 || config_id >= kNumConfigs) return -1;
+    const int cfg = config_id >= 0 ? config_id : choose_config(M, N, K, mode, has_bias);
+    const int sp = choose_splits(cfg, M, N, K);
+    const int64_t k_iters = cdiv(K, kConfigs[cfg].bk);
+    return sp > k_iters ? (int)k_iters : sp;
+}
+
+int64_t fp8_scaled_mm_workspace_size(int64_t M, int64_t N, int64_t K, int mode, int has_bias,
+                                     int config_id, int splits) {
+    if (mode != FP8MM_PER_TENSOR && mode != FP8MM_ROWWISE) return -1;
+    if (M <= 0 || N <= 0 || K < 16 || K % 16 != 0 || config_id >= kNumConfigs) return 0;
+    const int cfg = config_id >= 0 ? config_id : choose_config(M, N, K, mode, has_bias);
+    int sp = splits > 0 ? splits : choose_splits(cfg, M, N, K);
+    const int64_t k_iters = cdiv(K, kConfigs[cfg].bk);
+    if (sp > k_iters) sp = (int)k_iters;
+    if (cdiv(M, kConfigs[cfg].bm) * cdiv(N, kConfigs[cfg].bn) > kMaxSplitTiles ||
+        !kConfigs[cfg].split_ok)
+        sp = 1;
+    return workspace_bytes(cfg, M, N, sp);
 }
 
 }  // extern "C"

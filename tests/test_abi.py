@@ -116,3 +116,32 @@ def test_python_binding_rejects_bad_tensors():
         binding.fp8_scaled_mm(a, a, a, a)
     with pytest.raises(ValueError):
         binding.fp8_scaled_mm(a, a, a, a, mode="columnwise")
+
+
+def test_workspace_and_split_host_logic(L):
+    # a grid that fills the GPU needs no split and no workspace
+    assert L.fp8_scaled_mm_select_splits(8192, 8192, 8192, 0, 0, -1) == 1
+    assert L.fp8_scaled_mm_workspace_size(8192, 8192, 8192, 0, 0, -1, 0) == 0
+    # a few tiles with a long K split, and the workspace covers counters + partials
+    cfg = binding.config_names().index("bm128_bn128_bk128_w2x2_s3_mfma32")
+    s = L.fp8_scaled_mm_select_splits(128, 8192, 28672, 1, 1, cfg)
+    assert s > 1
+    ws = L.fp8_scaled_mm_workspace_size(128, 8192, 28672, 1, 1, cfg, s)
+    tiles = 1 * 64
+    assert ws >= tiles * s * 128 * 128 * 4 + tiles * 4
+    # explicit split counts are clamped to the number of K slices
+    assert L.fp8_scaled_mm_workspace_size(128, 128, 256, 0, 0, cfg, 8) == \
+        L.fp8_scaled_mm_workspace_size(128, 128, 256, 0, 0, cfg, 2)
+    assert L.fp8_scaled_mm_select_splits(16, 16, 16, 5, 0, -1) == -1
+
+
+def test_plan_validation(L):
+    P = 0x10000
+    f = L.fp8_scaled_mm_with_plan
+    cfg = binding.config_names().index("bm128_bn128_bk128_w2x2_s3_mfma32")
+    assert f(P, P, P, P, None, P, 128, 128, 4096, 0, None, cfg, 65, None, 0) == binding.ERR_CONFIG
+    assert f(P, P, P, P, None, P, 128, 128, 4096, 0, None, cfg, -1, None, 0) == binding.ERR_CONFIG
+    # caller workspace too small for a 4-way split
+    assert f(P, P, P, P, None, P, 128, 128, 4096, 0, None, cfg, 4, P, 1024) == binding.ERR_WORKSPACE
+    need = L.fp8_scaled_mm_workspace_size(128, 128, 4096, 0, 0, cfg, 4)
+    assert f(P, P, P, P, None, P, 128, 128, 4096, 0, None, cfg, 4, P + 128, need) == binding.ERR_ALIGN

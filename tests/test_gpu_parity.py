@@ -236,3 +236,68 @@ def test_workload_largest(name):
     print(f"[parity] workload {name} shape={inp.shape}", flush=True)
     out = run_gpu(inp)
     check_sampled(inp, out, n_rows=8, n_cols=8)
+
+
+# ---------------------------------------------------------------- split-K ---
+
+def _cfg(name):
+    return binding.config_names().index(name)
+
+
+@pytest.mark.parametrize("config", ["bm128_bn128_bk128_w2x2_s3_mfma32", "bm16_bn64_bk256_w1x4_s4_mfma16",
+                                    "bm64_bn64_bk128_w4x1_s8_mfma16", "bm64_bn112_bk128_w4x1_s7_mfma16",
+                                    "bm128_bn64_bk128_w4x1_s6_mfma16"])
+@pytest.mark.parametrize("splits", [2, 3, 4, 7])
+@pytest.mark.parametrize("mode", [PT, RW])
+def test_split_k_parity(config, splits, mode):
+    # K = 1040: 9 slices of 128 (last ragged), so splits do not divide it evenly
+    inp = wl.make_inputs(150, 230, 1040, mode, "codes", bias=mode == RW, key=splits * 7 + mode)
+    got = out_bits(run_gpu_plan(inp, _cfg(config), splits))
+    ref = oracle.scaled_mm(inp.a, inp.b, inp.scale_a, inp.scale_b, inp.bias, inp.mode)
+    nbad, worst, first = compare(got, ref)
+    assert nbad == 0, (nbad, worst, first)
+
+
+def run_gpu_plan(inp, config, splits, workspace=None, out=None):
+    a, b = _to_dev(inp.a), _to_dev(inp.b)
+    sa, sb = _to_dev(inp.scale_a), _to_dev(inp.scale_b)
+    bias = _to_dev(inp.bias)
+    out = binding.fp8_scaled_mm(a, b, sa, sb, bias, out=out, mode=inp.mode, config=config,
+                                splits=splits, workspace=workspace)
+    torch.cuda.synchronize()
+    return out
+
+
+def test_split_k_more_splits_than_slices():
+    inp = wl.make_inputs(64, 96, 256, PT, "codes", key=3)
+    got = out_bits(run_gpu_plan(inp, _cfg("bm128_bn128_bk128_w2x2_s3_mfma32"), 16))
+    ref = oracle.scaled_mm(inp.a, inp.b, inp.scale_a, inp.scale_b, None, PT)
+    assert compare(got, ref)[0] == 0
+
+
+def test_split_k_deterministic_and_workspace_equivalent():
+    inp = wl.make_inputs(128, 512, 8192, RW, "normal", bias=True, key=11)
+    cfg = _cfg("bm128_bn128_bk128_w2x2_s3_mfma32")
+    r1 = out_bits(run_gpu_plan(inp, cfg, 8))
+    r2 = out_bits(run_gpu_plan(inp, cfg, 8))
+    need = binding.workspace_size(128, 512, 8192, RW, True, cfg, 8)
+    ws = torch.zeros(need, dtype=torch.uint8, device=DEV)
+    r3 = out_bits(run_gpu_plan(inp, cfg, 8, workspace=ws))
+    r4 = out_bits(run_gpu_plan(inp, cfg, 8, workspace=ws))      # left zero-filled by r3
+    assert np.array_equal(r1, r2) and np.array_equal(r1, r3) and np.array_equal(r1, r4)
+    assert int(ws[:262144].sum()) == 0                            # counters back at zero
+    ref = oracle.scaled_mm(inp.a, inp.b, inp.scale_a, inp.scale_b, inp.bias, RW)
+    assert compare(r1, ref)[0] == 0
+
+
+def test_split_k_changing_plans_on_one_stream():
+    cfg = _cfg("bm128_bn128_bk128_w2x2_s3_mfma32")
+    # the 1-tile plan leaves non-zero partials right after the counters of a
+    # small plan; the 72-tile plan that follows must still find zero counters
+    for i, (shape, splits) in enumerate([((256, 384, 2048), 4), ((128, 256, 4096), 2),
+                                         ((256, 384, 2048), 8), ((300, 130, 1552), 3),
+                                         ((128, 128, 8192), 8), ((1024, 1152, 2048), 2)]):
+        inp = wl.make_inputs(*shape, PT, "codes", key=100 + i)
+        got = out_bits(run_gpu_plan(inp, cfg, splits))
+        ref = oracle.scaled_mm(inp.a, inp.b, inp.scale_a, inp.scale_b, None, PT)
+        assert compare(got, ref)[0] == 0, (shape, splits)
