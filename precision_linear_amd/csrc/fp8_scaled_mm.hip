@@ -78,6 +78,20 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
     return u >> 16;
 }
 
+// One 16-byte-per-lane buffer load that writes LDS directly: lane l's 16
+// bytes from rsrc + voff + soff land at LDS byte address lds + 16*l (lds is
+// wave-uniform and goes to M0).  Written as inline asm so that the compiler
+// does not treat later LDS reads as dependent on it: every wait on these loads
+// is an explicit vmcnt wait placed by the code that issues them.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, const void* lds, uint32_t voff,
+                                      uint32_t soff) {
+    const uint32_t m0 = (uint32_t)(uintptr_t)lds;
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+                 :
+                 : "v"(voff), "s"(rsrc), "s"(soff), "{m0}"(m0)
+                 : "memory");
+}
+
 // Position of 16-byte chunk c of LDS row r is c ^ chunk_swizzle(r).  The MFMA
 // operand reads have 8 (or 16) consecutive lanes read the same logical chunk
 // of 8 (16) consecutive rows; the mask makes those land in distinct banks
@@ -161,6 +175,9 @@ struct Cfg {
     // partials, so it is compiled only where both fit in registers.
     static constexpr int PER_LANE_ACC = FM * FN * (MI == 32 ? 16 : 4);
     static constexpr bool SPLIT_OK = PER_LANE_ACC <= 64;
+    // Spread a stage's loads between MFMAs only where a K step has enough
+    // MFMAs to hide them (the big, MFMA-bound tiles).
+    static constexpr bool INTERLEAVE = MI == 32 && FM * FN >= 8;
     static constexpr int BK_ = BK;
     static constexpr int STAGES_ = STAGES;
     static_assert(WTM % MI == 0 && WTN % MI == 0, "wave tile must hold whole MFMA tiles");
@@ -192,8 +209,7 @@ __device__ __forceinline__ void load_stage(uint8_t* lds_stage, __amdgpu_buffer_r
         const int c = pos ^ chunk_swizzle<C::CPR>(r);
         const int k = k0 + c * 16;
         const uint32_t off = k < klim ? (uint32_t)(r * ld + k) : kOutOfRange;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            ra, (lds_void_t*)(lds_stage + blk * 1024), 16, off, 0, 0, 0);
+        dma16(ra, lds_stage + blk * 1024, off, 0);
     }
 #pragma unroll
     for (int i = 0; i < C::B_LOADS; ++i) {
@@ -202,8 +218,56 @@ __device__ __forceinline__ void load_stage(uint8_t* lds_stage, __amdgpu_buffer_r
         const int c = pos ^ chunk_swizzle<C::CPR>(r);
         const int k = k0 + c * 16;
         const uint32_t off = k < klim ? (uint32_t)(r * ld + k) : kOutOfRange;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rb, (lds_void_t*)(lds_stage + C::A_BYTES + blk * 1024), 16, off, 0, 0, 0);
+        dma16(rb, lds_stage + C::A_BYTES + blk * 1024, off, 0);
+    }
+}
+
+// Load number `idx` (0 <= idx < LOADS) of this wave for one K slice: the
+// first A_LOADS go to the A tile, the rest to the B tile.  With live == false
+// every lane reads out of range (zeros land in a buffer nobody reads again);
+// this keeps the number of loads per stage fixed, which the vmcnt waits use.
+template <class C, int idx>
+__device__ __forceinline__ void load_one(uint8_t* lds_stage, __amdgpu_buffer_rsrc_t ra,
+                                         __amdgpu_buffer_rsrc_t rb, int ld, int klim, int k0,
+                                         int wave, int l, bool live) {
+    constexpr int RPB = 1024 / (C::CPR * 16);
+    constexpr bool IS_A = idx < C::A_LOADS;
+    constexpr int i = IS_A ? idx : idx - C::A_LOADS;
+    const int blk = min(wave + i * C::WAVES, (IS_A ? C::A_BLOCKS : C::B_BLOCKS) - 1);
+    const int rr = l / C::CPR;
+    const int pos = l % C::CPR;
+    const int r = blk * RPB + rr;
+    const int c = pos ^ chunk_swizzle<C::CPR>(r);
+    const int k = k0 + c * 16;
+    const uint32_t off = (live && k < klim) ? (uint32_t)(r * ld + k) : kOutOfRange;
+    dma16(IS_A ? ra : rb, lds_stage + (IS_A ? 0 : C::A_BYTES) + blk * 1024, off, 0);
+}
+
+template <class C, int LO, int HI>
+__device__ __forceinline__ void load_range(uint8_t* lds_stage, __amdgpu_buffer_rsrc_t ra,
+                                           __amdgpu_buffer_rsrc_t rb, int ld, int klim, int k0,
+                                           int wave, int l, bool live) {
+    if constexpr (LO < HI) {
+        load_one<C, LO>(lds_stage, ra, rb, ld, klim, k0, wave, l, live);
+        load_range<C, LO + 1, HI>(lds_stage, ra, rb, ld, klim, k0, wave, l, live);
+    }
+}
+
+template <class C, int Q>
+__device__ __forceinline__ void mfma_with_loads(typename Mfma<C::MI_>::acc_t (&acc)[C::FN][C::FM],
+                                                const v8i (&fa)[C::FM], const v8i (&fb)[C::FN],
+                                                uint8_t* lds_stage, __amdgpu_buffer_rsrc_t ra,
+                                                __amdgpu_buffer_rsrc_t rb, int ld, int klim, int k0,
+                                                int wave, int l, bool live) {
+    constexpr int NQ = C::FN * C::FM;
+    if constexpr (Q < NQ) {
+        constexpr int i = Q / C::FM, j = Q % C::FM;
+        acc[i][j] = Mfma<C::MI_>::run(fb[i], fa[j], acc[i][j]);
+        // the share of loads issued after MFMA Q of NQ
+        load_range<C, Q * C::LOADS / NQ, (Q + 1) * C::LOADS / NQ>(lds_stage, ra, rb, ld, klim, k0,
+                                                                  wave, l, live);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_with_loads<C, Q + 1>(acc, fa, fb, lds_stage, ra, rb, ld, klim, k0, wave, l, live);
     }
 }
 
@@ -279,16 +343,39 @@ __device__ __forceinline__ void run_stage(typename Mfma<C::MI_>::acc_t (&acc)[C:
         if (ks + 1 < C::NKS) {
             read_frags<C>(fa[cur ^ 1], fb[cur ^ 1], st, ks + 1, wm, wn, lane);
         } else if (HAS_NEXT) {
-            // Loads issued so far cover slices 0 .. min(kt+S-1, k_iters-1);
-            // slice kt+1 has landed once the S-2 newest slices remain.
-            if (kt + S - 1 < k_iters) wait_vmcnt<C::LOADS * (S - 2)>();
-            else wait_vmcnt<0>();
-            barrier_lds();
-            if (kt + S < k_iters)
-                load_stage<C>(smem + (kt % S) * C::STAGE_BYTES, ra, rb, ld, klim, (kt + S) * C::BK_,
-                              wave, lane);
-            read_frags<C>(fa[cur ^ 1], fb[cur ^ 1], smem + ((kt + 1) % S) * C::STAGE_BYTES, 0, wm,
-                          wn, lane);
+            if constexpr (C::INTERLEAVE) {
+                // Every earlier stage issued exactly LOADS loads per wave (dead
+                // ones read out of range), so slice kt+1 has landed once the
+                // S-2 newest slices' loads remain.
+                wait_vmcnt<C::LOADS * (S - 2)>();
+                barrier_lds();
+                // The buffer just released is refilled with slice kt+S.
+                // MFMA-bound tiles: the loads are spread between this step's
+                // MFMAs; issued as one burst they stall the wave in the memory
+                // pipeline's queue while the MFMA unit idles.
+                read_frags<C>(fa[cur ^ 1], fb[cur ^ 1], smem + ((kt + 1) % S) * C::STAGE_BYTES, 0,
+                              wm, wn, lane);
+                __builtin_amdgcn_sched_barrier(0);
+                int l = lane;
+                asm volatile("" : "+v"(l));
+                mfma_with_loads<C, 0>(acc, fa[cur], fb[cur], smem + (kt % S) * C::STAGE_BYTES, ra,
+                                      rb, ld, klim, (kt + S) * C::BK_, wave, l, kt + S < k_iters);
+                continue;
+            } else {
+                // Memory-bound tiles: the loads go out first, as early as
+                // possible, and only for slices that exist.  Loads issued so
+                // far cover slices up to min(kt+S-1, k_iters-1) (the prologue
+                // may add dead ones past the end); slice kt+1 has landed once
+                // the S-2 newest slices remain, near the end once none do.
+                if (kt + S - 1 < k_iters) wait_vmcnt<C::LOADS * (S - 2)>();
+                else wait_vmcnt<0>();
+                barrier_lds();
+                if (kt + S < k_iters)
+                    load_stage<C>(smem + (kt % S) * C::STAGE_BYTES, ra, rb, ld, klim,
+                                  (kt + S) * C::BK_, wave, lane);
+                read_frags<C>(fa[cur ^ 1], fb[cur ^ 1], smem + ((kt + 1) % S) * C::STAGE_BYTES, 0,
+                              wm, wn, lane);
+            }
         }
         // Keep the compiler from sinking the LDS reads below the MFMAs: they
         // must be in flight while the MFMAs of this step run.
@@ -381,8 +468,8 @@ fp8_gemm_kernel(Params p) {
         // slice kt + STAGES once stage kt has been read.
 #pragma unroll
         for (int s = 0; s < STAGES; ++s)
-            if (s < k_iters)
-                load_stage<C>(smem + s * C::STAGE_BYTES, ra, rb, p.K, klim, s * BK, wave, lane);
+            load_stage<C>(smem + s * C::STAGE_BYTES, ra, rb, p.K, s < k_iters ? klim : 0, s * BK,
+                          wave, lane);
 
         // Software pipeline over K steps: the operand fragments of step q+1 are
         // read from LDS while the MFMAs of step q run.  At the last step of a
@@ -391,8 +478,7 @@ fp8_gemm_kernel(Params p) {
         // loads STAGES slices ahead, and reads the next stage's first fragments;
         // the barrier therefore sits under the tail of the previous MFMAs.
         v8i fa[2][C::FM], fb[2][C::FN];
-        if (STAGES - 1 < k_iters) wait_vmcnt<C::LOADS * (STAGES - 1)>();   // stage 0 landed
-        else wait_vmcnt<0>();
+        wait_vmcnt<C::LOADS * (STAGES - 1)>();   // stage 0 landed (S-1 newer slices may not)
         barrier_lds();
         if (k_iters > 0) read_frags<C>(fa[0], fb[0], smem, 0, wm, wn, lane);
 
