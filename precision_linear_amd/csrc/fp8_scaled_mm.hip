@@ -56,6 +56,7 @@ struct Params {
     int tiles_m, tiles_n, num_tiles, k_iters;
     int rowwise;
     int vec_store;         // N % 4 == 0 and out 8-byte aligned
+    int vec16;             // N % 8 == 0 and out 16-byte aligned
     // Split-K: each output tile is computed by `splits` work units, unit s
     // covering K slices [s*k_chunk, (s+1)*k_chunk).  With splits > 1 the fp32
     // partial tiles go to `partials` and the unit that arrives last at the
@@ -68,14 +69,6 @@ struct Params {
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
                                              (int)kBufferWord3);
-}
-
-// fp32 -> bf16, round to nearest even; NaN -> quiet NaN with the sign kept.
-__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return ((u >> 16) & 0x8000u) | 0x7fc0u;
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return u >> 16;
 }
 
 // One 16-byte-per-lane buffer load that writes LDS directly: lane l's 16
@@ -318,6 +311,120 @@ __device__ __forceinline__ void wait_vmcnt() {
     // expcnt [6:4] and lgkmcnt [11:8] left at their maxima (no wait).
     static_assert(N >= 0 && N <= 63, "vmcnt range");
     __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Two fp32 -> bf16 conversions, round to nearest even, packed low | high << 16
+// (one v_cvt_pk_bf16_f32; fp32 denormals are kept, so the bf16 denormal range
+// rounds like the rest).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{lo, hi}, bf2));
+}
+
+// Epilogue of one wave's FM x FN blocks of MI x MI outputs, whose top-left
+// corner is (row0 + mbase, col0 + nbase).  The MFMA was fed B as its first
+// operand, so lane l holds output row m = l % MI of each block and runs of 4
+// consecutive columns n.  Row-wise scales and bias come from the LDS copies of
+// the tile's parameters (indexed from the tile's corner).  y = acc * s, or
+// fma(acc, s, bias) with a bias, with s = sa * sb formed in fp32; then RNE.
+// RW, BIAS and FULL (the wave's block lies inside the output and 8-byte stores
+// are allowed) are compile-time, so the block has no branches; all parameters
+// are read from LDS before the first use.
+template <int MI, int FM, int FN, bool RW, bool BIAS, bool FULL>
+__device__ __forceinline__ void store_tile_impl(const typename Mfma<MI>::acc_t (&acc)[FN][FM],
+                                                const Params& p, int row0, int col0, int mbase,
+                                                int nbase, const float* epi_sa,
+                                                const float* epi_sb, const uint16_t* epi_bias,
+                                                float s_pt, int lane) {
+    constexpr int G = Mfma<MI>::NACC / 4;   // runs of 4 columns per block and lane
+    auto col = [&](int i, int g) {
+        return nbase + i * MI + (MI == 32 ? 8 * g + 4 * (lane / 32) : 4 * (lane / 16));
+    };
+    float sa_r[FM];
+    v4f sb_r[FN][G];
+    uint2 b_r[FN][G];
+#pragma unroll
+    for (int j = 0; j < FM; ++j) sa_r[j] = RW ? epi_sa[mbase + j * MI + lane % MI] : s_pt;
+#pragma unroll
+    for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            if constexpr (RW) sb_r[i][g] = *reinterpret_cast<const v4f*>(epi_sb + col(i, g));
+            if constexpr (BIAS) b_r[i][g] = *reinterpret_cast<const uint2*>(epi_bias + col(i, g));
+        }
+#pragma unroll
+    for (int j = 0; j < FM; ++j) {
+        const int ml = mbase + j * MI + lane % MI;
+        const int m = row0 + ml;
+        if (!FULL && m >= p.M) continue;
+        uint16_t* orow = p.out + (size_t)m * p.N + col0;
+#pragma unroll
+        for (int i = 0; i < FN; ++i)
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                const int nl = col(i, g);
+                if (!FULL && col0 + nl >= p.N) continue;
+                float y[4];
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const float sc = RW ? sa_r[j] * sb_r[i][g][c] : s_pt;
+                    const float v = acc[i][j][4 * g + c];
+                    if constexpr (BIAS) {
+                        const uint32_t bw = c < 2 ? b_r[i][g].x : b_r[i][g].y;
+                        const float bv = __uint_as_float(c % 2 == 0 ? bw << 16 : bw & 0xffff0000u);
+                        y[c] = __builtin_fmaf(v, sc, bv);
+                    } else {
+                        y[c] = v * sc;
+                    }
+                }
+                const uint32_t lo = pack_bf16x2(y[0], y[1]);
+                const uint32_t hi = pack_bf16x2(y[2], y[3]);
+                if (FULL || (p.vec_store && col0 + nl + 3 < p.N)) {
+                    uint2 w;
+                    w.x = lo;
+                    w.y = hi;
+                    *reinterpret_cast<uint2*>(orow + nl) = w;
+                } else {
+                    const uint16_t h[4] = {(uint16_t)lo, (uint16_t)(lo >> 16), (uint16_t)hi,
+                                           (uint16_t)(hi >> 16)};
+#pragma unroll
+                    for (int c = 0; c < 4; ++c)
+                        if (col0 + nl + c < p.N) orow[nl + c] = h[c];
+                }
+            }
+    }
+}
+
+template <int MI, int FM, int FN>
+__device__ __forceinline__ void store_tile(const typename Mfma<MI>::acc_t (&acc)[FN][FM],
+                                           const Params& p, int row0, int col0, int mbase,
+                                           int nbase, const float* epi_sa, const float* epi_sb,
+                                           const uint16_t* epi_bias, float s_pt, bool has_bias,
+                                           int lane) {
+    // Derive every epilogue address from an opaque copy of the lane id, so the
+    // compiler cannot hoist them out of the tile loop and keep them live (in
+    // registers the K loop needs) across it.
+    asm volatile("" : "+v"(lane));
+    const bool full = p.vec_store && row0 + mbase + FM * MI <= p.M &&
+                      col0 + nbase + FN * MI <= p.N;   // wave-uniform
+#define FP8MM_EPI(RW, BIAS, FULL)                                                               \
+    store_tile_impl<MI, FM, FN, RW, BIAS, FULL>(acc, p, row0, col0, mbase, nbase, epi_sa, epi_sb, \
+                                                epi_bias, s_pt, lane)
+    if (full) {
+        if (p.rowwise) {
+            if (has_bias) FP8MM_EPI(true, true, true); else FP8MM_EPI(true, false, true);
+        } else {
+            if (has_bias) FP8MM_EPI(false, true, true); else FP8MM_EPI(false, false, true);
+        }
+    } else {
+        if (p.rowwise) {
+            if (has_bias) FP8MM_EPI(true, true, false); else FP8MM_EPI(true, false, false);
+        } else {
+            if (has_bias) FP8MM_EPI(false, true, false); else FP8MM_EPI(false, false, false);
+        }
+    }
+#undef FP8MM_EPI
 }
 
 // One K stage (BK bytes of K) of the software pipeline.  The fragments of
@@ -588,61 +695,395 @@ fp8_gemm_kernel(Params p) {
             barrier_lds();
         }
 
-        // Epilogue.  The MFMA was fed B as its first operand, so lane l holds
-        // output row m = l % MI of each sub-tile and runs of 4 consecutive
-        // columns n.
+        store_tile<MI, C::FM, C::FN>(acc, p, row0, col0, wm * C::WTM, wn * C::WTN, epi_sa, epi_sb,
+                                     epi_bias, s_pt, has_bias, lane);
+    }
+}
+
+// ------------------------------------------------------ ping-pong kernel ---
+//
+// 256 x 256 output tiles, K slices of 128 bytes, 8 waves in two groups of four
+// with one wave of each group on every SIMD (waves w and w+4 share SIMD w).
+// Group 1 runs one phase behind group 0, so on every SIMD one wave issues the
+// 16 MFMAs of a K slice from registers while the other reads its fragments of
+// that slice from LDS and issues global -> LDS loads; at the end of each phase a
+// workgroup barrier swaps the roles.  Wave (g, q) computes rows g*128 .. +128
+// and columns q*64 .. +64 of the tile with fp32 accumulators in registers.
+//
+// Two LDS stage buffers, slice s in buffer s % 2, each holding the slice's A
+// rows 0-127 ("A-top", read only by group 0), A rows 128-255 ("A-bottom", read
+// only by group 1) and B (read by both).  Group 0 reads slice s in phase 2s,
+// group 1 in phase 2s+1.  The loads are issued in memory phases only, 8 per wave
+// per phase:
+//   phase 2s   (group 0): B of slice s+1        (its buffer was last read in 2s-1)
+//   phase 2s+1 (group 1): A-bottom of slice s+1 (last read in 2s-1) and A-top of
+//                         slice s+2             (last read in 2s)
+// and each wave waits for its own loads (vmcnt 0) at the end of its next
+// compute phase, before the barrier after which the data is first read.
+// Between tiles, group 0 issues the next tile's first slices and its
+// epilogue parameters right after its last compute phase, then writes its
+// outputs while group 1 finishes.
+namespace pp {
+constexpr int BM = 256, BN = 256, BK = 128;
+constexpr int WAVES = 8;
+constexpr int THREADS = WAVES * kWave;
+constexpr int CPR = BK / 16;                        // 16-byte chunks per LDS row
+constexpr int A_BYTES = BM * BK;                    // 32 KiB
+constexpr int HALF_A = A_BYTES / 2;                 // A-top / A-bottom, 16 KiB
+constexpr int STAGE_BYTES = (BM + BN) * BK;         // 64 KiB
+constexpr int MAIN_BYTES = 2 * STAGE_BYTES;
+constexpr int FM = 4, FN = 2;                       // 32 x 32 blocks per wave
+constexpr int KSTEPS = BK / Mfma<32>::KSTEP;        // 2 MFMA K steps per slice
+constexpr int NOFF = 8;                             // load row groups per wave
+constexpr int EPI_BYTES = BM * 4 + BN * 4 + BN * 2; // row scales, column scales, bias
+// Output staging: group 0's waves use 4 KiB each after the parameters; group 1's
+// waves use the A-bottom part of stage buffer 1, which is idle while they write
+// their outputs (the next tile's first loads fill buffer 0 and buffer 1's A-top).
+constexpr int STG_BYTES = 4096;
+constexpr int STG0 = MAIN_BYTES + 2 * EPI_BYTES;
+constexpr int STG1 = STAGE_BYTES + HALF_A;
+constexpr int LDS_BYTES = STG0 + 4 * STG_BYTES;
+static_assert(LDS_BYTES <= 160 * 1024, "gfx950 LDS is 160 KiB per workgroup");
+static_assert(4 * STG_BYTES <= HALF_A, "group 1 staging fits in the A-bottom half");
+}  // namespace pp
+
+// Per-lane load offsets of wave q (0..3 within its group): offset i covers LDS
+// block q + 4i (rows 8*(q + 4i) .. +8 of a 256-row panel, 1 KiB); lane l fills
+// position l % 8 of row 8*(q + 4i) + l / 8 with logical chunk (l % 8) ^
+// swizzle(row).  Row bits 0..3 are the same for every i, so is the chunk.
+struct PpLoads {
+    uint32_t off[pp::NOFF];   // row * K + chunk * 16
+    uint32_t cbyte;           // chunk * 16
+    uint32_t bot;             // 128 * K: A-bottom rows relative to A-top rows
+};
+
+__device__ __forceinline__ void pp_dma(__amdgpu_buffer_rsrc_t r, uint8_t* dst, uint32_t off,
+                                       uint32_t k0, bool inside) {
+    dma16(r, dst, inside ? off : kOutOfRange, k0);
+}
+
+// Loads of slice s (K bytes s*BK ..) into stage buffer buf.  In the K-tail
+// slice, lanes whose chunk lies at or past K read zeros (offset beyond the
+// record limit).
+__device__ __forceinline__ void pp_load_b(uint8_t* smem, int buf, int q, int s,
+                                          __amdgpu_buffer_rsrc_t rb, const PpLoads& L, int K) {
+    const uint32_t k0 = (uint32_t)s * pp::BK;
+    const bool inside = k0 + L.cbyte < (uint32_t)K;
+    uint8_t* st = smem + buf * pp::STAGE_BYTES + pp::A_BYTES;
 #pragma unroll
-        for (int j = 0; j < C::FM; ++j) {
-            const int ml = wm * C::WTM + j * MI + lane % MI;
-            const int m = row0 + ml;
-            if (m >= p.M) continue;
-            const float sa_m = p.rowwise ? epi_sa[ml] : 0.f;
-            uint16_t* orow = p.out + (size_t)m * p.N;
+    for (int i = 0; i < pp::NOFF; ++i) pp_dma(rb, st + (q + 4 * i) * 1024, L.off[i], k0, inside);
+}
+
+template <bool BOTTOM>
+__device__ __forceinline__ void pp_load_a_half(uint8_t* smem, int buf, int q, int s,
+                                               __amdgpu_buffer_rsrc_t ra, const PpLoads& L, int K) {
+    const uint32_t k0 = (uint32_t)s * pp::BK;
+    const bool inside = k0 + L.cbyte < (uint32_t)K;
+    uint8_t* st = smem + buf * pp::STAGE_BYTES + (BOTTOM ? pp::HALF_A : 0);
 #pragma unroll
-            for (int i = 0; i < C::FN; ++i) {
+    for (int i = 0; i < pp::NOFF / 2; ++i)
+        pp_dma(ra, st + (q + 4 * i) * 1024, L.off[i] + (BOTTOM ? L.bot : 0u), k0, inside);
+}
+
+// Fragments of one slice for wave (grp, q): A rows grp*128 + j*32 + l, B rows
+// q*64 + i*32 + l; lanes 32..63 take K bytes 32..63 of each 64-byte step.
+__device__ __forceinline__ void pp_read(v8i (&fa)[pp::KSTEPS][pp::FM],
+                                        v8i (&fb)[pp::KSTEPS][pp::FN], const uint8_t* st, int grp,
+                                        int q, int lane) {
+    // Addresses are recomputed here from an opaque copy of the lane id: kept
+    // live across the loop they would cost registers the fragments need.
+    int l = lane % 32;
+    int lh = lane / 32;
+    asm volatile("" : "+v"(l), "+v"(lh));
 #pragma unroll
-                for (int g = 0; g < F::NACC / 4; ++g) {
-                    const int nl = wn * C::WTN + i * MI +
-                                   (MI == 32 ? 8 * g + 4 * (lane / 32) : 4 * (lane / 16));
-                    const int n = col0 + nl;
-                    if (n >= p.N) continue;
-                    float s4[4], b4[4];
-                    if (p.rowwise) {
-                        const v4f sb4 = *reinterpret_cast<const v4f*>(epi_sb + nl);
+    for (int ks = 0; ks < pp::KSTEPS; ++ks) {
+        const int c0 = ks * 4 + lh * 2;
 #pragma unroll
-                        for (int c = 0; c < 4; ++c) s4[c] = sa_m * sb4[c];
+        for (int j = 0; j < pp::FM; ++j)
+            fa[ks][j] = read_frag<pp::CPR>(st, grp * 128 + j * 32, l, c0);
+#pragma unroll
+        for (int i = 0; i < pp::FN; ++i)
+            fb[ks][i] = read_frag<pp::CPR>(st + pp::A_BYTES, q * 64 + i * 32, l, c0);
+    }
+}
+
+// The 16 MFMAs of one slice, from registers only.
+__device__ __forceinline__ void pp_compute(v16f (&acc)[pp::FN][pp::FM],
+                                           const v8i (&fa)[pp::KSTEPS][pp::FM],
+                                           const v8i (&fb)[pp::KSTEPS][pp::FN]) {
+#pragma unroll
+    for (int ks = 0; ks < pp::KSTEPS; ++ks)
+#pragma unroll
+        for (int i = 0; i < pp::FN; ++i)
+#pragma unroll
+            for (int j = 0; j < pp::FM; ++j)
+                acc[i][j] = Mfma<32>::run(fb[ks][i], fa[ks][j], acc[i][j]);
+}
+
+struct PpTile {
+    int row0, col0;
+    __amdgpu_buffer_rsrc_t ra, rb;
+};
+
+__device__ __forceinline__ PpTile pp_tile(const Params& p, int t, int group_m) {
+    PpTile T;
+    int pm, pn;
+    tile_coords(t, p.tiles_m, p.tiles_n, group_m, pm, pn);
+    T.row0 = pm * pp::BM;
+    T.col0 = pn * pp::BN;
+    const uint32_t rows_a = (uint32_t)min(pp::BM, p.M - T.row0);
+    const uint32_t rows_b = (uint32_t)min(pp::BN, p.N - T.col0);
+    T.ra = make_rsrc(p.A + (size_t)T.row0 * p.K, rows_a * (uint32_t)p.K);
+    T.rb = make_rsrc(p.B + (size_t)T.col0 * p.K, rows_b * (uint32_t)p.K);
+    return T;
+}
+
+// A tile's first loads, all from group 0 (wave q): its first K slice (s0)
+// whole and A-top of its second (s1); plus the tile's epilogue parameters (thread q*64 + lane takes row /
+// column q*64 + lane) into the given LDS area.
+__device__ __forceinline__ void pp_tile_start(uint8_t* smem, const Params& p, const PpTile& T,
+                                              const PpLoads& L, int q, int lane, int s0, int s1,
+                                              bool need_epi, bool has_bias, float* epi_sa,
+                                              float* epi_sb, uint16_t* epi_bias) {
+    pp_load_b(smem, 0, q, s0, T.rb, L, p.K);
+    pp_load_a_half<false>(smem, 0, q, s0, T.ra, L, p.K);
+    pp_load_a_half<true>(smem, 0, q, s0, T.ra, L, p.K);
+    if (p.k_iters > 1) pp_load_a_half<false>(smem, 1, q, s1, T.ra, L, p.K);
+    if (need_epi) {
+        const int r = q * kWave + lane;   // 0..255
+        float pa = 0.f, pb = 0.f;
+        uint16_t pbias = 0;
+        if (p.rowwise) {
+            pa = T.row0 + r < p.M ? p.scale_a[T.row0 + r] : 0.f;
+            pb = T.col0 + r < p.N ? p.scale_b[T.col0 + r] : 0.f;
+        }
+        if (has_bias && T.col0 + r < p.N) pbias = p.bias[T.col0 + r];
+        epi_sa[r] = pa;
+        epi_sb[r] = pb;
+        epi_bias[r] = pbias;
+    }
+}
+
+// Epilogue of wave (g, q) of the ping-pong kernel through a private 4 KiB LDS
+// area: each 32 x 64 block row of its outputs is written to LDS in the MFMA
+// layout (row l % 32, 4 columns per lane) and read back as 8 rows x 128 bytes
+// per instruction, so every global store writes 8 whole 128-byte lines
+// (instead of 32 pieces of 16 bytes).  LDS operations of one wave complete in
+// order, so no barrier is needed.  In the LDS area, 16-byte chunk c of row r
+// sits at c ^ ((r >> 1) & 7) (at most 2-way bank conflicts on the writes).
+// Falls back to store_tile where the block is not wholly inside the output or
+// 16-byte stores are not allowed.
+template <bool RW, bool BIAS>
+__device__ __forceinline__ void pp_store_staged(const v16f (&acc)[pp::FN][pp::FM], const Params& p,
+                                                int row0, int col0, int mbase, int nbase,
+                                                const float* epi_sa, const float* epi_sb,
+                                                const uint16_t* epi_bias, float s_pt, int lane,
+                                                uint8_t* stg) {
+    constexpr int FM = pp::FM, FN = pp::FN;
+    float sa_r[FM];
+    v4f sb_r[FN][4];
+    uint2 b_r[FN][4];
+    const int h = lane / 32;
+#pragma unroll
+    for (int j = 0; j < FM; ++j) sa_r[j] = RW ? epi_sa[mbase + j * 32 + lane % 32] : s_pt;
+#pragma unroll
+    for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const int nl = nbase + i * 32 + 8 * g + 4 * h;
+            if constexpr (RW) sb_r[i][g] = *reinterpret_cast<const v4f*>(epi_sb + nl);
+            if constexpr (BIAS) b_r[i][g] = *reinterpret_cast<const uint2*>(epi_bias + nl);
+        }
+    const int r = lane % 32;
+#pragma unroll
+    for (int j = 0; j < FM; ++j) {
+#pragma unroll
+        for (int i = 0; i < FN; ++i)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                float y[4];
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const float sc = RW ? sa_r[j] * sb_r[i][g][c] : s_pt;
+                    const float v = acc[i][j][4 * g + c];
+                    if constexpr (BIAS) {
+                        const uint32_t bw = c < 2 ? b_r[i][g].x : b_r[i][g].y;
+                        const float bv = __uint_as_float(c % 2 == 0 ? bw << 16 : bw & 0xffff0000u);
+                        y[c] = __builtin_fmaf(v, sc, bv);
                     } else {
-#pragma unroll
-                        for (int c = 0; c < 4; ++c) s4[c] = s_pt;
-                    }
-                    if (has_bias) {
-                        const uint2 bb = *reinterpret_cast<const uint2*>(epi_bias + nl);
-                        b4[0] = __uint_as_float(bb.x << 16);
-                        b4[1] = __uint_as_float(bb.x & 0xffff0000u);
-                        b4[2] = __uint_as_float(bb.y << 16);
-                        b4[3] = __uint_as_float(bb.y & 0xffff0000u);
-                    }
-                    uint32_t h[4];
-#pragma unroll
-                    for (int c = 0; c < 4; ++c) {
-                        const float y = acc[i][j][4 * g + c];
-                        h[c] = f32_to_bf16_rne(has_bias ? __builtin_fmaf(y, s4[c], b4[c])
-                                                        : y * s4[c]);
-                    }
-                    if (p.vec_store && n + 3 < p.N) {
-                        uint2 w;
-                        w.x = h[0] | (h[1] << 16);
-                        w.y = h[2] | (h[3] << 16);
-                        *reinterpret_cast<uint2*>(orow + n) = w;
-                    } else {
-#pragma unroll
-                        for (int c = 0; c < 4; ++c)
-                            if (n + c < p.N) orow[n + c] = (uint16_t)h[c];
+                        y[c] = v * sc;
                     }
                 }
+                uint2 w;
+                w.x = pack_bf16x2(y[0], y[1]);
+                w.y = pack_bf16x2(y[2], y[3]);
+                const int cpos = (i * 4 + g) ^ ((r >> 1) & 7);
+                *reinterpret_cast<uint2*>(stg + r * 128 + cpos * 16 + h * 8) = w;
             }
+#pragma unroll
+        for (int pass = 0; pass < 4; ++pass) {
+            const int rr = pass * 8 + lane / 8;
+            const int cc = lane % 8;
+            const v4i v = *reinterpret_cast<const v4i*>(stg + rr * 128 + ((cc ^ ((rr >> 1) & 7)) * 16));
+            uint16_t* dst = p.out + (size_t)(row0 + mbase + j * 32 + rr) * p.N + col0 + nbase + cc * 8;
+            *reinterpret_cast<v4i*>(dst) = v;
         }
     }
+}
+
+__device__ __forceinline__ void pp_store(const v16f (&acc)[pp::FN][pp::FM], const Params& p,
+                                         int row0, int col0, int mbase, int nbase,
+                                         const float* epi_sa, const float* epi_sb,
+                                         const uint16_t* epi_bias, float s_pt, bool has_bias,
+                                         int lane, uint8_t* stg) {
+    asm volatile("" : "+v"(lane));
+    const bool full = p.vec16 && row0 + mbase + pp::FM * 32 <= p.M &&
+                      col0 + nbase + pp::FN * 32 <= p.N;   // wave-uniform
+    if (!full) {
+        store_tile<32, pp::FM, pp::FN>(acc, p, row0, col0, mbase, nbase, epi_sa, epi_sb, epi_bias,
+                                       s_pt, has_bias, lane);
+        return;
+    }
+    if (p.rowwise) {
+        if (has_bias)
+            pp_store_staged<true, true>(acc, p, row0, col0, mbase, nbase, epi_sa, epi_sb, epi_bias,
+                                        s_pt, lane, stg);
+        else
+            pp_store_staged<true, false>(acc, p, row0, col0, mbase, nbase, epi_sa, epi_sb, epi_bias,
+                                         s_pt, lane, stg);
+    } else {
+        if (has_bias)
+            pp_store_staged<false, true>(acc, p, row0, col0, mbase, nbase, epi_sa, epi_sb, epi_bias,
+                                         s_pt, lane, stg);
+        else
+            pp_store_staged<false, false>(acc, p, row0, col0, mbase, nbase, epi_sa, epi_sb,
+                                          epi_bias, s_pt, lane, stg);
+    }
+}
+
+template <int GROUP_M>
+__global__ void __launch_bounds__(pp::THREADS) fp8_gemm_pp_kernel(Params p) {
+    using namespace pp;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[LDS_BYTES];
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int lane = tid % kWave;
+    const int grp = wave / 4;
+    const int q = wave % 4;
+
+    const int G = gridDim.x;
+    int wg = blockIdx.x;
+    if (G % kXcds == 0) wg = (blockIdx.x % kXcds) * (G / kXcds) + blockIdx.x / kXcds;
+    if (wg >= p.num_tiles) return;   // whole workgroup
+    // The workgroups of XCD x walk K starting at slice x * k_iters / 8 (and
+    // wrap): the XCDs finish their tiles at different times, so the output
+    // stores of the whole GPU do not all arrive at once.  The 32 workgroups of
+    // one XCD stay in step and keep sharing the slices in its L2.
+    const int k_iters = p.k_iters;
+    const int rot = G % kXcds == 0 ? (int)(blockIdx.x % kXcds) * k_iters / kXcds : 0;
+    auto slice = [&](int step) { return step + rot < k_iters ? step + rot : step + rot - k_iters; };
+
+    PpLoads L;
+    L.cbyte = (uint32_t)(((lane % 8) ^ chunk_swizzle<CPR>((q & 1) * 8 + lane / 8)) * 16);
+#pragma unroll
+    for (int i = 0; i < NOFF; ++i)
+        L.off[i] = (uint32_t)((8 * (q + 4 * i) + lane / 8) * p.K) + L.cbyte;
+    L.bot = 128u * (uint32_t)p.K;
+
+    const float s_pt = p.rowwise ? 0.f : p.scale_a[0] * p.scale_b[0];
+    const bool has_bias = p.bias != nullptr;
+    const bool need_epi = p.rowwise || has_bias;
+    auto epi_area = [&](int parity, float*& sa, float*& sb, uint16_t*& bias) {
+        sa = reinterpret_cast<float*>(smem + MAIN_BYTES + parity * EPI_BYTES);
+        sb = sa + BM;
+        bias = reinterpret_cast<uint16_t*>(sb + BN);
+    };
+
+    int parity = 0;
+    PpTile T = pp_tile(p, wg, GROUP_M);
+    if (grp == 0) {
+        float *sa, *sb;
+        uint16_t* bias;
+        epi_area(0, sa, sb, bias);
+        pp_tile_start(smem, p, T, L, q, lane, slice(0), slice(1), need_epi, has_bias, sa, sb, bias);
+        wait_vmcnt<0>();
+    }
+    barrier_lds();
+    __builtin_amdgcn_sched_barrier(0);
+
+    for (int t = wg; t < p.num_tiles; t += G, parity ^= 1) {
+        v16f acc[FN][FM];
+#pragma unroll
+        for (int i = 0; i < FN; ++i)
+#pragma unroll
+            for (int j = 0; j < FM; ++j) acc[i][j] = v16f{};
+        v8i fa[KSTEPS][FM], fb[KSTEPS][FN];
+        float *epi_sa, *epi_sb;
+        uint16_t* epi_bias;
+        epi_area(parity, epi_sa, epi_sb, epi_bias);
+
+        if (grp == 0) {
+            for (int s = 0; s < k_iters; ++s) {
+                // memory phase 2s: fragments of slice s, B of slice s+1
+                pp_read(fa, fb, smem + (s & 1) * STAGE_BYTES, 0, q, lane);
+                if (s + 1 < k_iters) pp_load_b(smem, (s + 1) & 1, q, slice(s + 1), T.rb, L, p.K);
+                barrier_lds();
+                __builtin_amdgcn_sched_barrier(0);
+                // compute phase 2s+1
+                pp_compute(acc, fa, fb);
+                __builtin_amdgcn_sched_barrier(0);
+                wait_vmcnt<0>();
+                barrier_lds();
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            // Between tiles: the next tile's first loads and parameters (every
+            // stage buffer is free: group 1 is in its last compute phase), then
+            // this tile's outputs.
+            const int tn = t + G;
+            const PpTile T0 = T;
+            if (tn < p.num_tiles) {
+                T = pp_tile(p, tn, GROUP_M);
+                float *sa, *sb;
+                uint16_t* bias;
+                epi_area(parity ^ 1, sa, sb, bias);
+                pp_tile_start(smem, p, T, L, q, lane, slice(0), slice(1), need_epi, has_bias, sa, sb,
+                              bias);
+            }
+            pp_store(acc, p, T0.row0, T0.col0, 0, q * 64, epi_sa, epi_sb, epi_bias, s_pt, has_bias,
+                     lane, smem + STG0 + q * STG_BYTES);
+            wait_vmcnt<0>();
+            barrier_lds();   // pairs with group 1's last barrier of the tile
+            __builtin_amdgcn_sched_barrier(0);
+        } else {
+            __builtin_amdgcn_s_barrier();   // one phase behind group 0
+            __builtin_amdgcn_sched_barrier(0);
+            for (int s = 0; s < k_iters; ++s) {
+                // memory phase 2s+1: fragments of slice s, A-bottom of s+1, A-top of s+2
+                pp_read(fa, fb, smem + (s & 1) * STAGE_BYTES, 1, q, lane);
+                if (s + 1 < k_iters)
+                    pp_load_a_half<true>(smem, (s + 1) & 1, q, slice(s + 1), T.ra, L, p.K);
+                if (s + 2 < k_iters)
+                    pp_load_a_half<false>(smem, s & 1, q, slice(s + 2), T.ra, L, p.K);
+                barrier_lds();
+                __builtin_amdgcn_sched_barrier(0);
+                // compute phase 2s+2
+                pp_compute(acc, fa, fb);
+                __builtin_amdgcn_sched_barrier(0);
+                wait_vmcnt<0>();
+                barrier_lds();
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            pp_store(acc, p, T.row0, T.col0, 128, q * 64, epi_sa, epi_sb, epi_bias, s_pt, has_bias,
+                     lane, smem + STG1 + q * STG_BYTES);
+            if (t + G < p.num_tiles) T = pp_tile(p, t + G, GROUP_M);
+        }
+    }
+}
+
+template <int GROUP_M>
+void launch_pp(const Params& p, dim3 grid, hipStream_t stream) {
+    hipLaunchKernelGGL((fp8_gemm_pp_kernel<GROUP_M>), grid, dim3(pp::THREADS), 0, stream, p);
 }
 
 // ------------------------------------------------------------------ host ---
@@ -663,6 +1104,7 @@ void launch_cfg(const Params& p, dim3 grid, hipStream_t stream) {
     hipLaunchKernelGGL((fp8_gemm_kernel<BM, BN, BK, WAVES_M, WAVES_N, STAGES, MI, GROUP_M>), grid,
                        dim3(C::THREADS), 0, stream, p);
 }
+
 
 #define FP8MM_CFG(name, BM, BN, BK, WMW, WNW, ST, MI, GM)                                      \
     ConfigInfo {                                                                               \
@@ -687,8 +1129,11 @@ const ConfigInfo kConfigs[] = {
     FP8MM_CFG("bm128_bn112_bk128_w4x1_s5_mfma16", 128, 112, 128, 4, 1, 5, 16, 8),
     FP8MM_CFG("bm128_bn64_bk128_w4x1_s6_mfma16", 128, 64, 128, 4, 1, 6, 16, 8),
     FP8MM_CFG("bm64_bn64_bk128_w4x1_s8_mfma16", 64, 64, 128, 4, 1, 8, 16, 8),
+    ConfigInfo{"pp_bm256_bn256_bk128_w8_mfma32", pp::BM, pp::BN, pp::BK, false, pp::THREADS,
+               pp::LDS_BYTES, 1, &launch_pp<8>},
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
+constexpr int kPingPongConfig = 14;   // "pp_bm256_bn256_bk128_w8_mfma32"
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -703,9 +1148,10 @@ int choose_config(int64_t M, int64_t N, int64_t K, int mode, int has_bias) {
     if (M <= 16) return 3;
     if (M <= 64) return 13;
     if (M <= 128) return 1;
-    // 256 x 256 tiles (8 waves) once they fill most of the 256 CUs; else 128 x 128.
+    // 256 x 256 tiles on the ping-pong kernel once they fill most of the 256
+    // CUs; else 128 x 128.
     const int64_t big_tiles = cdiv(M, 256) * cdiv(N, 256);
-    if (big_tiles >= 192) return 5;
+    if (big_tiles >= 192) return kPingPongConfig;
     return 1;
 }
 
@@ -893,6 +1339,7 @@ int fp8_scaled_mm_with_plan(const void* A, const void* B, const float* scale_a,
     p.k_iters = (int)k_iters;
     p.rowwise = mode == FP8MM_ROWWISE;
     p.vec_store = (N % 4 == 0) && aligned(out, 8);
+    p.vec16 = (N % 8 == 0) && aligned(out, 16);
     p.splits = sp;
     p.k_chunk = (int)cdiv(k_iters, sp);
     p.counters = nullptr;

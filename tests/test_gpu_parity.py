@@ -89,7 +89,11 @@ def _configs():
     return list(range(len(binding.config_names())))
 
 
-@pytest.mark.parametrize("config", _configs())
+def _config_ids():
+    return [f"{i}_{n}" for i, n in enumerate(binding.config_names())]
+
+
+@pytest.mark.parametrize("config", _configs(), ids=_config_ids())
 @pytest.mark.parametrize("mode", [PT, RW])
 @pytest.mark.parametrize("bias", [False, True])
 @pytest.mark.parametrize("shape", [(300, 200, 160), (257, 515, 400), (64, 128, 1024), (16, 300, 2080)])
@@ -170,6 +174,49 @@ def test_identity_is_exact():
     want = np.where(want == 0x8000, np.uint16(0), want)
     got = np.where(got == 0x8000, np.uint16(0), got)
     assert np.array_equal(got, want)
+
+
+def _rounding_inputs(M, N, K, mode, key):
+    """One-hot rows of A (code 0x38 = 1.0 at column m % K) make every fp32
+    accumulator one e4m3 value of B exactly; scale_b = 1 makes s = scale_a
+    exactly; an e4m3 value (at most 4 significant bits) times a scale of at most
+    20 significant bits is exact in fp32.  The conversion to bf16 is then the
+    only rounding, so the output must match the oracle bit for bit.  The row
+    scales include exact bf16 ties (1 + k*2^-7 + 2^-8, which round to even),
+    20-bit values, and values near 2^-128 whose products land in the bf16
+    denormal range."""
+    rng = np.random.Generator(np.random.PCG64(key))
+    a = np.zeros((M, K), np.uint8)
+    a[np.arange(M), np.arange(M) % K] = 0x38
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    b = codes[rng.integers(0, len(codes), (N, K))]
+    n = M if mode == RW else 1
+    kind = rng.integers(0, 3, n)
+    tie = (1.0 + rng.integers(0, 128, n) * 2.0 ** -7 + 2.0 ** -8) * 2.0 ** rng.integers(-20, 21, n)
+    wide = (1.0 + rng.integers(0, 2 ** 19, n) * 2.0 ** -19) * 2.0 ** rng.integers(-20, 21, n)
+    tiny = (1.0 + rng.integers(0, 16, n) / 16.0) * 2.0 ** -128
+    sa = np.where(kind == 0, tie, np.where(kind == 1, wide, tiny))
+    sa = (sa * np.where(rng.integers(0, 2, n) == 1, -1.0, 1.0)).astype(np.float32)
+    assert np.array_equal(sa.astype(np.float64), np.where(kind == 0, tie, np.where(kind == 1, wide, tiny))
+                          * np.sign(sa.astype(np.float64)))
+    sb = np.ones(N if mode == RW else 1, np.float32)
+    return wl.Inputs(a, b, sa, sb, None, mode)
+
+
+@pytest.mark.parametrize("config", _configs(), ids=_config_ids())
+@pytest.mark.parametrize("mode", [PT, RW])
+@pytest.mark.parametrize("shape", [(512, 256, 64), (300, 200, 64)])
+def test_epilogue_rounding_bitexact(config, mode, shape):
+    inp = _rounding_inputs(*shape, mode, key=config * 7 + mode + shape[0])
+    got = out_bits(run_gpu(inp, config))
+    want = oracle.scaled_mm(inp.a, inp.b, inp.scale_a, inp.scale_b, None, mode)["bits"]
+    # +0 and -0 are the same value (the fp32 accumulator of a zero product sum
+    # is +0 on the GPU, and the sign of s then decides the sign of zero)
+    got = np.where(got == 0x8000, np.uint16(0), got)
+    want = np.where(want == 0x8000, np.uint16(0), want)
+    bad = np.argwhere(got != want)
+    assert bad.size == 0, (f"{len(bad)} mismatches, first at {tuple(bad[0])}: "
+                           f"got {got[tuple(bad[0])]:#06x} want {want[tuple(bad[0])]:#06x}")
 
 
 def test_every_element_written():
