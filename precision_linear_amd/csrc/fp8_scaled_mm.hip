@@ -1131,9 +1131,17 @@ const ConfigInfo kConfigs[] = {
     FP8MM_CFG("bm64_bn64_bk128_w4x1_s8_mfma16", 64, 64, 128, 4, 1, 8, 16, 8),
     ConfigInfo{"pp_bm256_bn256_bk128_w8_mfma32", pp::BM, pp::BN, pp::BK, false, pp::THREADS,
                pp::LDS_BYTES, 1, &launch_pp<8>},
+    FP8MM_CFG("bm64_bn112_bk256_w1x7_s3_mfma16", 64, 112, 256, 1, 7, 3, 16, 8),
+    FP8MM_CFG("bm128_bn112_bk128_w1x7_s5_mfma16", 128, 112, 128, 1, 7, 5, 16, 8),
+    FP8MM_CFG("bm128_bn128_bk128_w2x2_s4_mfma32", 128, 128, 128, 2, 2, 4, 32, 8),
+    FP8MM_CFG("bm64_bn64_bk256_w1x4_s4_mfma16", 64, 64, 256, 1, 4, 4, 16, 8),
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 constexpr int kPingPongConfig = 14;   // "pp_bm256_bn256_bk128_w8_mfma32"
+constexpr int kSkinny16x112 = 8;      // "bm16_bn112_bk256_w1x7_s4_mfma16"
+constexpr int kSkinny64x112 = 15;     // "bm64_bn112_bk256_w1x7_s3_mfma16"
+constexpr int kSkinny64x64 = 18;      // "bm64_bn64_bk256_w1x4_s4_mfma16"
+constexpr int kSkinny128x128 = 17;    // "bm128_bn128_bk128_w2x2_s4_mfma32"
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -1141,13 +1149,15 @@ int choose_splits(int cfg, int64_t M, int64_t N, int64_t K);
 
 int choose_config(int64_t M, int64_t N, int64_t K, int mode, int has_bias) {
     (void)K; (void)mode; (void)has_bias;
-    // Skinny problems (M <= 128) are HBM-bound on B: tiles as tall as M with
-    // deep B prefetch; when such tiles leave CUs idle the K reduction is split
-    // (choose_splits).  Chosen from measurements on MI355X of the six skinny
-    // inference shapes.
-    if (M <= 16) return 3;
-    if (M <= 64) return 13;
-    if (M <= 128) return 1;
+    // Skinny problems (M <= 128) are HBM-bound on B: tiles as tall as M and
+    // 112 columns wide when that gives about one tile per CU (N = 28672 is
+    // 256 x 112), else narrower tiles whose K reduction is split until the
+    // work units fill the CUs (choose_splits).  Chosen from measurements on
+    // MI355X of the six skinny inference shapes.
+    const bool wide = cdiv(N, 112) >= 224;
+    if (M <= 16) return wide ? kSkinny16x112 : 3;
+    if (M <= 64) return wide ? kSkinny64x112 : kSkinny64x64;
+    if (M <= 128) return kSkinny128x128;
     // 256 x 256 tiles on the ping-pong kernel once they fill most of the 256
     // CUs; else 128 x 128.
     const int64_t big_tiles = cdiv(M, 256) * cdiv(N, 256);
