@@ -149,7 +149,13 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-secondary", action="store_true", help="skip the skinny shapes")
     ap.add_argument("--profile-gemm", type=int, default=0, metavar="N",
-                    help="only launch the M=N=K=8192 per-tensor multiply N times (counter runs)")
+                    help="only launch one workload's multiply N times (counter runs)")
+    ap.add_argument("--profile-workload", default="sq8192_pt", metavar="NAME",
+                    help="the workload --profile-gemm launches (default: the M=N=K=8192 "
+                         "per-tensor multiply)")
+    ap.add_argument("--profile-flush", action="store_true",
+                    help="with --profile-gemm: read a 1 GiB buffer before every launch so "
+                         "the operands come from HBM")
     ap.add_argument("--profile-copy-mib", type=int, default=0, metavar="MIB",
                     help="only run one device-to-device copy of MIB MiB (counter calibration)")
     args = ap.parse_args()
@@ -174,11 +180,16 @@ def main():
         print(json.dumps({"copy_bytes": src.numel()}))
         return
     if args.profile_gemm:
-        p = Problem("sq8192_pt", dev)
+        p = Problem(args.profile_workload, dev)
+        flush = (torch.ones(1 << 30, dtype=torch.uint8, device=dev)
+                 if args.profile_flush else None)
         for _ in range(args.profile_gemm):
+            if flush is not None:
+                evict_caches(flush)
             p.launch()
         torch.cuda.synchronize()
-        print(json.dumps({"launches": args.profile_gemm, "workload": p.name}))
+        print(json.dumps({"launches": args.profile_gemm, "workload": p.name,
+                          "flush": flush is not None}))
         return
     probs = [Problem("sq8192_pt", dev), Problem("sq8192_rw", dev)]
     flops_step = sum(p.w.flops for p in probs)
