@@ -75,14 +75,23 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 // bytes from rsrc + voff + soff land at LDS byte address lds + 16*l (lds is
 // wave-uniform and goes to M0).  Written as inline asm so that the compiler
 // does not treat later LDS reads as dependent on it: every wait on these loads
-// is an explicit vmcnt wait placed by the code that issues them.
+// is an explicit vmcnt wait placed by the code that issues them.  NT marks the
+// load non-temporal (data read once: it should not displace reused lines from
+// the L2).
+template <bool NT = false>
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, const void* lds, uint32_t voff,
                                       uint32_t soff) {
     const uint32_t m0 = (uint32_t)(uintptr_t)lds;
-    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
-                 :
-                 : "v"(voff), "s"(rsrc), "s"(soff), "{m0}"(m0)
-                 : "memory");
+    if constexpr (NT)
+        asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen nt lds"
+                     :
+                     : "v"(voff), "s"(rsrc), "s"(soff), "{m0}"(m0)
+                     : "memory");
+    else
+        asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+                     :
+                     : "v"(voff), "s"(rsrc), "s"(soff), "{m0}"(m0)
+                     : "memory");
 }
 
 // Position of 16-byte chunk c of LDS row r is c ^ chunk_swizzle(r).  The MFMA
@@ -133,8 +142,13 @@ __device__ __forceinline__ void tile_coords(int t, int tiles_m, int tiles_n, int
     pn = w / rows;
 }
 
-template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int STAGES, int MI, int GROUP_M>
+template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int STAGES, int MI, int GROUP_M,
+          bool NT_B = false>
 struct Cfg {
+    // B is read by one tile row only (the grid has a single row of tiles):
+    // its loads are marked non-temporal so that they do not evict A, which
+    // every tile reads.
+    static constexpr bool STREAM_B = NT_B;
     static constexpr int WAVES = WAVES_M * WAVES_N;
     static constexpr int THREADS = WAVES * kWave;
     static constexpr int WTM = BM / WAVES_M;     // wave tile rows (m)
@@ -211,7 +225,7 @@ __device__ __forceinline__ void load_stage(uint8_t* lds_stage, __amdgpu_buffer_r
         const int c = pos ^ chunk_swizzle<C::CPR>(r);
         const int k = k0 + c * 16;
         const uint32_t off = k < klim ? (uint32_t)(r * ld + k) : kOutOfRange;
-        dma16(rb, lds_stage + C::A_BYTES + blk * 1024, off, 0);
+        dma16<C::STREAM_B>(rb, lds_stage + C::A_BYTES + blk * 1024, off, 0);
     }
 }
 
@@ -233,7 +247,10 @@ __device__ __forceinline__ void load_one(uint8_t* lds_stage, __amdgpu_buffer_rsr
     const int c = pos ^ chunk_swizzle<C::CPR>(r);
     const int k = k0 + c * 16;
     const uint32_t off = (live && k < klim) ? (uint32_t)(r * ld + k) : kOutOfRange;
-    dma16(IS_A ? ra : rb, lds_stage + (IS_A ? 0 : C::A_BYTES) + blk * 1024, off, 0);
+    if constexpr (IS_A)
+        dma16(ra, lds_stage + blk * 1024, off, 0);
+    else
+        dma16<C::STREAM_B>(rb, lds_stage + C::A_BYTES + blk * 1024, off, 0);
 }
 
 template <class C, int LO, int HI>
@@ -495,10 +512,11 @@ __device__ __forceinline__ void run_stage(typename Mfma<C::MI_>::acc_t (&acc)[C:
     }
 }
 
-template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int STAGES, int MI, int GROUP_M>
+template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int STAGES, int MI, int GROUP_M,
+          bool NT_B>
 __global__ void __launch_bounds__(WAVES_M * WAVES_N * kWave)
 fp8_gemm_kernel(Params p) {
-    using C = Cfg<BM, BN, BK, WAVES_M, WAVES_N, STAGES, MI, GROUP_M>;
+    using C = Cfg<BM, BN, BK, WAVES_M, WAVES_N, STAGES, MI, GROUP_M, NT_B>;
     using F = Mfma<MI>;
     __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS_BYTES];
 
@@ -1096,52 +1114,51 @@ struct ConfigInfo {
     int lds_bytes;
     int occupancy;   // workgroups per CU the persistent grid assumes
     void (*launch)(const Params&, dim3, hipStream_t);
+    // The same tiles with B loaded non-temporally, for grids with a single row
+    // of tiles (B is then read once); null where not compiled.
+    void (*launch_stream)(const Params&, dim3, hipStream_t);
 };
 
-template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int STAGES, int MI, int GROUP_M>
+template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int STAGES, int MI, int GROUP_M,
+          bool NT_B>
 void launch_cfg(const Params& p, dim3 grid, hipStream_t stream) {
-    using C = Cfg<BM, BN, BK, WAVES_M, WAVES_N, STAGES, MI, GROUP_M>;
-    hipLaunchKernelGGL((fp8_gemm_kernel<BM, BN, BK, WAVES_M, WAVES_N, STAGES, MI, GROUP_M>), grid,
-                       dim3(C::THREADS), 0, stream, p);
+    using C = Cfg<BM, BN, BK, WAVES_M, WAVES_N, STAGES, MI, GROUP_M, NT_B>;
+    hipLaunchKernelGGL((fp8_gemm_kernel<BM, BN, BK, WAVES_M, WAVES_N, STAGES, MI, GROUP_M, NT_B>),
+                       grid, dim3(C::THREADS), 0, stream, p);
 }
 
-
-#define FP8MM_CFG(name, BM, BN, BK, WMW, WNW, ST, MI, GM)                                      \
-    ConfigInfo {                                                                               \
-        name, BM, BN, BK, Cfg<BM, BN, BK, WMW, WNW, ST, MI, GM>::SPLIT_OK,                         \
-            Cfg<BM, BN, BK, WMW, WNW, ST, MI, GM>::THREADS,                                    \
-            Cfg<BM, BN, BK, WMW, WNW, ST, MI, GM>::LDS_BYTES, 1,                               \
-            &launch_cfg<BM, BN, BK, WMW, WNW, ST, MI, GM>                                      \
+#define FP8MM_CFG(name, BM, BN, BK, WMW, WNW, ST, MI, GM, STREAM)                                 \
+    ConfigInfo {                                                                                  \
+        name, BM, BN, BK, Cfg<BM, BN, BK, WMW, WNW, ST, MI, GM>::SPLIT_OK,                        \
+            Cfg<BM, BN, BK, WMW, WNW, ST, MI, GM>::THREADS,                                       \
+            Cfg<BM, BN, BK, WMW, WNW, ST, MI, GM>::LDS_BYTES, 1,                                  \
+            &launch_cfg<BM, BN, BK, WMW, WNW, ST, MI, GM, false>,                                 \
+            STREAM ? &launch_cfg<BM, BN, BK, WMW, WNW, ST, MI, GM, true> : nullptr                \
     }
 
+// Ids are the positions in this table (the C ABI's config_id).
 const ConfigInfo kConfigs[] = {
-    FP8MM_CFG("bm256_bn256_bk128_w2x2_s2_mfma32", 256, 256, 128, 2, 2, 2, 32, 8),
-    FP8MM_CFG("bm128_bn128_bk128_w2x2_s3_mfma32", 128, 128, 128, 2, 2, 3, 32, 8),
-    FP8MM_CFG("bm32_bn64_bk256_w1x2_s4_mfma32", 32, 64, 256, 1, 2, 4, 32, 8),
-    FP8MM_CFG("bm16_bn64_bk256_w1x4_s4_mfma16", 16, 64, 256, 1, 4, 4, 16, 8),
-    FP8MM_CFG("bm256_bn256_bk64_w2x4_s4_mfma32", 256, 256, 64, 2, 4, 4, 32, 8),
-    FP8MM_CFG("bm256_bn256_bk128_w2x4_s2_mfma32", 256, 256, 128, 2, 4, 2, 32, 8),
-    FP8MM_CFG("bm256_bn256_bk64_w2x2_s4_mfma32", 256, 256, 64, 2, 2, 4, 32, 8),
-    FP8MM_CFG("bm256_bn256_bk64_w4x2_s4_mfma32", 256, 256, 64, 4, 2, 4, 32, 8),
-    FP8MM_CFG("bm16_bn112_bk256_w1x7_s4_mfma16", 16, 112, 256, 1, 7, 4, 16, 8),
-    FP8MM_CFG("bm16_bn32_bk512_w1x2_s6_mfma16", 16, 32, 512, 1, 2, 6, 16, 8),
-    FP8MM_CFG("bm64_bn112_bk128_w4x1_s7_mfma16", 64, 112, 128, 4, 1, 7, 16, 8),
-    FP8MM_CFG("bm128_bn112_bk128_w4x1_s5_mfma16", 128, 112, 128, 4, 1, 5, 16, 8),
-    FP8MM_CFG("bm128_bn64_bk128_w4x1_s6_mfma16", 128, 64, 128, 4, 1, 6, 16, 8),
-    FP8MM_CFG("bm64_bn64_bk128_w4x1_s8_mfma16", 64, 64, 128, 4, 1, 8, 16, 8),
+    FP8MM_CFG("bm128_bn128_bk128_w2x2_s3_mfma32", 128, 128, 128, 2, 2, 3, 32, 8, true),
+    FP8MM_CFG("bm16_bn64_bk256_w1x4_s4_mfma16", 16, 64, 256, 1, 4, 4, 16, 8, true),
+    FP8MM_CFG("bm16_bn112_bk256_w1x7_s4_mfma16", 16, 112, 256, 1, 7, 4, 16, 8, true),
+    FP8MM_CFG("bm16_bn32_bk512_w1x2_s6_mfma16", 16, 32, 512, 1, 2, 6, 16, 8, true),
+    FP8MM_CFG("bm64_bn64_bk128_w4x1_s8_mfma16", 64, 64, 128, 4, 1, 8, 16, 8, true),
+    FP8MM_CFG("bm64_bn112_bk256_w1x7_s3_mfma16", 64, 112, 256, 1, 7, 3, 16, 8, true),
+    FP8MM_CFG("bm64_bn64_bk256_w1x4_s4_mfma16", 64, 64, 256, 1, 4, 4, 16, 8, true),
+    FP8MM_CFG("bm128_bn128_bk128_w2x2_s4_mfma32", 128, 128, 128, 2, 2, 4, 32, 8, true),
+    FP8MM_CFG("bm128_bn128_bk128_w2x4_s4_mfma32", 128, 128, 128, 2, 4, 4, 32, 8, true),
+    FP8MM_CFG("bm256_bn256_bk128_w2x4_s2_mfma32", 256, 256, 128, 2, 4, 2, 32, 8, false),
     ConfigInfo{"pp_bm256_bn256_bk128_w8_mfma32", pp::BM, pp::BN, pp::BK, false, pp::THREADS,
-               pp::LDS_BYTES, 1, &launch_pp<8>},
-    FP8MM_CFG("bm64_bn112_bk256_w1x7_s3_mfma16", 64, 112, 256, 1, 7, 3, 16, 8),
-    FP8MM_CFG("bm128_bn112_bk128_w1x7_s5_mfma16", 128, 112, 128, 1, 7, 5, 16, 8),
-    FP8MM_CFG("bm128_bn128_bk128_w2x2_s4_mfma32", 128, 128, 128, 2, 2, 4, 32, 8),
-    FP8MM_CFG("bm64_bn64_bk256_w1x4_s4_mfma16", 64, 64, 256, 1, 4, 4, 16, 8),
+               pp::LDS_BYTES, 1, &launch_pp<8>, nullptr},
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
-constexpr int kPingPongConfig = 14;   // "pp_bm256_bn256_bk128_w8_mfma32"
-constexpr int kSkinny16x112 = 8;      // "bm16_bn112_bk256_w1x7_s4_mfma16"
-constexpr int kSkinny64x112 = 15;     // "bm64_bn112_bk256_w1x7_s3_mfma16"
-constexpr int kSkinny64x64 = 18;      // "bm64_bn64_bk256_w1x4_s4_mfma16"
-constexpr int kSkinny128x128 = 17;    // "bm128_bn128_bk128_w2x2_s4_mfma32"
+constexpr int kMidConfig = 0;         // "bm128_bn128_bk128_w2x2_s3_mfma32"
+constexpr int kSkinny16x64 = 1;       // "bm16_bn64_bk256_w1x4_s4_mfma16"
+constexpr int kSkinny16x112 = 2;      // "bm16_bn112_bk256_w1x7_s4_mfma16"
+constexpr int kSkinny64x112 = 5;      // "bm64_bn112_bk256_w1x7_s3_mfma16"
+constexpr int kSkinny64x64 = 6;       // "bm64_bn64_bk256_w1x4_s4_mfma16"
+constexpr int kSkinny128x128 = 8;     // "bm128_bn128_bk128_w2x4_s4_mfma32"
+constexpr int kPingPongConfig = 10;   // "pp_bm256_bn256_bk128_w8_mfma32"
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -1155,14 +1172,14 @@ int choose_config(int64_t M, int64_t N, int64_t K, int mode, int has_bias) {
     // work units fill the CUs (choose_splits).  Chosen from measurements on
     // MI355X of the six skinny inference shapes.
     const bool wide = cdiv(N, 112) >= 224;
-    if (M <= 16) return wide ? kSkinny16x112 : 3;
+    if (M <= 16) return wide ? kSkinny16x112 : kSkinny16x64;
     if (M <= 64) return wide ? kSkinny64x112 : kSkinny64x64;
     if (M <= 128) return kSkinny128x128;
     // 256 x 256 tiles on the ping-pong kernel once they fill most of the 256
     // CUs; else 128 x 128.
     const int64_t big_tiles = cdiv(M, 256) * cdiv(N, 256);
     if (big_tiles >= 192) return kPingPongConfig;
-    return 1;
+    return kMidConfig;
 }
 
 int device_cus(int dev) {
@@ -1361,7 +1378,8 @@ int fp8_scaled_mm_with_plan(const void* A, const void* B, const float* scale_a,
 
     const dim3 grid((unsigned)grid_for(cfg, M, N, sp, cus));
     (void)hipGetLastError();  // clear a stale error from earlier, unrelated calls
-    c.launch(p, grid, hs);
+    if (p.tiles_m == 1 && c.launch_stream) c.launch_stream(p, grid, hs);
+    else c.launch(p, grid, hs);
     if (hipGetLastError() != hipSuccess) return FP8MM_ERR_LAUNCH;
     return FP8MM_OK;
 }

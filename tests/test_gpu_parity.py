@@ -292,13 +292,15 @@ def _cfg(name):
 
 
 @pytest.mark.parametrize("config", ["bm128_bn128_bk128_w2x2_s3_mfma32", "bm16_bn64_bk256_w1x4_s4_mfma16",
-                                    "bm64_bn64_bk128_w4x1_s8_mfma16", "bm64_bn112_bk128_w4x1_s7_mfma16",
-                                    "bm128_bn64_bk128_w4x1_s6_mfma16"])
+                                    "bm64_bn64_bk128_w4x1_s8_mfma16", "bm64_bn112_bk256_w1x7_s3_mfma16",
+                                    "bm64_bn64_bk256_w1x4_s4_mfma16", "bm128_bn128_bk128_w2x4_s4_mfma32"])
 @pytest.mark.parametrize("splits", [2, 3, 4, 7])
 @pytest.mark.parametrize("mode", [PT, RW])
-def test_split_k_parity(config, splits, mode):
-    # K = 1040: 9 slices of 128 (last ragged), so splits do not divide it evenly
-    inp = wl.make_inputs(150, 230, 1040, mode, "codes", bias=mode == RW, key=splits * 7 + mode)
+@pytest.mark.parametrize("M", [150, 16])
+def test_split_k_parity(config, splits, mode, M):
+    # K = 1040: 9 slices of 128 (last ragged), so splits do not divide it evenly.
+    # M = 16 gives a single row of tiles (the non-temporal-B launch).
+    inp = wl.make_inputs(M, 230, 1040, mode, "codes", bias=mode == RW, key=splits * 7 + mode + M)
     got = out_bits(run_gpu_plan(inp, _cfg(config), splits))
     ref = oracle.scaled_mm(inp.a, inp.b, inp.scale_a, inp.scale_b, inp.bias, inp.mode)
     nbad, worst, first = compare(got, ref)
