@@ -8,3 +8,6 @@ from .fp8_scaled_mm_ref import (  # noqa: F401
     PER_TENSOR, ROWWISE, e4m3fn_value, e4m3fn_decode_table, decode,
     bf16_bits_to_f64, f64_to_bf16_rne, scaled_mm,
 )
+from .quantize_ref import (  # noqa: F401,E402
+    E4M3_MAX, e4m3fn_encode_rne, quantize_e4m3, dequantize,
+)
