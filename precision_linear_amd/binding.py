@@ -27,7 +27,12 @@ _ARG_ERRORS = {ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_MODE, ERR_CONFIG, ERR_WORKSPA
 EXPORTS = ("fp8_scaled_mm", "fp8_scaled_mm_with_config", "fp8_scaled_mm_with_plan",
            "fp8_scaled_mm_workspace_size", "fp8_scaled_mm_select_splits",
            "fp8_scaled_mm_num_configs", "fp8_scaled_mm_config_name", "fp8_scaled_mm_select_config",
-           "fp8_scaled_mm_grid_size", "fp8_scaled_mm_status_string")
+           "fp8_scaled_mm_grid_size", "fp8_scaled_mm_status_string",
+           "fp8_quantize_e4m3", "fp8_quantize_status_string")
+
+# status codes from include/fp8_quantize.h
+Q_OK, Q_ERR_NULL, Q_ERR_SHAPE, Q_ERR_ALIGN, Q_ERR_MODE, Q_ERR_DEVICE, Q_ERR_LAUNCH = range(7)
+_Q_ARG_ERRORS = {Q_ERR_NULL, Q_ERR_SHAPE, Q_ERR_ALIGN, Q_ERR_MODE}
 
 
 class Fp8MMError(RuntimeError):
@@ -69,6 +74,10 @@ def lib() -> ctypes.CDLL:
         L.fp8_scaled_mm_grid_size.restype = i64
         L.fp8_scaled_mm_status_string.argtypes = [i32]
         L.fp8_scaled_mm_status_string.restype = ctypes.c_char_p
+        L.fp8_quantize_e4m3.argtypes = [vp, vp, vp, i64, i64, i32, vp]
+        L.fp8_quantize_e4m3.restype = i32
+        L.fp8_quantize_status_string.argtypes = [i32]
+        L.fp8_quantize_status_string.restype = ctypes.c_char_p
         _lib = L
     return _lib
 
@@ -163,3 +172,37 @@ def fp8_scaled_mm(a: torch.Tensor, b: torch.Tensor, scale_a: torch.Tensor, scale
             raise ValueError(f"fp8_scaled_mm: {status_string(st)} (status {st})")
         raise Fp8MMError(st)
     return out
+
+
+def fp8_quantize(x: torch.Tensor, mode="rowwise", q: torch.Tensor | None = None,
+                 scale: torch.Tensor | None = None):
+    """(q, scale) = dynamic e4m3fn quantisation of a rows x cols bf16 GPU matrix:
+    scale = amax/448 (one value, or one per row), q = e4m3fn(clamp(x/scale, +-448))
+    as uint8 codes.  `q` and `scale` may be passed to reuse buffers."""
+    if mode not in _MODES:
+        raise ValueError(f"mode must be 'per_tensor' or 'rowwise', got {mode!r}")
+    m = _MODES[mode]
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or not x.is_contiguous() or not x.is_cuda:
+        raise ValueError("x must be a contiguous 2-D bf16 GPU tensor")
+    rows, cols = x.shape
+    n_scale = 1 if m == PER_TENSOR else rows
+    if q is None:
+        q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+    elif q.dtype not in (torch.uint8, torch.float8_e4m3fn) or tuple(q.shape) != (rows, cols) \
+            or not q.is_contiguous():
+        raise ValueError("q must be a contiguous uint8 (or float8_e4m3fn) rows x cols tensor")
+    if scale is None:
+        scale = torch.empty(n_scale, dtype=torch.float32, device=x.device)
+    elif scale.dtype != torch.float32 or scale.numel() != n_scale or not scale.is_contiguous():
+        raise ValueError(f"scale must be a contiguous float32 tensor of {n_scale} elements")
+    stream = torch.cuda.current_stream(x.device).cuda_stream
+    with torch.cuda.device(x.device):
+        st = lib().fp8_quantize_e4m3(x.data_ptr() if x.numel() else None,
+                                     q.data_ptr() if q.numel() else None, scale.data_ptr(),
+                                     rows, cols, m, stream)
+    if st != Q_OK:
+        msg = f"fp8_quantize_e4m3: {lib().fp8_quantize_status_string(st).decode()} (status {st})"
+        if st in _Q_ARG_ERRORS:
+            raise ValueError(msg)
+        raise RuntimeError(msg)
+    return q, scale

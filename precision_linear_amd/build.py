@@ -1,4 +1,5 @@
-"""Builds libfp8_scaled_mm.so (the HIP kernels and their C ABI) for gfx950.
+"""Builds libfp8_scaled_mm.so (the HIP kernels -- scaled multiply and
+quantiser -- and their C ABI) for gfx950.
 
 hipcc cross-compiles without a GPU.  The library is written next to this
 file so that it travels with the source tree.
@@ -10,7 +11,8 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SRC = os.path.join(HERE, "csrc", "fp8_scaled_mm.hip")
+SRCS = [os.path.join(HERE, "csrc", "fp8_scaled_mm.hip"),
+        os.path.join(HERE, "csrc", "fp8_quantize.hip")]
 LIB = os.path.join(HERE, "libfp8_scaled_mm.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -24,11 +26,11 @@ FLAGS = [
 
 def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, SRC, "-o", tmp]
+    cmd = [HIPCC, *FLAGS, *SRCS, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError(f"hipcc failed ({res.returncode}) building {SRC}")
+        raise RuntimeError(f"hipcc failed ({res.returncode}) building {' '.join(SRCS)}")
     if verbose:
         sys.stderr.write(res.stderr)
     shutil.move(tmp, LIB)

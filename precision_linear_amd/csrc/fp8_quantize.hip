@@ -1,0 +1,273 @@
+// Dynamic FP8 (e4m3fn) quantisation of a bf16 matrix for gfx950 (MI355X).
+//
+//   scale = amax / 448            (fp32; amax over the matrix or over each row)
+//   q     = e4m3fn_RNE( clamp( x / scale, -448, 448 ) )     (x / scale in fp32)
+//
+// The quantisation of the gist "matmul_fp8.py" (a-r-r-o-w), functions
+// `get_scale` and `benchmark` (scale = amax / finfo(e4m3fn).max, divide,
+// clamp, cast): the producer of A and scale_a for the scaled multiply, which
+// pytorch PR #130422, Testing, notes can be fused with the preceding op.
+// A row (or matrix) whose amax is 0 gets scale 0 and codes 0 (the division
+// would be 0/0).
+//
+// HBM-bound: every element is read once (twice for the per-tensor mode, whose
+// second pass usually hits the 256 MB MALL) and written once.
+//   * Row-wise: one workgroup per row at a time (grid-stride over rows).  A row
+//     of up to 8 x 4096 elements stays in registers between the amax and the
+//     quantisation (16 bf16 = 32 bytes per thread and chunk, loaded as two
+//     16-byte vectors); longer rows are read a second time (from L2).
+//   * Per-tensor: a zeroing launch, a grid-stride amax pass (atomic max of the
+//     fp32 bit pattern, monotone for non-negative floats), a quantisation pass
+//     and a launch that turns the stored amax into the scale.
+//   * The division is the correctly rounded fp32 one; the conversion is
+//     v_cvt_pk_fp8_f32 (round to nearest even; inputs are already clamped).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/fp8_quantize.h"
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kGroup = 16;                      // elements per thread per chunk
+constexpr int kChunkElems = kThreads * kGroup;  // 4096
+constexpr float kE4m3Max = 448.f;
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// 16 bf16 values (two 16-byte vectors) -> max |x|.
+__device__ __forceinline__ float absmax16(const uint4 (&v)[2]) {
+    float m = 0.f;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const uint32_t w[4] = {v[h].x, v[h].y, v[h].z, v[h].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            m = fmaxf(m, fabsf(bf16_lo(w[i])));
+            m = fmaxf(m, fabsf(bf16_hi(w[i])));
+        }
+    }
+    return m;
+}
+
+__device__ __forceinline__ float quant1(float x, float s) {
+    if (s == 0.f) return 0.f;
+    const float y = x / s;   // correctly rounded fp32 division
+    return fminf(fmaxf(y, -kE4m3Max), kE4m3Max);
+}
+
+// 16 bf16 values -> 16 e4m3fn codes (one 16-byte vector).
+__device__ __forceinline__ uint4 quant16(const uint4 (&v)[2], float s) {
+    uint32_t out[4];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const uint32_t w[4] = {v[h].x, v[h].y, v[h].z, v[h].w};
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            int packed = __builtin_amdgcn_cvt_pk_fp8_f32(quant1(bf16_lo(w[2 * p]), s),
+                                                         quant1(bf16_hi(w[2 * p]), s), 0, false);
+            packed = __builtin_amdgcn_cvt_pk_fp8_f32(quant1(bf16_lo(w[2 * p + 1]), s),
+                                                     quant1(bf16_hi(w[2 * p + 1]), s), packed,
+                                                     true);
+            out[2 * h + p] = (uint32_t)packed;
+        }
+    }
+    return uint4{out[0], out[1], out[2], out[3]};
+}
+
+__device__ __forceinline__ void load16(const uint16_t* p, uint4 (&v)[2]) {
+    const uint4* q = reinterpret_cast<const uint4*>(p);
+    v[0] = q[0];
+    v[1] = q[1];
+}
+
+// Maximum over the workgroup (all lanes return it).
+__device__ __forceinline__ float block_max(float m, float* red) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+    const int wave = threadIdx.x / 64;
+    __syncthreads();   // red[] may still be read by the previous row's reduction
+    if (threadIdx.x % 64 == 0) red[wave] = m;
+    __syncthreads();
+    m = red[0];
+#pragma unroll
+    for (int w = 1; w < kThreads / 64; ++w) m = fmaxf(m, red[w]);
+    return m;
+}
+
+// Row-wise.  CHUNKS > 0: the row (at most CHUNKS * 4096 elements) is held in
+// registers; CHUNKS == 0: any length, read twice.
+template <int CHUNKS>
+__global__ void __launch_bounds__(kThreads)
+quant_rowwise_kernel(const uint16_t* __restrict__ x, uint8_t* __restrict__ q, float* __restrict__ scale,
+                     int64_t rows, int64_t cols) {
+    __shared__ float red[kThreads / 64];
+    const int64_t groups = cols / kGroup;
+    for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
+        const uint16_t* xr = x + r * cols;
+        uint8_t* qr = q + r * cols;
+        float m = 0.f;
+        if constexpr (CHUNKS > 0) {
+            uint4 v[CHUNKS][2];
+#pragma unroll
+            for (int c = 0; c < CHUNKS; ++c) {
+                const int64_t g = threadIdx.x + (int64_t)c * kThreads;
+                if (g < groups) {
+                    load16(xr + g * kGroup, v[c]);
+                    m = fmaxf(m, absmax16(v[c]));
+                }
+            }
+            const float s = block_max(m, red) / kE4m3Max;
+            if (threadIdx.x == 0) scale[r] = s;
+#pragma unroll
+            for (int c = 0; c < CHUNKS; ++c) {
+                const int64_t g = threadIdx.x + (int64_t)c * kThreads;
+                if (g < groups) *reinterpret_cast<uint4*>(qr + g * kGroup) = quant16(v[c], s);
+            }
+        } else {
+            for (int64_t g = threadIdx.x; g < groups; g += kThreads) {
+                uint4 v[2];
+                load16(xr + g * kGroup, v);
+                m = fmaxf(m, absmax16(v));
+            }
+            const float s = block_max(m, red) / kE4m3Max;
+            if (threadIdx.x == 0) scale[r] = s;
+            for (int64_t g = threadIdx.x; g < groups; g += kThreads) {
+                uint4 v[2];
+                load16(xr + g * kGroup, v);
+                *reinterpret_cast<uint4*>(qr + g * kGroup) = quant16(v, s);
+            }
+        }
+    }
+}
+
+// n floats of 0 (the scales of rows without elements).
+__global__ void __launch_bounds__(kThreads) zero_kernel(float* p, int64_t n) {
+    for (int64_t i = blockIdx.x * (int64_t)kThreads + threadIdx.x; i < n;
+         i += (int64_t)gridDim.x * kThreads)
+        p[i] = 0.f;
+}
+
+// Per-tensor pass 0: the amax slot starts at +0.
+__global__ void amax_zero_kernel(float* slot) {
+    if (threadIdx.x == 0) slot[0] = 0.f;
+}
+
+// Per-tensor pass 1: amax over every element, into slot[0] (as a float whose
+// bit pattern only grows).
+__global__ void __launch_bounds__(kThreads)
+amax_kernel(const uint16_t* __restrict__ x, int64_t groups, float* slot) {
+    __shared__ float red[kThreads / 64];
+    float m = 0.f;
+    for (int64_t g = blockIdx.x * (int64_t)kThreads + threadIdx.x; g < groups;
+         g += (int64_t)gridDim.x * kThreads) {
+        uint4 v[2];
+        load16(x + g * kGroup, v);
+        m = fmaxf(m, absmax16(v));
+    }
+    m = block_max(m, red);
+    if (threadIdx.x == 0) atomicMax(reinterpret_cast<unsigned*>(slot), __float_as_uint(m));
+}
+
+// Per-tensor pass 2: quantise with scale = slot[0] / 448.
+__global__ void __launch_bounds__(kThreads)
+quant_tensor_kernel(const uint16_t* __restrict__ x, uint8_t* __restrict__ q, int64_t groups,
+                    const float* slot) {
+    const float s = slot[0] / kE4m3Max;
+    for (int64_t g = blockIdx.x * (int64_t)kThreads + threadIdx.x; g < groups;
+         g += (int64_t)gridDim.x * kThreads) {
+        uint4 v[2];
+        load16(x + g * kGroup, v);
+        *reinterpret_cast<uint4*>(q + g * kGroup) = quant16(v, s);
+    }
+}
+
+// Per-tensor pass 3: the stored amax becomes the scale.
+__global__ void amax_to_scale_kernel(float* slot) {
+    if (threadIdx.x == 0) slot[0] = slot[0] / kE4m3Max;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+int device_cus_q() {
+    int dev = -1, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return 0;
+    return cus;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fp8_quantize_e4m3(const void* x, void* q, float* scale, int64_t rows, int64_t cols,
+                      int scaling_mode, struct ihipStream_t* stream) {
+    if (scaling_mode != FP8Q_PER_TENSOR && scaling_mode != FP8Q_ROWWISE) return FP8Q_ERR_MODE;
+    if (rows < 0 || cols < 0 || cols % kGroup != 0 || cols > (int64_t(1) << 31) ||
+        rows > (int64_t(1) << 31))
+        return FP8Q_ERR_SHAPE;
+    const bool empty = rows == 0 || cols == 0;
+    const int64_t n_scales = scaling_mode == FP8Q_PER_TENSOR ? 1 : rows;
+    if ((n_scales > 0 && !scale) || (!empty && (!x || !q))) return FP8Q_ERR_NULL;
+    if ((uintptr_t)scale & 3) return FP8Q_ERR_ALIGN;
+    if (!empty && (!aligned16(x) || !aligned16(q))) return FP8Q_ERR_ALIGN;
+    if (n_scales == 0) return FP8Q_OK;   // row-wise without rows: nothing to write
+    const int cus = device_cus_q();
+    if (cus <= 0) return FP8Q_ERR_DEVICE;
+    const hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+    const uint16_t* xb = static_cast<const uint16_t*>(x);
+    uint8_t* qb = static_cast<uint8_t*>(q);
+    (void)hipGetLastError();
+    if (empty) {
+        // No element: amax is 0, so every scale is 0.
+        const int64_t blocks = (n_scales + kThreads - 1) / kThreads;
+        hipLaunchKernelGGL(zero_kernel, dim3((unsigned)(blocks < 4096 ? blocks : 4096)),
+                           dim3(kThreads), 0, hs, scale, n_scales);
+    } else if (scaling_mode == FP8Q_ROWWISE) {
+        const int64_t chunks = (cols + kChunkElems - 1) / kChunkElems;
+        const unsigned grid = (unsigned)(rows < (int64_t)cus * 8 ? rows : (int64_t)cus * 8);
+        if (chunks <= 1)
+            hipLaunchKernelGGL(quant_rowwise_kernel<1>, dim3(grid), dim3(kThreads), 0, hs, xb, qb,
+                               scale, rows, cols);
+        else if (chunks <= 2)
+            hipLaunchKernelGGL(quant_rowwise_kernel<2>, dim3(grid), dim3(kThreads), 0, hs, xb, qb,
+                               scale, rows, cols);
+        else if (chunks <= 4)
+            hipLaunchKernelGGL(quant_rowwise_kernel<4>, dim3(grid), dim3(kThreads), 0, hs, xb, qb,
+                               scale, rows, cols);
+        else if (chunks <= 8)
+            hipLaunchKernelGGL(quant_rowwise_kernel<8>, dim3(grid), dim3(kThreads), 0, hs, xb, qb,
+                               scale, rows, cols);
+        else
+            hipLaunchKernelGGL(quant_rowwise_kernel<0>, dim3(grid), dim3(kThreads), 0, hs, xb, qb,
+                               scale, rows, cols);
+    } else {
+        const int64_t groups = rows * cols / kGroup;
+        const int64_t want = (groups + kThreads - 1) / kThreads;
+        const unsigned grid = (unsigned)(want < (int64_t)cus * 8 ? want : (int64_t)cus * 8);
+        hipLaunchKernelGGL(amax_zero_kernel, dim3(1), dim3(64), 0, hs, scale);
+        hipLaunchKernelGGL(amax_kernel, dim3(grid), dim3(kThreads), 0, hs, xb, groups, scale);
+        hipLaunchKernelGGL(quant_tensor_kernel, dim3(grid), dim3(kThreads), 0, hs, xb, qb, groups,
+                           scale);
+        hipLaunchKernelGGL(amax_to_scale_kernel, dim3(1), dim3(64), 0, hs, scale);
+    }
+    if (hipGetLastError() != hipSuccess) return FP8Q_ERR_LAUNCH;
+    return FP8Q_OK;
+}
+
+const char* fp8_quantize_status_string(int s) {
+    switch (s) {
+        case FP8Q_OK: return "ok";
+        case FP8Q_ERR_NULL: return "a required pointer is NULL";
+        case FP8Q_ERR_SHAPE: return "rows or cols out of range (need cols % 16 == 0, both < 2^31)";
+        case FP8Q_ERR_ALIGN: return "misaligned pointer (x, q: 16 B; scale: 4 B)";
+        case FP8Q_ERR_MODE: return "unknown scaling mode";
+        case FP8Q_ERR_DEVICE: return "no usable HIP device";
+        case FP8Q_ERR_LAUNCH: return "kernel launch failed";
+        default: return "unknown status";
+    }
+}
+
+}  // extern "C"

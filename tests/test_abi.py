@@ -10,7 +10,7 @@ import pytest
 from precision_linear_amd import binding
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "fp8_scaled_mm.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("fp8_scaled_mm.h", "fp8_quantize.h")]
 
 
 @pytest.fixture(scope="module")
@@ -22,14 +22,17 @@ def L():
 
 
 def _declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(fp8_scaled_mm\w*)\s*\(", text)))
+    names = set()
+    for h in HEADERS:
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names |= set(re.findall(r"\b(fp8_\w+)\s*\(", text))
+    return sorted(names)
 
 
 def test_exports_every_declared_function(L):
     names = _declared_functions()
-    assert len(names) >= 7
+    assert len(names) >= 9 and "fp8_quantize_e4m3" in names
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(binding.EXPORTS)
@@ -145,3 +148,34 @@ def test_plan_validation(L):
     assert f(P, P, P, P, None, P, 128, 128, 4096, 0, None, cfg, 4, P, 1024) == binding.ERR_WORKSPACE
     need = L.fp8_scaled_mm_workspace_size(128, 128, 4096, 0, 0, cfg, 4)
     assert f(P, P, P, P, None, P, 128, 128, 4096, 0, None, cfg, 4, P + 128, need) == binding.ERR_ALIGN
+
+
+# ---- quantiser ---------------------------------------------------------------
+
+def qcall(L, x=P, q=P, scale=P, rows=64, cols=64, mode=1):
+    return L.fp8_quantize_e4m3(x, q, scale, rows, cols, mode, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(mode=2), binding.Q_ERR_MODE), (dict(mode=-1), binding.Q_ERR_MODE),
+    (dict(cols=24), binding.Q_ERR_SHAPE), (dict(rows=-1), binding.Q_ERR_SHAPE),
+    (dict(cols=-16), binding.Q_ERR_SHAPE), (dict(cols=(1 << 31) + 16), binding.Q_ERR_SHAPE),
+    (dict(x=None), binding.Q_ERR_NULL), (dict(q=None), binding.Q_ERR_NULL),
+    (dict(scale=None), binding.Q_ERR_NULL), (dict(scale=None, rows=0, mode=0), binding.Q_ERR_NULL),
+    (dict(x=P + 8), binding.Q_ERR_ALIGN), (dict(q=P + 4), binding.Q_ERR_ALIGN),
+    (dict(scale=P + 2), binding.Q_ERR_ALIGN),
+])
+def test_quantize_rejects_bad_arguments(L, kw, code):
+    assert qcall(L, **kw) == code
+
+
+def test_quantize_empty_rowwise_needs_no_device(L):
+    # no rows: nothing at all to do, not even scales
+    assert qcall(L, x=None, q=None, rows=0, cols=64, mode=1) == binding.Q_OK
+    assert qcall(L, x=None, q=None, scale=None, rows=0, cols=64, mode=1) == binding.Q_OK
+
+
+def test_quantize_status_strings(L):
+    for s in range(7):
+        assert L.fp8_quantize_status_string(s)
+    assert L.fp8_quantize_status_string(42) == b"unknown status"
