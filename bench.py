@@ -141,6 +141,45 @@ def skinny_results(dev, reps=20):
     return res
 
 
+QUANT_SHAPES = [(8192, 8192, "rowwise"), (8192, 8192, "per_tensor"), (128, 28672, "rowwise")]
+
+
+def quant_results(dev, reps=20):
+    """The dynamic e4m3fn quantiser on seeded N(0,1) bf16 matrices (the producer
+    of A and scale_a), with the MALL flushed before every launch.  Algorithmic
+    bytes: 2 per input element + 1 per code + 4 per scale.  The per-tensor mode
+    reads the input twice (amax pass, then conversion): its bytes count once."""
+    import torch
+    from precision_linear_amd import binding
+    from precision_linear_amd import workloads as wl
+    flush = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
+    res = []
+    for rows, cols, mode in QUANT_SHAPES:
+        bits = wl.bf16_matrix_bits(rows, cols, key=wl.workload_key(f"quant_{rows}x{cols}"))
+        x = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+        q, s = binding.fp8_quantize(x, mode)
+        evs = []
+        for i in range(reps + 3):
+            evict_caches(flush)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            binding.fp8_quantize(x, mode, q=q, scale=s)
+            e1.record()
+            if i >= 3:
+                evs.append((e0, e1))
+        torch.cuda.synchronize()
+        ts = sorted(a.elapsed_time(b) for a, b in evs)
+        t50 = ts[len(ts) // 2] * 1e-3
+        nbytes = 3 * rows * cols + 4 * (rows if mode == "rowwise" else 1)
+        gbs = nbytes / t50 / 1e9
+        res.append({"workload": f"quantize_e4m3_{mode}_{rows}x{cols}", "rows": rows, "cols": cols,
+                    "us_p50": round(t50 * 1e6, 2), "hbm_gbs": round(gbs, 1),
+                    "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)})
+        del x, q, s
+        torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -253,7 +292,7 @@ def main():
                      "traffic": traffic},
     }
     if not args.no_secondary:
-        line["secondary"] = skinny_results(dev)
+        line["secondary"] = skinny_results(dev) + quant_results(dev)
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(probs[0])
     print(json.dumps(line), flush=True)

@@ -201,6 +201,14 @@ def make_inputs(M: int, N: int, K: int, mode: int, recipe: str, bias: bool = Fal
     return Inputs(a, b, sa, sb, bias_bits, mode)
 
 
+def bf16_matrix_bits(rows: int, cols: int, key: int, std: float = 1.0) -> np.ndarray:
+    """Seeded rows x cols matrix of N(0, std) draws cast to bf16 by torch,
+    returned as uint16 bit patterns (the quantiser's input)."""
+    torch = _torch()
+    x = _bf16_normal(key, 5, (rows, cols), std)
+    return torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16).copy()
+
+
 def _bf16_bits_normal(rng, n) -> np.ndarray:
     torch = _torch()
     x = rng.standard_normal(n, dtype=np.float32)
