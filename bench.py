@@ -144,6 +144,25 @@ def skinny_results(dev, reps=20):
 QUANT_SHAPES = [(8192, 8192, "rowwise"), (8192, 8192, "per_tensor"), (128, 28672, "rowwise")]
 
 
+def gist_results(dev, reps=20):
+    """The gist's mid-size shape sweep (MFMA-bound), operands resident in HBM."""
+    import torch
+    from precision_linear_amd import workloads as wl
+    res = []
+    for name in [n for n in wl.WORKLOADS if n.startswith("gist")]:
+        p = Problem(name, dev)
+        time_launches(p, 3)
+        ts = sorted(time_launches(p, reps))
+        t50 = ts[len(ts) // 2] * 1e-3
+        tf = p.w.flops / t50 / 1e12
+        res.append({"workload": name, "M": p.w.M, "N": p.w.N, "K": p.w.K,
+                    "us_p50": round(t50 * 1e6, 2), "tflops": round(tf, 1),
+                    "frac_mfma": round(tf / PEAK_FP8_TFLOPS, 4)})
+        del p
+        torch.cuda.empty_cache()
+    return res
+
+
 def quant_results(dev, reps=20):
     """The dynamic e4m3fn quantiser on seeded N(0,1) bf16 matrices (the producer
     of A and scale_a), with the MALL flushed before every launch.  Algorithmic
@@ -292,7 +311,7 @@ def main():
                      "traffic": traffic},
     }
     if not args.no_secondary:
-        line["secondary"] = skinny_results(dev) + quant_results(dev)
+        line["secondary"] = skinny_results(dev) + gist_results(dev) + quant_results(dev)
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(probs[0])
     print(json.dumps(line), flush=True)

@@ -1152,7 +1152,7 @@ const ConfigInfo kConfigs[] = {
                pp::LDS_BYTES, 1, &launch_pp<8>, nullptr},
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
-constexpr int kMidConfig = 0;         // "bm128_bn128_bk128_w2x2_s3_mfma32"
+constexpr int kMidConfig = 8;         // "bm128_bn128_bk128_w2x4_s4_mfma32"
 constexpr int kSkinny16x64 = 1;       // "bm16_bn64_bk256_w1x4_s4_mfma16"
 constexpr int kSkinny16x112 = 2;      // "bm16_bn112_bk256_w1x7_s4_mfma16"
 constexpr int kSkinny64x112 = 5;      // "bm64_bn112_bk256_w1x7_s3_mfma16"
@@ -1175,10 +1175,12 @@ int choose_config(int64_t M, int64_t N, int64_t K, int mode, int has_bias) {
     if (M <= 16) return wide ? kSkinny16x112 : kSkinny16x64;
     if (M <= 64) return wide ? kSkinny64x112 : kSkinny64x64;
     if (M <= 128) return kSkinny128x128;
-    // 256 x 256 tiles on the ping-pong kernel once they fill most of the 256
-    // CUs; else 128 x 128.
+    // 256 x 256 tiles on the ping-pong kernel from about 96 tiles on (it beats
+    // 128 x 128 tiles down to there on MI355X even with CUs idle), when rows
+    // of the output allow its 16-byte stores; else 128 x 128 tiles (8 waves),
+    // with split-K when even those leave CUs idle.
     const int64_t big_tiles = cdiv(M, 256) * cdiv(N, 256);
-    if (big_tiles >= 192) return kPingPongConfig;
+    if (big_tiles >= 96 && N % 8 == 0) return kPingPongConfig;
     return kMidConfig;
 }
 

@@ -68,7 +68,8 @@ def _wl(name, M, N, K, mode, recipe, bias=False):
 
 # The synthetic workloads: square shapes with N(0,1) inputs quantised by amax,
 # skinny inference shapes (activations N(0,1), weights N(0,0.02), bf16 bias),
-# and ragged shapes whose operands are raw e4m3fn codes.
+# ragged shapes whose operands are raw e4m3fn codes, and the gist's mid-size
+# shape sweep with N(0,1) inputs.
 WORKLOADS = {w.name: w for w in [
     _wl("sq256_pt", 256, 256, 256, PER_TENSOR, "normal"),
     _wl("sq2048_rw", 2048, 2048, 2048, ROWWISE, "normal"),
@@ -81,6 +82,12 @@ WORKLOADS = {w.name: w for w in [
     _wl(f"ragged_{m}x{n}x{k}_{MODE_NAMES[mode]}", m, n, k, mode, "codes")
     for (m, n, k) in ((4096, 4096, 32), (4095, 4097, 96), (8191, 1000, 4160),
                       (16384, 16384, 8192))
+    for mode in (PER_TENSOR, ROWWISE)
+] + [
+    # the gist "matmul_fp8.py" `main` shape sweep (M, K, N), both scaling modes
+    _wl(f"gist_m{m}_k{k}_n{n}_{MODE_NAMES[mode]}", m, n, k, mode, "normal")
+    for m in (512, 1152, 2304, 4608)
+    for (k, n) in ((3072, 12288), (12288, 3072))
     for mode in (PER_TENSOR, ROWWISE)
 ]}
 
