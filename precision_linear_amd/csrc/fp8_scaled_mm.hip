@@ -22,7 +22,9 @@
 //   * Inner loop: v_mfma_f32_32x32x64_f8f6f4 (or 16x16x128) with e4m3 operands
 //     and fp32 accumulators held in registers for the whole K loop.
 //   * Epilogue: scale (fp32 sa*sb in both modes), optional bias, RNE to bf16,
-//     stores of 4 consecutive bf16 per lane (8 bytes) where the row allows.
+//     then the bf16 tile goes through LDS so that the stores to the output
+//     write whole runs of its rows (16, 4 or 2 bytes per lane, as wide as the
+//     row alignment allows).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -57,6 +59,7 @@ struct Params {
     int rowwise;
     int vec_store;         // N % 4 == 0 and out 8-byte aligned
     int vec16;             // N % 8 == 0 and out 16-byte aligned
+    int vec4;              // N % 2 == 0 and out 4-byte aligned
     // Split-K: each output tile is computed by `splits` work units, unit s
     // covering K slices [s*k_chunk, (s+1)*k_chunk).  With splits > 1 the fp32
     // partial tiles go to `partials` and the unit that arrives last at the
@@ -186,7 +189,12 @@ struct Cfg {
     // MFMAs to hide them (the big, MFMA-bound tiles).
     static constexpr bool INTERLEAVE = MI == 32 && FM * FN >= 8;
     static constexpr int BK_ = BK;
+    static constexpr int BM_ = BM;
+    static constexpr int BN_ = BN;
     static constexpr int STAGES_ = STAGES;
+    // The epilogue stages the finished bf16 tile (rows of BN * 2 bytes, whole
+    // 16-byte chunks) in the stage buffers.
+    static constexpr int STG_CHUNKS = BN * 2 / 16;
     static_assert(WTM % MI == 0 && WTN % MI == 0, "wave tile must hold whole MFMA tiles");
     static_assert(MI % 16 == 0, "fragment row blocks must be 16-row aligned for the swizzle");
     static_assert(BK % KSTEP == 0, "BK must be a multiple of the MFMA K step");
@@ -194,6 +202,7 @@ struct Cfg {
     static_assert(A_BYTES % 1024 == 0 && B_BYTES % 1024 == 0, "stages are whole 1 KiB blocks");
     static_assert(LDS_BYTES <= 160 * 1024, "gfx950 LDS is 160 KiB per workgroup");
     static_assert(STAGES >= 2, "at least double buffering");
+    static_assert(BN % 8 == 0 && BM * BN * 2 <= MAIN_BYTES, "the output tile fits the stage buffers");
     static_assert(LOADS * (STAGES - 1) <= 63, "vmcnt counts up to 63");
 };
 
@@ -442,6 +451,121 @@ __device__ __forceinline__ void store_tile(const typename Mfma<MI>::acc_t (&acc)
         }
     }
 #undef FP8MM_EPI
+}
+
+// Staged epilogue of the generic kernel, first half: each wave converts its
+// FM x FN blocks (y = acc * s, or fma(acc, s, bias); RNE to bf16) and writes
+// them into a row-major copy of the whole BM x BN tile in LDS.  Row r of that
+// copy has STG_CHUNKS 16-byte chunks; chunk c sits at position (c + r) mod
+// STG_CHUNKS, so the lanes of one MFMA block, which hold one column run each
+// of consecutive rows, write to different banks.  Rows and columns outside
+// the output are converted too (from zero accumulators) and never stored.
+template <class C, bool RW, bool BIAS>
+__device__ __forceinline__ void stage_tile_impl(
+    const typename Mfma<C::MI_>::acc_t (&acc)[C::FN][C::FM], uint8_t* stg, int mbase, int nbase,
+    const float* epi_sa, const float* epi_sb, const uint16_t* epi_bias, float s_pt, int lane) {
+    constexpr int MI = C::MI_;
+    constexpr int G = Mfma<MI>::NACC / 4;
+    constexpr int NCH = C::STG_CHUNKS;
+    float sa_r[C::FM];
+#pragma unroll
+    for (int j = 0; j < C::FM; ++j) sa_r[j] = RW ? epi_sa[mbase + j * MI + lane % MI] : s_pt;
+    // Column runs outermost: each run's scales and bias are read once and
+    // stay live only while its FM row blocks are written.
+#pragma unroll
+    for (int i = 0; i < C::FN; ++i)
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            const int nl = nbase + i * MI + (MI == 32 ? 8 * g + 4 * (lane / 32) : 4 * (lane / 16));
+            v4f sb_r;
+            uint2 b_r;
+            if constexpr (RW) sb_r = *reinterpret_cast<const v4f*>(epi_sb + nl);
+            if constexpr (BIAS) b_r = *reinterpret_cast<const uint2*>(epi_bias + nl);
+            const int byte = nl * 2;   // a multiple of 8: one half of a chunk
+#pragma unroll
+            for (int j = 0; j < C::FM; ++j) {
+                const int ml = mbase + j * MI + lane % MI;
+                float y[4];
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const float sc = RW ? sa_r[j] * sb_r[c] : s_pt;
+                    const float v = acc[i][j][4 * g + c];
+                    if constexpr (BIAS) {
+                        const uint32_t bw = c < 2 ? b_r.x : b_r.y;
+                        const float bv = __uint_as_float(c % 2 == 0 ? bw << 16 : bw & 0xffff0000u);
+                        y[c] = __builtin_fmaf(v, sc, bv);
+                    } else {
+                        y[c] = v * sc;
+                    }
+                }
+                uint2 w;
+                w.x = pack_bf16x2(y[0], y[1]);
+                w.y = pack_bf16x2(y[2], y[3]);
+                *reinterpret_cast<uint2*>(stg + ml * (NCH * 16) + (((byte >> 4) + ml) % NCH) * 16 +
+                                          (byte & 15)) = w;
+            }
+        }
+}
+
+// Second half: the workgroup stores the staged tile row by row, consecutive
+// lanes on consecutive W-byte pieces of a row, so each store instruction
+// writes whole runs of a row instead of a few bytes of many rows.  W is the
+// widest piece every row start allows: 16 (N % 8 == 0, out 16-byte aligned),
+// 4 (N even, out 4-byte aligned) or 2.  Only rows and columns inside the
+// output are written.
+template <class C, int W>
+__device__ __forceinline__ void store_staged(const uint8_t* stg, const Params& p, int row0, int col0,
+                                             int tid) {
+    constexpr int NCH = C::STG_CHUNKS;
+    constexpr int CW = C::BN_ * 2 / W;               // pieces per row
+    constexpr int TOTAL = C::BM_ * CW;
+    constexpr int ITERS = (TOTAL + C::THREADS - 1) / C::THREADS;
+    const int rows = min(C::BM_, p.M - row0);
+    const int pieces = min(CW, (p.N - col0) * 2 / W);   // W divides 2 * N here
+#pragma unroll 4
+    for (int it = 0; it < ITERS; ++it) {
+        const int q = tid + it * C::THREADS;
+        const int r = q / CW;
+        const int cw = q - r * CW;
+        if (q >= TOTAL || r >= rows || cw >= pieces) continue;
+        const int byte = cw * W;
+        const uint8_t* src = stg + r * (NCH * 16) + (((byte >> 4) + r) % NCH) * 16 + (byte & 15);
+        uint16_t* dst = p.out + (size_t)(row0 + r) * p.N + col0 + byte / 2;
+        if constexpr (W == 16)
+            *reinterpret_cast<v4i*>(dst) = *reinterpret_cast<const v4i*>(src);
+        else if constexpr (W == 4)
+            *reinterpret_cast<uint32_t*>(dst) = *reinterpret_cast<const uint32_t*>(src);
+        else
+            *dst = *reinterpret_cast<const uint16_t*>(src);
+    }
+}
+
+template <class C>
+__device__ __forceinline__ void stage_and_store(
+    const typename Mfma<C::MI_>::acc_t (&acc)[C::FN][C::FM], uint8_t* stg, const Params& p,
+    int row0, int col0, int mbase, int nbase, const float* epi_sa, const float* epi_sb,
+    const uint16_t* epi_bias, float s_pt, bool has_bias, int lane, int tid) {
+    // As in store_tile: opaque lane id, so the addresses are not kept live
+    // across the K loop.
+    asm volatile("" : "+v"(lane));
+    if (p.rowwise) {
+        if (has_bias)
+            stage_tile_impl<C, true, true>(acc, stg, mbase, nbase, epi_sa, epi_sb, epi_bias, s_pt, lane);
+        else
+            stage_tile_impl<C, true, false>(acc, stg, mbase, nbase, epi_sa, epi_sb, epi_bias, s_pt, lane);
+    } else {
+        if (has_bias)
+            stage_tile_impl<C, false, true>(acc, stg, mbase, nbase, epi_sa, epi_sb, epi_bias, s_pt, lane);
+        else
+            stage_tile_impl<C, false, false>(acc, stg, mbase, nbase, epi_sa, epi_sb, epi_bias, s_pt, lane);
+    }
+    barrier_lds();
+    if (p.vec16)
+        store_staged<C, 16>(stg, p, row0, col0, tid);
+    else if (p.vec4)
+        store_staged<C, 4>(stg, p, row0, col0, tid);
+    else
+        store_staged<C, 2>(stg, p, row0, col0, tid);
 }
 
 // One K stage (BK bytes of K) of the software pipeline.  The fragments of
@@ -695,7 +819,7 @@ fp8_gemm_kernel(Params p) {
                 for (int j = 0; j < C::FM; ++j) acc[i][j] = sum[i][j];
         }
 
-        // Epilogue parameters into LDS (the stage buffers are not touched).
+        // Epilogue parameters into LDS (beside the stage buffers).
         if (p.rowwise || has_bias) {
 #pragma unroll
             for (int i = 0; i < C::NSA; ++i) {
@@ -710,11 +834,14 @@ fp8_gemm_kernel(Params p) {
                     epi_bias[c] = bias_v[i];
                 }
             }
-            barrier_lds();
         }
-
-        store_tile<MI, C::FM, C::FN>(acc, p, row0, col0, wm * C::WTM, wn * C::WTN, epi_sa, epi_sb,
-                                     epi_bias, s_pt, has_bias, lane);
+        // The output tile is staged in the stage buffers: every wave must be
+        // done reading the last stage, and every load (including the trailing
+        // ones of slices past the end) must have landed.
+        wait_vmcnt<0>();
+        barrier_lds();
+        stage_and_store<C>(acc, smem, p, row0, col0, wm * C::WTM, wn * C::WTN, epi_sa, epi_sb,
+                           epi_bias, s_pt, has_bias, lane, tid);
     }
 }
 
@@ -1369,6 +1496,7 @@ int fp8_scaled_mm_with_plan(const void* A, const void* B, const float* scale_a,
     p.rowwise = mode == FP8MM_ROWWISE;
     p.vec_store = (N % 4 == 0) && aligned(out, 8);
     p.vec16 = (N % 8 == 0) && aligned(out, 16);
+    p.vec4 = (N % 2 == 0) && aligned(out, 4);
     p.splits = sp;
     p.k_chunk = (int)cdiv(k_iters, sp);
     p.counters = nullptr;
