@@ -683,9 +683,12 @@ fp8_gemm_kernel(Params p) {
         const __amdgpu_buffer_rsrc_t rb =
             make_rsrc(p.B + (size_t)col0 * p.K + kskip, rows_b * (uint32_t)p.K - (uint32_t)kskip);
 
-        // Every wave must be done with the LDS of the previous tile (and its
-        // own epilogue stores must have left) before this tile's loads start.
-        wait_vmcnt<0>();
+        // Every wave must be done with the LDS of the previous tile before
+        // this tile's loads start.  The previous tile's output stores may
+        // still be in flight: vector memory operations are counted together,
+        // and loads return in order among themselves, so a wait for "at most
+        // n outstanding" still covers every load older than the last n; the
+        // stores only make the first wait of the tile longer.
         barrier_lds();
 
         // This tile's scales and bias, fetched now into registers and moved to
