@@ -1,4 +1,4 @@
-"""Plain CPU oracle for the FP8 (e4m3fn) scaled matrix multiply.
+"""Plain CPU oracle for the FP8 (e4m3fn, e5m2) scaled matrix multiply.
 
 TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
 benchmark's CPU-baseline leg may import this module.  The GPU library never
@@ -8,7 +8,8 @@ What it computes (the plain definition of the method):
 
     out[m, n] = RNE_bf16( s[m, n] * sum_k dec(A[m, k]) * dec(B[n, k])  (+ bias[n]) )
 
-  * A is M x K and B is N x K, both e4m3fn codes with K fastest.  B is the
+  * A is M x K and B is N x K, float8 codes with K fastest: e4m3fn, or
+    e5m2 (the gist's `benchmark` takes either dtype), each operand its own.  B is the
     K x N column-major right operand of the pages ("TN"): the gist
     "matmul_fp8.py", function `benchmark`, makes b column-major before the
     call, and the row-wise kernel PR (pytorch #125204, Summary) supports only
@@ -37,6 +38,13 @@ import numpy as np
 PER_TENSOR = 0
 ROWWISE = 1
 
+# Operand formats.  The gist's `benchmark` accepts float8_e4m3fn or
+# float8_e5m2 as the operand dtype (its quantisation branch lists both);
+# A and B may also differ.
+E4M3FN = 0
+E5M2 = 1
+FORMAT_NAMES = {E4M3FN: "e4m3fn", E5M2: "e5m2"}
+
 
 def e4m3fn_value(code: int) -> float:
     """Closed-form value of one OCP float8 e4m3fn byte.
@@ -57,16 +65,52 @@ def e4m3fn_value(code: int) -> float:
     return sign * (1.0 + m / 8.0) * 2.0 ** (e - 7)
 
 
+def e5m2_value(code: int) -> float:
+    """Closed-form value of one OCP float8 e5m2 byte.
+
+    Bit layout s eeeee mm, exponent bias 15, IEEE-style specials: exponent
+    field 31 is infinity (mantissa 0) or NaN (mantissa 1..3); exponent field
+    0 is subnormal, m * 2^-16; otherwise (1 + m/4) * 2^(e-15).  The largest
+    finite magnitude is 1.75 * 2^15 = 57344 (torch.finfo(float8_e5m2).max,
+    the clamp limit of the gist's quantisation for that dtype).
+    """
+    s = (code >> 7) & 1
+    e = (code >> 2) & 0x1F
+    m = code & 0x3
+    sign = -1.0 if s else 1.0
+    if e == 0x1F:
+        return sign * float("inf") if m == 0 else float("nan")
+    if e == 0:
+        return sign * m * 2.0 ** -16
+    return sign * (1.0 + m / 4.0) * 2.0 ** (e - 15)
+
+
 def e4m3fn_decode_table() -> np.ndarray:
     """fp64 value of every byte code 0..255."""
     return np.array([e4m3fn_value(c) for c in range(256)], dtype=np.float64)
 
 
+def e5m2_decode_table() -> np.ndarray:
+    """fp64 value of every e5m2 byte code 0..255."""
+    return np.array([e5m2_value(c) for c in range(256)], dtype=np.float64)
+
+
 _DECODE = e4m3fn_decode_table()
+_DECODE_E5M2 = e5m2_decode_table()
+
+# Every finite value of a format is an integer multiple of 2^-UNIT_EXP: its
+# smallest subnormal.
+UNIT_EXP = {E4M3FN: 9, E5M2: 16}
 
 
-def decode(codes: np.ndarray) -> np.ndarray:
-    return _DECODE[np.asarray(codes, dtype=np.uint8)]
+def decode(codes: np.ndarray, fmt: int = E4M3FN) -> np.ndarray:
+    if fmt == E4M3FN:
+        table = _DECODE
+    elif fmt == E5M2:
+        table = _DECODE_E5M2
+    else:
+        raise ValueError(f"unknown operand format {fmt}")
+    return table[np.asarray(codes, dtype=np.uint8)]
 
 
 def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
@@ -100,12 +144,36 @@ def f64_to_bf16_rne(y: np.ndarray) -> np.ndarray:
     return bits.astype(np.uint16)
 
 
-def scaled_mm(a, b, scale_a, scale_b, bias=None, mode=PER_TENSOR, rows=None, cols=None):
+def _exact_integer_acc(da: np.ndarray, db: np.ndarray, qa: int, qb: int) -> np.ndarray:
+    """sum_k da[m, k] * db[n, k] for finite values that are integer multiples
+    of 2^-qa and 2^-qb, formed exactly in integers and rounded once to fp64.
+
+    With na = da * 2^qa and nb = db * 2^qb (integers, |na|, |nb| < 2^32 for
+    both formats), nb is split as hi * 2^16 + lo with 0 <= lo < 2^16 and
+    |hi| < 2^16.  Each of sum_k na*hi and sum_k na*lo then stays below
+    2^32 * 2^16 * K <= 2^63 for K <= 32768, so both int64 products are exact;
+    they are joined as Python integers and converted to fp64 once (Python's
+    int -> float conversion rounds to nearest even), then scaled by the exact
+    power of two 2^-(qa + qb).
+    """
+    na = np.rint(np.ldexp(da, qa)).astype(np.int64)
+    nb = np.rint(np.ldexp(db, qb)).astype(np.int64)
+    hi = nb >> 16                         # floor division by 2^16
+    lo = nb & 0xFFFF
+    s_hi = na @ hi.T
+    s_lo = na @ lo.T
+    total = s_hi.astype(object) * 65536 + s_lo.astype(object)
+    acc = np.array([float(v) for v in total.ravel()], dtype=np.float64).reshape(total.shape)
+    return np.ldexp(acc, -(qa + qb))
+
+
+def scaled_mm(a, b, scale_a, scale_b, bias=None, mode=PER_TENSOR, rows=None, cols=None,
+              a_format=E4M3FN, b_format=E4M3FN):
     """Reference result for out[rows][:, cols] (all rows/cols by default).
 
     a: uint8 [M, K] codes; b: uint8 [N, K] codes; scale_a/scale_b: float32
     arrays of length 1 (per-tensor) or M / N (row-wise); bias: uint16 [N] bf16
-    bits or None.
+    bits or None; a_format / b_format: E4M3FN (default) or E5M2.
 
     Returns a dict with
       bits : uint16 [m, n]  the bf16 output
@@ -120,6 +188,12 @@ def scaled_mm(a, b, scale_a, scale_b, bias=None, mode=PER_TENSOR, rows=None, col
     K <= 2^16 terms stays below 2^52 units.  All of them are fp64 numbers, so
     the fp64 sum is exact in any order; the matrix product below is just a
     convenient way to form it.
+
+    With an e5m2 operand that argument fails (e5m2 spans 2^-16 .. 57344, so a
+    sum can need more than 53 bits); acc is then the exact integer sum of
+    `_exact_integer_acc` rounded once to fp64 (relative error <= 2^-53), for
+    finite codes and K <= 32768, and mag is the fp64 matrix product of the
+    magnitudes (a tolerance term, relative error below K * 2^-53).
     """
     a = np.asarray(a, dtype=np.uint8)
     b = np.asarray(b, dtype=np.uint8)
@@ -132,9 +206,16 @@ def scaled_mm(a, b, scale_a, scale_b, bias=None, mode=PER_TENSOR, rows=None, col
     rows = np.arange(M) if rows is None else np.asarray(rows, dtype=np.int64)
     cols = np.arange(N) if cols is None else np.asarray(cols, dtype=np.int64)
 
-    da = decode(a[rows])                     # [m, K]
-    db = decode(b[cols])                     # [n, K]
-    acc = da @ db.T
+    da = decode(a[rows], a_format)           # [m, K]
+    db = decode(b[cols], b_format)           # [n, K]
+    if a_format == E4M3FN and b_format == E4M3FN:
+        acc = da @ db.T
+    else:
+        if K > 32768:
+            raise ValueError("the integer accumulation is only argued for K <= 32768")
+        if not (np.all(np.isfinite(da)) and np.all(np.isfinite(db))):
+            raise ValueError("e5m2 operands must be finite (no inf or NaN codes)")
+        acc = _exact_integer_acc(da, db, UNIT_EXP[a_format], UNIT_EXP[b_format])
     mag = np.abs(da) @ np.abs(db).T
 
     sa = np.asarray(scale_a, dtype=np.float32).astype(np.float64).reshape(-1)
