@@ -63,6 +63,14 @@ enum fp8q_status {
 int fp8_quantize_e4m3(const void* x, void* q, float* scale, int64_t rows, int64_t cols,
                       int scaling_mode, struct ihipStream_t* stream);
 
+/* The same for float8 e5m2 codes (the gist's `benchmark` quantises for
+ * float8_e5m2 the same way, with finfo(float8_e5m2).max = 57344):
+ *     scale = amax / 57344;  q = e5m2_RNE( clamp( x / scale, -57344, 57344 ) )
+ * Arguments, preconditions and errors as for fp8_quantize_e4m3; the codes are
+ * what fp8_scaled_mm_typed takes with FP8MM_E5M2. */
+int fp8_quantize_e5m2(const void* x, void* q, float* scale, int64_t rows, int64_t cols,
+                      int scaling_mode, struct ihipStream_t* stream);
+
 /* Static, NUL-terminated text for a status code. */
 const char* fp8_quantize_status_string(int status);
 

@@ -8,7 +8,8 @@
  *     out[m][n] = bf16_rne( s[m][n] * sum_{k<K} A[m][k] * B[n][k]  (+ bias[n]) )
  *
  *   A    M x K float8 e4m3fn (OCP), row-major, row stride K bytes.
- *   B    N x K float8 e4m3fn, row-major, row stride K bytes.  This is the
+ *   B    N x K float8 e4m3fn, row-major, row stride K bytes.
+ *        (fp8_scaled_mm_typed also takes e5m2 for either operand.)  This is the
  *        "TN" right operand: the K x N column-major matrix of the pages,
  *        handed over as its N x K transpose (PR #125204 Summary: only TN is
  *        supported and the scale of B runs along its fast dimension).
@@ -80,7 +81,15 @@ enum fp8mm_status {
     FP8MM_ERR_DEVICE = 5,  /* no usable HIP device, or not a gfx950 */
     FP8MM_ERR_LAUNCH = 6,  /* the kernel launch failed */
     FP8MM_ERR_CONFIG = 7,  /* unknown tile configuration id or split count */
-    FP8MM_ERR_WORKSPACE = 8 /* caller workspace smaller than required */
+    FP8MM_ERR_WORKSPACE = 8, /* caller workspace smaller than required */
+    FP8MM_ERR_FORMAT = 9     /* unknown operand format */
+};
+
+/* Operand formats (OCP 8-bit floating point).  The gist "matmul_fp8.py",
+ * function `benchmark`, accepts float8_e4m3fn or float8_e5m2 operands. */
+enum fp8mm_format {
+    FP8MM_E4M3FN = 0,   /* bias 7, no infinities, NaN = S.1111.111, max 448 */
+    FP8MM_E5M2 = 1      /* bias 15, IEEE-style inf/NaN, max 57344 */
 };
 
 /* The scaled multiply described above, with the tile configuration chosen
@@ -111,6 +120,20 @@ int fp8_scaled_mm_with_plan(const void* A, const void* B, const float* scale_a,
                             int64_t M, int64_t N, int64_t K, int scaling_mode,
                             struct ihipStream_t* stream, int config_id, int splits,
                             void* workspace, int64_t workspace_bytes);
+
+/* fp8_scaled_mm_with_plan with the operand formats given: A holds a_format
+ * codes and B b_format codes (FP8MM_E4M3FN or FP8MM_E5M2 each; mixed pairs
+ * allowed).  The products of two float8 values are exact in fp32 for every
+ * pair, so only the format decode differs; the rest of the contract, the
+ * configurations and the workspace rules are those of fp8_scaled_mm_with_plan
+ * (which is this call with both formats FP8MM_E4M3FN).  Infinite or NaN
+ * inputs give IEEE results of the fp32 accumulation (not otherwise checked).
+ * Returns FP8MM_ERR_FORMAT for any other format value. */
+int fp8_scaled_mm_typed(const void* A, int a_format, const void* B, int b_format,
+                        const float* scale_a, const float* scale_b, const void* bias_or_null,
+                        void* out, int64_t M, int64_t N, int64_t K, int scaling_mode,
+                        struct ihipStream_t* stream, int config_id, int splits, void* workspace,
+                        int64_t workspace_bytes);
 
 /* Workspace bytes the plan (config_id, splits; negative/zero = automatic)
  * needs for this problem; 0 when it does not split K, -1 for a bad mode.

@@ -20,15 +20,22 @@ ROWWISE = 1
 _MODES = {"per_tensor": PER_TENSOR, "tensorwise": PER_TENSOR, "rowwise": ROWWISE,
           PER_TENSOR: PER_TENSOR, ROWWISE: ROWWISE}
 
+# operand formats (enum fp8mm_format)
+E4M3FN = 0
+E5M2 = 1
+_FORMATS = {"e4m3fn": E4M3FN, "e5m2": E5M2, E4M3FN: E4M3FN, E5M2: E5M2}
+
 # status codes from include/fp8_scaled_mm.h
-OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_MODE, ERR_DEVICE, ERR_LAUNCH, ERR_CONFIG, ERR_WORKSPACE = range(9)
-_ARG_ERRORS = {ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_MODE, ERR_CONFIG, ERR_WORKSPACE}
+(OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_MODE, ERR_DEVICE, ERR_LAUNCH, ERR_CONFIG, ERR_WORKSPACE,
+ ERR_FORMAT) = range(10)
+_ARG_ERRORS = {ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_MODE, ERR_CONFIG, ERR_WORKSPACE, ERR_FORMAT}
 
 EXPORTS = ("fp8_scaled_mm", "fp8_scaled_mm_with_config", "fp8_scaled_mm_with_plan",
+           "fp8_scaled_mm_typed",
            "fp8_scaled_mm_workspace_size", "fp8_scaled_mm_select_splits",
            "fp8_scaled_mm_num_configs", "fp8_scaled_mm_config_name", "fp8_scaled_mm_select_config",
            "fp8_scaled_mm_grid_size", "fp8_scaled_mm_status_string",
-           "fp8_quantize_e4m3", "fp8_quantize_status_string")
+           "fp8_quantize_e4m3", "fp8_quantize_e5m2", "fp8_quantize_status_string")
 
 # status codes from include/fp8_quantize.h
 Q_OK, Q_ERR_NULL, Q_ERR_SHAPE, Q_ERR_ALIGN, Q_ERR_MODE, Q_ERR_DEVICE, Q_ERR_LAUNCH = range(7)
@@ -60,6 +67,9 @@ def lib() -> ctypes.CDLL:
         L.fp8_scaled_mm_with_plan.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, vp, i32,
                                               i32, vp, i64]
         L.fp8_scaled_mm_with_plan.restype = i32
+        L.fp8_scaled_mm_typed.argtypes = [vp, i32, vp, i32, vp, vp, vp, vp, i64, i64, i64, i32, vp,
+                                          i32, i32, vp, i64]
+        L.fp8_scaled_mm_typed.restype = i32
         L.fp8_scaled_mm_workspace_size.argtypes = [i64, i64, i64, i32, i32, i32, i32]
         L.fp8_scaled_mm_workspace_size.restype = i64
         L.fp8_scaled_mm_select_splits.argtypes = [i64, i64, i64, i32, i32, i32]
@@ -76,6 +86,8 @@ def lib() -> ctypes.CDLL:
         L.fp8_scaled_mm_status_string.restype = ctypes.c_char_p
         L.fp8_quantize_e4m3.argtypes = [vp, vp, vp, i64, i64, i32, vp]
         L.fp8_quantize_e4m3.restype = i32
+        L.fp8_quantize_e5m2.argtypes = [vp, vp, vp, i64, i64, i32, vp]
+        L.fp8_quantize_e5m2.restype = i32
         L.fp8_quantize_status_string.argtypes = [i32]
         L.fp8_quantize_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -105,28 +117,41 @@ def workspace_size(M, N, K, mode, has_bias=False, config=-1, splits=0) -> int:
                                                   int(config), int(splits)))
 
 
-def _as_codes(t: torch.Tensor, name: str) -> torch.Tensor:
-    if t.dtype == torch.float8_e4m3fn:
-        return t.view(torch.uint8)
+_TORCH_FORMATS = {torch.float8_e4m3fn: E4M3FN, torch.float8_e5m2: E5M2}
+
+
+def _as_codes(t: torch.Tensor, name: str, fmt) -> tuple:
+    """(uint8 view, format id).  A float8 tensor carries its format; uint8
+    codes take `fmt` (default e4m3fn)."""
+    if fmt is not None and fmt not in _FORMATS:
+        raise ValueError(f"{name}_format must be 'e4m3fn' or 'e5m2', got {fmt!r}")
+    if t.dtype in _TORCH_FORMATS:
+        f = _TORCH_FORMATS[t.dtype]
+        if fmt is not None and _FORMATS[fmt] != f:
+            raise ValueError(f"{name} is {t.dtype} but {name}_format={fmt!r}")
+        return t.view(torch.uint8), f
     if t.dtype == torch.uint8:
-        return t
-    raise ValueError(f"{name} must be float8_e4m3fn (or uint8 codes), got {t.dtype}")
+        return t, E4M3FN if fmt is None else _FORMATS[fmt]
+    raise ValueError(f"{name} must be float8_e4m3fn, float8_e5m2 or uint8 codes, got {t.dtype}")
 
 
 def fp8_scaled_mm(a: torch.Tensor, b: torch.Tensor, scale_a: torch.Tensor, scale_b: torch.Tensor,
                   bias: torch.Tensor | None = None, out: torch.Tensor | None = None,
                   mode="per_tensor", config: int = -1, splits: int = 0,
-                  workspace: torch.Tensor | None = None) -> torch.Tensor:
+                  workspace: torch.Tensor | None = None, a_format=None,
+                  b_format=None) -> torch.Tensor:
     """out = bf16(scale_a * scale_b * (a @ b^T) + bias) with a: M x K and b: N x K
-    (e4m3fn, K contiguous).  b may also be given as a K x N column-major view
-    (stride (1, K)), which is the same memory.  `config` (-1: automatic) and
-    `splits` (0: automatic) select the plan; `workspace` (a GPU byte tensor,
-    zero-filled before first use) replaces the library-owned split-K workspace."""
+    (float8 codes, K contiguous).  b may also be given as a K x N column-major
+    view (stride (1, K)), which is the same memory.  Each operand is e4m3fn or
+    e5m2: taken from its torch dtype, or from a_format / b_format for uint8
+    codes (default e4m3fn).  `config` (-1: automatic) and `splits` (0:
+    automatic) select the plan; `workspace` (a GPU byte tensor, zero-filled
+    before first use) replaces the library-owned split-K workspace."""
     if mode not in _MODES:
         raise ValueError(f"mode must be 'per_tensor' or 'rowwise', got {mode!r}")
     m = _MODES[mode]
-    a = _as_codes(a, "a")
-    b = _as_codes(b, "b")
+    a, fa = _as_codes(a, "a", a_format)
+    b, fb = _as_codes(b, "b", b_format)
     if a.dim() != 2 or b.dim() != 2:
         raise ValueError("a and b must be 2-D")
     M, K = a.shape
@@ -163,8 +188,8 @@ def fp8_scaled_mm(a: torch.Tensor, b: torch.Tensor, scale_a: torch.Tensor, scale
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
     stream = torch.cuda.current_stream(a.device).cuda_stream
     with torch.cuda.device(a.device):
-        st = lib().fp8_scaled_mm_with_plan(
-            a.data_ptr(), b.data_ptr(), scale_a.data_ptr(), scale_b.data_ptr(),
+        st = lib().fp8_scaled_mm_typed(
+            a.data_ptr(), fa, b.data_ptr(), fb, scale_a.data_ptr(), scale_b.data_ptr(),
             bias.data_ptr() if bias is not None else None, out.data_ptr(),
             M, N, K, m, stream, int(config), int(splits), ws_ptr, ws_bytes)
     if st != OK:
@@ -175,12 +200,17 @@ def fp8_scaled_mm(a: torch.Tensor, b: torch.Tensor, scale_a: torch.Tensor, scale
 
 
 def fp8_quantize(x: torch.Tensor, mode="rowwise", q: torch.Tensor | None = None,
-                 scale: torch.Tensor | None = None):
-    """(q, scale) = dynamic e4m3fn quantisation of a rows x cols bf16 GPU matrix:
-    scale = amax/448 (one value, or one per row), q = e4m3fn(clamp(x/scale, +-448))
-    as uint8 codes.  `q` and `scale` may be passed to reuse buffers."""
+                 scale: torch.Tensor | None = None, fmt="e4m3fn"):
+    """(q, scale) = dynamic float8 quantisation of a rows x cols bf16 GPU matrix:
+    scale = amax/qmax (one value, or one per row), q = RNE(clamp(x/scale, +-qmax))
+    as uint8 codes, with qmax = 448 (fmt 'e4m3fn') or 57344 ('e5m2').  `q` and
+    `scale` may be passed to reuse buffers."""
     if mode not in _MODES:
         raise ValueError(f"mode must be 'per_tensor' or 'rowwise', got {mode!r}")
+    if fmt not in _FORMATS:
+        raise ValueError(f"fmt must be 'e4m3fn' or 'e5m2', got {fmt!r}")
+    f = _FORMATS[fmt]
+    fn_name = "fp8_quantize_e4m3" if f == E4M3FN else "fp8_quantize_e5m2"
     m = _MODES[mode]
     if x.dtype != torch.bfloat16 or x.dim() != 2 or not x.is_contiguous() or not x.is_cuda:
         raise ValueError("x must be a contiguous 2-D bf16 GPU tensor")
@@ -188,20 +218,20 @@ def fp8_quantize(x: torch.Tensor, mode="rowwise", q: torch.Tensor | None = None,
     n_scale = 1 if m == PER_TENSOR else rows
     if q is None:
         q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
-    elif q.dtype not in (torch.uint8, torch.float8_e4m3fn) or tuple(q.shape) != (rows, cols) \
-            or not q.is_contiguous():
-        raise ValueError("q must be a contiguous uint8 (or float8_e4m3fn) rows x cols tensor")
+    elif q.dtype not in (torch.uint8, torch.float8_e4m3fn if f == E4M3FN else torch.float8_e5m2) \
+            or tuple(q.shape) != (rows, cols) or not q.is_contiguous():
+        raise ValueError(f"q must be a contiguous uint8 (or float8_{fmt}) rows x cols tensor")
     if scale is None:
         scale = torch.empty(n_scale, dtype=torch.float32, device=x.device)
     elif scale.dtype != torch.float32 or scale.numel() != n_scale or not scale.is_contiguous():
         raise ValueError(f"scale must be a contiguous float32 tensor of {n_scale} elements")
     stream = torch.cuda.current_stream(x.device).cuda_stream
     with torch.cuda.device(x.device):
-        st = lib().fp8_quantize_e4m3(x.data_ptr() if x.numel() else None,
+        st = getattr(lib(), fn_name)(x.data_ptr() if x.numel() else None,
                                      q.data_ptr() if q.numel() else None, scale.data_ptr(),
                                      rows, cols, m, stream)
     if st != Q_OK:
-        msg = f"fp8_quantize_e4m3: {lib().fp8_quantize_status_string(st).decode()} (status {st})"
+        msg = f"{fn_name}: {lib().fp8_quantize_status_string(st).decode()} (status {st})"
         if st in _Q_ARG_ERRORS:
             raise ValueError(msg)
         raise RuntimeError(msg)

@@ -8,32 +8,51 @@ import os
 import shutil
 import subprocess
 import sys
+import tempfile
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SRCS = [os.path.join(HERE, "csrc", "fp8_scaled_mm.hip"),
-        os.path.join(HERE, "csrc", "fp8_quantize.hip")]
+# The host logic and C ABI, one translation unit per operand-format pair of
+# the multiply's kernels, and the quantiser.  They compile in parallel.
+SRCS = [os.path.join(HERE, "csrc", f) for f in
+        ["fp8_scaled_mm.hip"] + [f"fp8_gemm_f{k}.hip" for k in range(4)] + ["fp8_quantize.hip"]]
+HEADERS = [os.path.join(HERE, "csrc", "fp8_gemm_kernels.h")]
 LIB = os.path.join(HERE, "libfp8_scaled_mm.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     # packed fp32 VALU forms are kept out of every kernel
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(ROOT, "include"),
 ]
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, *SRCS, "-o", tmp]
+def _run(cmd, verbose):
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError(f"hipcc failed ({res.returncode}) building {' '.join(SRCS)}")
+        raise RuntimeError(f"hipcc failed ({res.returncode}): {' '.join(cmd)}")
     if verbose:
         sys.stderr.write(res.stderr)
-    shutil.move(tmp, LIB)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source to an object (in parallel), then link the
+    shared library; always rebuilds."""
+    from concurrent.futures import ThreadPoolExecutor
+    objdir = tempfile.mkdtemp(prefix="fp8mm_build_")
+    try:
+        objs = [os.path.join(objdir, os.path.basename(src) + ".o") for src in SRCS]
+        jobs = [[HIPCC, *FLAGS, "-c", src, "-o", obj] for src, obj in zip(SRCS, objs)]
+        workers = max(1, min(len(jobs), os.cpu_count() or 1))
+        with ThreadPoolExecutor(max_workers=workers) as ex:
+            list(ex.map(lambda c: _run(c, verbose), jobs))
+        tmp = LIB + ".tmp"
+        _run([HIPCC, "--offload-arch=gfx950", "-shared", *objs, "-o", tmp], verbose)
+        shutil.move(tmp, LIB)
+    finally:
+        shutil.rmtree(objdir, ignore_errors=True)
     return LIB
 
 

@@ -1,0 +1,4 @@
+// Kernels of the FP8 scaled multiply for A in e4m3fn and B in e4m3fn.
+#include "fp8_gemm_kernels.h"
+
+FP8MM_DEFINE_LAUNCH_TABLE(kLaunchF0, 0)

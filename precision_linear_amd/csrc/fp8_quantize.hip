@@ -1,11 +1,12 @@
-// Dynamic FP8 (e4m3fn) quantisation of a bf16 matrix for gfx950 (MI355X).
+// Dynamic FP8 (e4m3fn or e5m2) quantisation of a bf16 matrix for gfx950 (MI355X).
 //
-//   scale = amax / 448            (fp32; amax over the matrix or over each row)
-//   q     = e4m3fn_RNE( clamp( x / scale, -448, 448 ) )     (x / scale in fp32)
+//   scale = amax / qmax           (fp32; amax over the matrix or over each row)
+//   q     = RNE( clamp( x / scale, -qmax, qmax ) )          (x / scale in fp32)
 //
-// The quantisation of the gist "matmul_fp8.py" (a-r-r-o-w), functions
-// `get_scale` and `benchmark` (scale = amax / finfo(e4m3fn).max, divide,
-// clamp, cast): the producer of A and scale_a for the scaled multiply, which
+// qmax = 448 for e4m3fn, 57344 for e5m2.  The quantisation of the gist
+// "matmul_fp8.py" (a-r-r-o-w), functions `get_scale` and `benchmark`
+// (scale = amax / finfo(dtype).max, divide, clamp, cast, for either float8
+// dtype): the producer of A and scale_a for the scaled multiply, which
 // pytorch PR #130422, Testing, notes can be fused with the preceding op.
 // A row (or matrix) whose amax is 0 gets scale 0 and codes 0 (the division
 // would be 0/0).
@@ -20,7 +21,8 @@
 //     fp32 bit pattern, monotone for non-negative floats), a quantisation pass
 //     and a launch that turns the stored amax into the scale.
 //   * The division is the correctly rounded fp32 one; the conversion is
-//     v_cvt_pk_fp8_f32 (round to nearest even; inputs are already clamped).
+//     v_cvt_pk_fp8_f32 (e4m3) or v_cvt_pk_bf8_f32 (e5m2), round to nearest
+//     even; inputs are already clamped.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -31,7 +33,23 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kGroup = 16;                      // elements per thread per chunk
 constexpr int kChunkElems = kThreads * kGroup;  // 4096
-constexpr float kE4m3Max = 448.f;
+
+// Format parameters: FMT 0 = e4m3fn, 1 = e5m2.
+template <int FMT> struct Fp8Fmt;
+template <> struct Fp8Fmt<0> {
+    static constexpr float kMax = 448.f;
+    template <bool HI>
+    __device__ static __forceinline__ int cvt_pk(float a, float b, int old) {
+        return __builtin_amdgcn_cvt_pk_fp8_f32(a, b, old, HI);
+    }
+};
+template <> struct Fp8Fmt<1> {
+    static constexpr float kMax = 57344.f;
+    template <bool HI>
+    __device__ static __forceinline__ int cvt_pk(float a, float b, int old) {
+        return __builtin_amdgcn_cvt_pk_bf8_f32(a, b, old, HI);
+    }
+};
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
@@ -51,13 +69,16 @@ __device__ __forceinline__ float absmax16(const uint4 (&v)[2]) {
     return m;
 }
 
+template <int FMT>
 __device__ __forceinline__ float quant1(float x, float s) {
+    constexpr float kMax = Fp8Fmt<FMT>::kMax;
     if (s == 0.f) return 0.f;
     const float y = x / s;   // correctly rounded fp32 division
-    return fminf(fmaxf(y, -kE4m3Max), kE4m3Max);
+    return fminf(fmaxf(y, -kMax), kMax);
 }
 
-// 16 bf16 values -> 16 e4m3fn codes (one 16-byte vector).
+// 16 bf16 values -> 16 float8 codes (one 16-byte vector).
+template <int FMT>
 __device__ __forceinline__ uint4 quant16(const uint4 (&v)[2], float s) {
     uint32_t out[4];
 #pragma unroll
@@ -65,11 +86,11 @@ __device__ __forceinline__ uint4 quant16(const uint4 (&v)[2], float s) {
         const uint32_t w[4] = {v[h].x, v[h].y, v[h].z, v[h].w};
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
-            int packed = __builtin_amdgcn_cvt_pk_fp8_f32(quant1(bf16_lo(w[2 * p]), s),
-                                                         quant1(bf16_hi(w[2 * p]), s), 0, false);
-            packed = __builtin_amdgcn_cvt_pk_fp8_f32(quant1(bf16_lo(w[2 * p + 1]), s),
-                                                     quant1(bf16_hi(w[2 * p + 1]), s), packed,
-                                                     true);
+            int packed = Fp8Fmt<FMT>::template cvt_pk<false>(quant1<FMT>(bf16_lo(w[2 * p]), s),
+                                                             quant1<FMT>(bf16_hi(w[2 * p]), s), 0);
+            packed = Fp8Fmt<FMT>::template cvt_pk<true>(quant1<FMT>(bf16_lo(w[2 * p + 1]), s),
+                                                        quant1<FMT>(bf16_hi(w[2 * p + 1]), s),
+                                                        packed);
             out[2 * h + p] = (uint32_t)packed;
         }
     }
@@ -98,7 +119,7 @@ __device__ __forceinline__ float block_max(float m, float* red) {
 
 // Row-wise.  CHUNKS > 0: the row (at most CHUNKS * 4096 elements) is held in
 // registers; CHUNKS == 0: any length, read twice.
-template <int CHUNKS>
+template <int CHUNKS, int FMT>
 __global__ void __launch_bounds__(kThreads)
 quant_rowwise_kernel(const uint16_t* __restrict__ x, uint8_t* __restrict__ q, float* __restrict__ scale,
                      int64_t rows, int64_t cols) {
@@ -118,12 +139,12 @@ quant_rowwise_kernel(const uint16_t* __restrict__ x, uint8_t* __restrict__ q, fl
                     m = fmaxf(m, absmax16(v[c]));
                 }
             }
-            const float s = block_max(m, red) / kE4m3Max;
+            const float s = block_max(m, red) / Fp8Fmt<FMT>::kMax;
             if (threadIdx.x == 0) scale[r] = s;
 #pragma unroll
             for (int c = 0; c < CHUNKS; ++c) {
                 const int64_t g = threadIdx.x + (int64_t)c * kThreads;
-                if (g < groups) *reinterpret_cast<uint4*>(qr + g * kGroup) = quant16(v[c], s);
+                if (g < groups) *reinterpret_cast<uint4*>(qr + g * kGroup) = quant16<FMT>(v[c], s);
             }
         } else {
             for (int64_t g = threadIdx.x; g < groups; g += kThreads) {
@@ -131,12 +152,12 @@ quant_rowwise_kernel(const uint16_t* __restrict__ x, uint8_t* __restrict__ q, fl
                 load16(xr + g * kGroup, v);
                 m = fmaxf(m, absmax16(v));
             }
-            const float s = block_max(m, red) / kE4m3Max;
+            const float s = block_max(m, red) / Fp8Fmt<FMT>::kMax;
             if (threadIdx.x == 0) scale[r] = s;
             for (int64_t g = threadIdx.x; g < groups; g += kThreads) {
                 uint4 v[2];
                 load16(xr + g * kGroup, v);
-                *reinterpret_cast<uint4*>(qr + g * kGroup) = quant16(v, s);
+                *reinterpret_cast<uint4*>(qr + g * kGroup) = quant16<FMT>(v, s);
             }
         }
     }
@@ -170,22 +191,24 @@ amax_kernel(const uint16_t* __restrict__ x, int64_t groups, float* slot) {
     if (threadIdx.x == 0) atomicMax(reinterpret_cast<unsigned*>(slot), __float_as_uint(m));
 }
 
-// Per-tensor pass 2: quantise with scale = slot[0] / 448.
+// Per-tensor pass 2: quantise with scale = slot[0] / qmax.
+template <int FMT>
 __global__ void __launch_bounds__(kThreads)
 quant_tensor_kernel(const uint16_t* __restrict__ x, uint8_t* __restrict__ q, int64_t groups,
                     const float* slot) {
-    const float s = slot[0] / kE4m3Max;
+    const float s = slot[0] / Fp8Fmt<FMT>::kMax;
     for (int64_t g = blockIdx.x * (int64_t)kThreads + threadIdx.x; g < groups;
          g += (int64_t)gridDim.x * kThreads) {
         uint4 v[2];
         load16(x + g * kGroup, v);
-        *reinterpret_cast<uint4*>(q + g * kGroup) = quant16(v, s);
+        *reinterpret_cast<uint4*>(q + g * kGroup) = quant16<FMT>(v, s);
     }
 }
 
 // Per-tensor pass 3: the stored amax becomes the scale.
+template <int FMT>
 __global__ void amax_to_scale_kernel(float* slot) {
-    if (threadIdx.x == 0) slot[0] = slot[0] / kE4m3Max;
+    if (threadIdx.x == 0) slot[0] = slot[0] / Fp8Fmt<FMT>::kMax;
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
@@ -198,12 +221,9 @@ int device_cus_q() {
     return cus;
 }
 
-}  // namespace
-
-extern "C" {
-
-int fp8_quantize_e4m3(const void* x, void* q, float* scale, int64_t rows, int64_t cols,
-                      int scaling_mode, struct ihipStream_t* stream) {
+template <int FMT>
+int quantize_impl(const void* x, void* q, float* scale, int64_t rows, int64_t cols,
+                  int scaling_mode, struct ihipStream_t* stream) {
     if (scaling_mode != FP8Q_PER_TENSOR && scaling_mode != FP8Q_ROWWISE) return FP8Q_ERR_MODE;
     if (rows < 0 || cols < 0 || cols % kGroup != 0 || cols > (int64_t(1) << 31) ||
         rows > (int64_t(1) << 31))
@@ -229,19 +249,19 @@ int fp8_quantize_e4m3(const void* x, void* q, float* scale, int64_t rows, int64_
         const int64_t chunks = (cols + kChunkElems - 1) / kChunkElems;
         const unsigned grid = (unsigned)(rows < (int64_t)cus * 8 ? rows : (int64_t)cus * 8);
         if (chunks <= 1)
-            hipLaunchKernelGGL(quant_rowwise_kernel<1>, dim3(grid), dim3(kThreads), 0, hs, xb, qb,
+            hipLaunchKernelGGL((quant_rowwise_kernel<1, FMT>), dim3(grid), dim3(kThreads), 0, hs, xb, qb,
                                scale, rows, cols);
         else if (chunks <= 2)
-            hipLaunchKernelGGL(quant_rowwise_kernel<2>, dim3(grid), dim3(kThreads), 0, hs, xb, qb,
+            hipLaunchKernelGGL((quant_rowwise_kernel<2, FMT>), dim3(grid), dim3(kThreads), 0, hs, xb, qb,
                                scale, rows, cols);
         else if (chunks <= 4)
-            hipLaunchKernelGGL(quant_rowwise_kernel<4>, dim3(grid), dim3(kThreads), 0, hs, xb, qb,
+            hipLaunchKernelGGL((quant_rowwise_kernel<4, FMT>), dim3(grid), dim3(kThreads), 0, hs, xb, qb,
                                scale, rows, cols);
         else if (chunks <= 8)
-            hipLaunchKernelGGL(quant_rowwise_kernel<8>, dim3(grid), dim3(kThreads), 0, hs, xb, qb,
+            hipLaunchKernelGGL((quant_rowwise_kernel<8, FMT>), dim3(grid), dim3(kThreads), 0, hs, xb, qb,
                                scale, rows, cols);
         else
-            hipLaunchKernelGGL(quant_rowwise_kernel<0>, dim3(grid), dim3(kThreads), 0, hs, xb, qb,
+            hipLaunchKernelGGL((quant_rowwise_kernel<0, FMT>), dim3(grid), dim3(kThreads), 0, hs, xb, qb,
                                scale, rows, cols);
     } else {
         const int64_t groups = rows * cols / kGroup;
@@ -249,12 +269,26 @@ int fp8_quantize_e4m3(const void* x, void* q, float* scale, int64_t rows, int64_
         const unsigned grid = (unsigned)(want < (int64_t)cus * 8 ? want : (int64_t)cus * 8);
         hipLaunchKernelGGL(amax_zero_kernel, dim3(1), dim3(64), 0, hs, scale);
         hipLaunchKernelGGL(amax_kernel, dim3(grid), dim3(kThreads), 0, hs, xb, groups, scale);
-        hipLaunchKernelGGL(quant_tensor_kernel, dim3(grid), dim3(kThreads), 0, hs, xb, qb, groups,
+        hipLaunchKernelGGL(quant_tensor_kernel<FMT>, dim3(grid), dim3(kThreads), 0, hs, xb, qb, groups,
                            scale);
-        hipLaunchKernelGGL(amax_to_scale_kernel, dim3(1), dim3(64), 0, hs, scale);
+        hipLaunchKernelGGL(amax_to_scale_kernel<FMT>, dim3(1), dim3(64), 0, hs, scale);
     }
     if (hipGetLastError() != hipSuccess) return FP8Q_ERR_LAUNCH;
     return FP8Q_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fp8_quantize_e4m3(const void* x, void* q, float* scale, int64_t rows, int64_t cols,
+                      int scaling_mode, struct ihipStream_t* stream) {
+    return quantize_impl<0>(x, q, scale, rows, cols, scaling_mode, stream);
+}
+
+int fp8_quantize_e5m2(const void* x, void* q, float* scale, int64_t rows, int64_t cols,
+                      int scaling_mode, struct ihipStream_t* stream) {
+    return quantize_impl<1>(x, q, scale, rows, cols, scaling_mode, stream);
 }
 
 const char* fp8_quantize_status_string(int s) {

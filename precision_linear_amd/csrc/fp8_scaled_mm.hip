@@ -1,4 +1,4 @@
-// FP8 (e4m3fn) scaled matrix multiply for gfx950 (MI355X, CDNA4).
+// FP8 (e4m3fn / e5m2) scaled matrix multiply for gfx950 (MI355X, CDNA4): host logic and C ABI.
 //
 //   out[m][n] = bf16_rne( s[m][n] * sum_k A[m][k] * B[n][k] (+ bias[n]) )
 //
@@ -25,6 +25,9 @@
 //     then the bf16 tile goes through LDS so that the stores to the output
 //     write whole runs of its rows (16, 4 or 2 bytes per lane, as wide as the
 //     row alignment allows).
+//
+// The kernels and their launch wrappers are in fp8_gemm_kernels.h; each
+// operand format pair's instances come from fp8_gemm_f<k>.hip.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -33,1206 +36,9 @@
 #include <utility>
 
 #include "../../include/fp8_scaled_mm.h"
+#include "fp8_gemm_kernels.h"
 
 namespace {
-
-typedef int v4i __attribute__((ext_vector_type(4)));
-typedef int v8i __attribute__((ext_vector_type(8)));
-typedef float v4f __attribute__((ext_vector_type(4)));
-typedef float v16f __attribute__((ext_vector_type(16)));
-typedef __attribute__((address_space(3))) void lds_void_t;
-
-constexpr int kWave = 64;
-constexpr uint32_t kBufferWord3 = 0x00020000u;   // raw buffer, 32-bit data format (gfx9 family)
-constexpr uint32_t kOutOfRange = 0x80000000u;    // any offset >= num_records reads zero
-constexpr int kXcds = 8;                         // gfx950: 8 XCDs, round-robin dispatch
-
-struct Params {
-    const uint8_t* A;
-    const uint8_t* B;
-    const float* scale_a;
-    const float* scale_b;
-    const uint16_t* bias;  // may be null
-    uint16_t* out;
-    int M, N, K;
-    int tiles_m, tiles_n, num_tiles, k_iters;
-    int rowwise;
-    int vec_store;         // N % 4 == 0 and out 8-byte aligned
-    int vec16;             // N % 8 == 0 and out 16-byte aligned
-    int vec4;              // N % 2 == 0 and out 4-byte aligned
-    // Split-K: each output tile is computed by `splits` work units, unit s
-    // covering K slices [s*k_chunk, (s+1)*k_chunk).  With splits > 1 the fp32
-    // partial tiles go to `partials` and the unit that arrives last at the
-    // tile's counter adds them up in split order and runs the epilogue.
-    int splits, k_chunk;
-    float* partials;       // num_tiles * splits * BM * BN floats (splits > 1)
-    unsigned* counters;    // num_tiles arrival counters (splits > 1)
-};
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
-                                             (int)kBufferWord3);
-}
-
-// One 16-byte-per-lane buffer load that writes LDS directly: lane l's 16
-// bytes from rsrc + voff + soff land at LDS byte address lds + 16*l (lds is
-// wave-uniform and goes to M0).  Written as inline asm so that the compiler
-// does not treat later LDS reads as dependent on it: every wait on these loads
-// is an explicit vmcnt wait placed by the code that issues them.  NT marks the
-// load non-temporal (data read once: it should not displace reused lines from
-// the L2).
-template <bool NT = false>
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, const void* lds, uint32_t voff,
-                                      uint32_t soff) {
-    const uint32_t m0 = (uint32_t)(uintptr_t)lds;
-    if constexpr (NT)
-        asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen nt lds"
-                     :
-                     : "v"(voff), "s"(rsrc), "s"(soff), "{m0}"(m0)
-                     : "memory");
-    else
-        asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
-                     :
-                     : "v"(voff), "s"(rsrc), "s"(soff), "{m0}"(m0)
-                     : "memory");
-}
-
-// Position of 16-byte chunk c of LDS row r is c ^ chunk_swizzle(r).  The MFMA
-// operand reads have 8 (or 16) consecutive lanes read the same logical chunk
-// of 8 (16) consecutive rows; the mask makes those land in distinct banks
-// whether the LDS serves 128 or 256 bytes per cycle.  It uses row bits 0..3
-// only, so every 16-row-aligned block of rows shares one pattern.
-template <int CPR>
-__device__ __forceinline__ int chunk_swizzle(int r) {
-    if constexpr (CPR == 4) return ((r >> 1) ^ (r >> 2)) & 3;   // 4 rows per 256 B
-    if constexpr (CPR == 8) return (r & 7) ^ ((r >> 3) & 1);    // 2 rows per 256 B
-    return r & 15;                                              // >= 256-byte rows
-}
-
-template <int MI>
-struct Mfma;
-
-template <>
-struct Mfma<32> {
-    static constexpr int KSTEP = 64;      // bytes of K per instruction
-    typedef v16f acc_t;
-    static constexpr int NACC = 16;
-    __device__ static __forceinline__ acc_t run(v8i a, v8i b, acc_t c) {
-        return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
-    }
-};
-
-template <>
-struct Mfma<16> {
-    static constexpr int KSTEP = 128;
-    typedef v4f acc_t;
-    static constexpr int NACC = 4;
-    __device__ static __forceinline__ acc_t run(v8i a, v8i b, acc_t c) {
-        return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
-    }
-};
-
-__device__ __forceinline__ void tile_coords(int t, int tiles_m, int tiles_n, int group_m,
-                                            int& pm, int& pn) {
-    // Bands of group_m tile rows; inside a band, tiles go down the band's rows
-    // first, then across the columns.
-    const int band = group_m * tiles_n;
-    const int g = t / band;
-    const int first = g * group_m;
-    const int rows = min(tiles_m - first, group_m);
-    const int w = t - g * band;
-    pm = first + w % rows;
-    pn = w / rows;
-}
-
-template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int STAGES, int MI, int GROUP_M,
-          bool NT_B = false>
-struct Cfg {
-    // B is read by one tile row only (the grid has a single row of tiles):
-    // its loads are marked non-temporal so that they do not evict A, which
-    // every tile reads.
-    static constexpr bool STREAM_B = NT_B;
-    static constexpr int WAVES = WAVES_M * WAVES_N;
-    static constexpr int THREADS = WAVES * kWave;
-    static constexpr int WTM = BM / WAVES_M;     // wave tile rows (m)
-    static constexpr int WTN = BN / WAVES_N;     // wave tile cols (n)
-    static constexpr int FM = WTM / MI;
-    static constexpr int FN = WTN / MI;
-    static constexpr int CPR = BK / 16;          // 16-byte chunks per LDS row
-    static constexpr int A_BYTES = BM * BK;
-    static constexpr int B_BYTES = BN * BK;
-    static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
-    static constexpr int MAIN_BYTES = STAGES * STAGE_BYTES;
-    // Epilogue parameters of the current tile: BM row scales, BN column
-    // scales (fp32) and BN bias values (bf16).
-    static constexpr int EPI_BYTES = BM * 4 + BN * 4 + BN * 2;
-    static constexpr int LDS_BYTES = MAIN_BYTES + ((EPI_BYTES + 15) / 16) * 16;
-    static constexpr int NSA = (BM + THREADS - 1) / THREADS;   // staged per thread
-    static constexpr int NSB = (BN + THREADS - 1) / THREADS;
-    static constexpr int A_BLOCKS = A_BYTES / 1024;  // 1 KiB = one wave-wide 16-byte load
-    static constexpr int B_BLOCKS = B_BYTES / 1024;
-    // Loads per wave per stage.  When the blocks do not split evenly over the
-    // waves, the surplus loads repeat the last block: the same bytes land at
-    // the same LDS address twice, and every wave keeps the same load count
-    // (which the vmcnt arithmetic relies on).
-    static constexpr int A_LOADS = (A_BLOCKS + WAVES - 1) / WAVES;
-    static constexpr int B_LOADS = (B_BLOCKS + WAVES - 1) / WAVES;
-    static constexpr int LOADS = A_LOADS + B_LOADS;
-    static constexpr int KSTEP = Mfma<MI>::KSTEP;
-    static constexpr int NKS = BK / KSTEP;        // MFMA K steps per stage
-    static constexpr int MI_ = MI;
-    // Split-K keeps a second copy of the accumulators while it sums the
-    // partials, so it is compiled only where both fit in registers.
-    static constexpr int PER_LANE_ACC = FM * FN * (MI == 32 ? 16 : 4);
-    static constexpr bool SPLIT_OK = PER_LANE_ACC <= 64;
-    // Spread a stage's loads between MFMAs only where a K step has enough
-    // MFMAs to hide them (the big, MFMA-bound tiles).
-    static constexpr bool INTERLEAVE = MI == 32 && FM * FN >= 8;
-    static constexpr int BK_ = BK;
-    static constexpr int BM_ = BM;
-    static constexpr int BN_ = BN;
-    static constexpr int STAGES_ = STAGES;
-    // The epilogue stages the finished bf16 tile (rows of BN * 2 bytes, whole
-    // 16-byte chunks) in the stage buffers.
-    static constexpr int STG_CHUNKS = BN * 2 / 16;
-    static_assert(WTM % MI == 0 && WTN % MI == 0, "wave tile must hold whole MFMA tiles");
-    static_assert(MI % 16 == 0, "fragment row blocks must be 16-row aligned for the swizzle");
-    static_assert(BK % KSTEP == 0, "BK must be a multiple of the MFMA K step");
-    static_assert(CPR == 4 || CPR == 8 || CPR == 16 || CPR == 32, "BK must be 64..512");
-    static_assert(A_BYTES % 1024 == 0 && B_BYTES % 1024 == 0, "stages are whole 1 KiB blocks");
-    static_assert(LDS_BYTES <= 160 * 1024, "gfx950 LDS is 160 KiB per workgroup");
-    static_assert(STAGES >= 2, "at least double buffering");
-    static_assert(BN % 8 == 0 && BM * BN * 2 <= MAIN_BYTES, "the output tile fits the stage buffers");
-    static_assert(LOADS * (STAGES - 1) <= 63, "vmcnt counts up to 63");
-};
-
-// Issue the direct-to-LDS loads of one K slice (k0) for this wave.
-template <class C>
-__device__ __forceinline__ void load_stage(uint8_t* lds_stage, __amdgpu_buffer_rsrc_t ra,
-                                           __amdgpu_buffer_rsrc_t rb, int ld, int klim, int k0,
-                                           int wave, int lane) {
-    constexpr int RPB = 1024 / (C::CPR * 16);    // LDS rows per 1 KiB block
-    // The lane-dependent offsets are cheap to recompute; keeping them live
-    // across the K loop would only cost registers the MFMA pipeline needs.
-    int l = lane;
-    asm volatile("" : "+v"(l));
-    const int rr = l / C::CPR;
-    const int pos = l % C::CPR;
-#pragma unroll
-    for (int i = 0; i < C::A_LOADS; ++i) {
-        const int blk = min(wave + i * C::WAVES, C::A_BLOCKS - 1);
-        const int r = blk * RPB + rr;
-        const int c = pos ^ chunk_swizzle<C::CPR>(r);
-        const int k = k0 + c * 16;
-        const uint32_t off = k < klim ? (uint32_t)(r * ld + k) : kOutOfRange;
-        dma16(ra, lds_stage + blk * 1024, off, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < C::B_LOADS; ++i) {
-        const int blk = min(wave + i * C::WAVES, C::B_BLOCKS - 1);
-        const int r = blk * RPB + rr;
-        const int c = pos ^ chunk_swizzle<C::CPR>(r);
-        const int k = k0 + c * 16;
-        const uint32_t off = k < klim ? (uint32_t)(r * ld + k) : kOutOfRange;
-        dma16<C::STREAM_B>(rb, lds_stage + C::A_BYTES + blk * 1024, off, 0);
-    }
-}
-
-// Load number `idx` (0 <= idx < LOADS) of this wave for one K slice: the
-// first A_LOADS go to the A tile, the rest to the B tile.  With live == false
-// every lane reads out of range (zeros land in a buffer nobody reads again);
-// this keeps the number of loads per stage fixed, which the vmcnt waits use.
-template <class C, int idx>
-__device__ __forceinline__ void load_one(uint8_t* lds_stage, __amdgpu_buffer_rsrc_t ra,
-                                         __amdgpu_buffer_rsrc_t rb, int ld, int klim, int k0,
-                                         int wave, int l, bool live) {
-    constexpr int RPB = 1024 / (C::CPR * 16);
-    constexpr bool IS_A = idx < C::A_LOADS;
-    constexpr int i = IS_A ? idx : idx - C::A_LOADS;
-    const int blk = min(wave + i * C::WAVES, (IS_A ? C::A_BLOCKS : C::B_BLOCKS) - 1);
-    const int rr = l / C::CPR;
-    const int pos = l % C::CPR;
-    const int r = blk * RPB + rr;
-    const int c = pos ^ chunk_swizzle<C::CPR>(r);
-    const int k = k0 + c * 16;
-    const uint32_t off = (live && k < klim) ? (uint32_t)(r * ld + k) : kOutOfRange;
-    if constexpr (IS_A)
-        dma16(ra, lds_stage + blk * 1024, off, 0);
-    else
-        dma16<C::STREAM_B>(rb, lds_stage + C::A_BYTES + blk * 1024, off, 0);
-}
-
-template <class C, int LO, int HI>
-__device__ __forceinline__ void load_range(uint8_t* lds_stage, __amdgpu_buffer_rsrc_t ra,
-                                           __amdgpu_buffer_rsrc_t rb, int ld, int klim, int k0,
-                                           int wave, int l, bool live) {
-    if constexpr (LO < HI) {
-        load_one<C, LO>(lds_stage, ra, rb, ld, klim, k0, wave, l, live);
-        load_range<C, LO + 1, HI>(lds_stage, ra, rb, ld, klim, k0, wave, l, live);
-    }
-}
-
-template <class C, int Q>
-__device__ __forceinline__ void mfma_with_loads(typename Mfma<C::MI_>::acc_t (&acc)[C::FN][C::FM],
-                                                const v8i (&fa)[C::FM], const v8i (&fb)[C::FN],
-                                                uint8_t* lds_stage, __amdgpu_buffer_rsrc_t ra,
-                                                __amdgpu_buffer_rsrc_t rb, int ld, int klim, int k0,
-                                                int wave, int l, bool live) {
-    constexpr int NQ = C::FN * C::FM;
-    if constexpr (Q < NQ) {
-        constexpr int i = Q / C::FM, j = Q % C::FM;
-        acc[i][j] = Mfma<C::MI_>::run(fb[i], fa[j], acc[i][j]);
-        // the share of loads issued after MFMA Q of NQ
-        load_range<C, Q * C::LOADS / NQ, (Q + 1) * C::LOADS / NQ>(lds_stage, ra, rb, ld, klim, k0,
-                                                                  wave, l, live);
-        __builtin_amdgcn_sched_barrier(0);
-        mfma_with_loads<C, Q + 1>(acc, fa, fb, lds_stage, ra, rb, ld, klim, k0, wave, l, live);
-    }
-}
-
-// 32 operand bytes for one MFMA: row base + l of an LDS operand tile
-// (base a multiple of 16, so the swizzle depends on l only), logical chunks c0
-// and c0+1.
-template <int CPR>
-__device__ __forceinline__ v8i read_frag(const uint8_t* tile, int base, int l, int c0) {
-    const int sw = chunk_swizzle<CPR>(l);
-    const uint8_t* row = tile + (base + l) * (CPR * 16);
-    v4i lo = *reinterpret_cast<const v4i*>(row + ((c0 ^ sw) << 4));
-    v4i hi = *reinterpret_cast<const v4i*>(row + (((c0 + 1) ^ sw) << 4));
-    v8i f;
-    f[0] = lo[0]; f[1] = lo[1]; f[2] = lo[2]; f[3] = lo[3];
-    f[4] = hi[0]; f[5] = hi[1]; f[6] = hi[2]; f[7] = hi[3];
-    return f;
-}
-
-// Workgroup barrier without the memory-model fence of __syncthreads(): the
-// waits it needs (LDS reads done, own LDS-DMA loads landed) are explicit.
-__device__ __forceinline__ void barrier_lds() {
-    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0), vmcnt/expcnt untouched
-    __builtin_amdgcn_s_barrier();
-}
-
-// Operand fragments of K step `ks` of one stage for this wave: FM row blocks
-// of A and FN row blocks of B.  Lanes 0..MI-1 take rows, the lane group
-// (lane / MI) takes chunk pair 2*(lane/MI) of the step (for MI=32 lanes
-// 32..63 take chunks 2,3; for MI=16 four lane groups take pairs 0..3).  A and
-// B use the same lane -> k assignment, which is all the MFMA contraction needs.
-template <class C>
-__device__ __forceinline__ void read_frags(v8i (&fa)[C::FM], v8i (&fb)[C::FN], const uint8_t* st,
-                                           int ks, int wm, int wn, int lane) {
-    constexpr int MI = C::MI_;
-    const int c0 = ks * (C::KSTEP / 16) + (lane / MI) * 2;
-    const int l = lane % MI;
-#pragma unroll
-    for (int j = 0; j < C::FM; ++j)
-        fa[j] = read_frag<C::CPR>(st, wm * C::WTM + j * MI, l, c0);
-#pragma unroll
-    for (int i = 0; i < C::FN; ++i)
-        fb[i] = read_frag<C::CPR>(st + C::A_BYTES, wn * C::WTN + i * MI, l, c0);
-}
-
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    // s_waitcnt encoding on gfx9: vmcnt low bits [3:0], high bits [15:14];
-    // expcnt [6:4] and lgkmcnt [11:8] left at their maxima (no wait).
-    static_assert(N >= 0 && N <= 63, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
-
-// Two fp32 -> bf16 conversions, round to nearest even, packed low | high << 16
-// (one v_cvt_pk_bf16_f32; fp32 denormals are kept, so the bf16 denormal range
-// rounds like the rest).
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    typedef float f2 __attribute__((ext_vector_type(2)));
-    typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{lo, hi}, bf2));
-}
-
-// Epilogue of one wave's FM x FN blocks of MI x MI outputs, whose top-left
-// corner is (row0 + mbase, col0 + nbase).  The MFMA was fed B as its first
-// operand, so lane l holds output row m = l % MI of each block and runs of 4
-// consecutive columns n.  Row-wise scales and bias come from the LDS copies of
-// the tile's parameters (indexed from the tile's corner).  y = acc * s, or
-// fma(acc, s, bias) with a bias, with s = sa * sb formed in fp32; then RNE.
-// RW, BIAS and FULL (the wave's block lies inside the output and 8-byte stores
-// are allowed) are compile-time, so the block has no branches; all parameters
-// are read from LDS before the first use.
-template <int MI, int FM, int FN, bool RW, bool BIAS, bool FULL>
-__device__ __forceinline__ void store_tile_impl(const typename Mfma<MI>::acc_t (&acc)[FN][FM],
-                                                const Params& p, int row0, int col0, int mbase,
-                                                int nbase, const float* epi_sa,
-                                                const float* epi_sb, const uint16_t* epi_bias,
-                                                float s_pt, int lane) {
-    constexpr int G = Mfma<MI>::NACC / 4;   // runs of 4 columns per block and lane
-    auto col = [&](int i, int g) {
-        return nbase + i * MI + (MI == 32 ? 8 * g + 4 * (lane / 32) : 4 * (lane / 16));
-    };
-    float sa_r[FM];
-    v4f sb_r[FN][G];
-    uint2 b_r[FN][G];
-#pragma unroll
-    for (int j = 0; j < FM; ++j) sa_r[j] = RW ? epi_sa[mbase + j * MI + lane % MI] : s_pt;
-#pragma unroll
-    for (int i = 0; i < FN; ++i)
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-            if constexpr (RW) sb_r[i][g] = *reinterpret_cast<const v4f*>(epi_sb + col(i, g));
-            if constexpr (BIAS) b_r[i][g] = *reinterpret_cast<const uint2*>(epi_bias + col(i, g));
-        }
-#pragma unroll
-    for (int j = 0; j < FM; ++j) {
-        const int ml = mbase + j * MI + lane % MI;
-        const int m = row0 + ml;
-        if (!FULL && m >= p.M) continue;
-        uint16_t* orow = p.out + (size_t)m * p.N + col0;
-#pragma unroll
-        for (int i = 0; i < FN; ++i)
-#pragma unroll
-            for (int g = 0; g < G; ++g) {
-                const int nl = col(i, g);
-                if (!FULL && col0 + nl >= p.N) continue;
-                float y[4];
-#pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    const float sc = RW ? sa_r[j] * sb_r[i][g][c] : s_pt;
-                    const float v = acc[i][j][4 * g + c];
-                    if constexpr (BIAS) {
-                        const uint32_t bw = c < 2 ? b_r[i][g].x : b_r[i][g].y;
-                        const float bv = __uint_as_float(c % 2 == 0 ? bw << 16 : bw & 0xffff0000u);
-                        y[c] = __builtin_fmaf(v, sc, bv);
-                    } else {
-                        y[c] = v * sc;
-                    }
-                }
-                const uint32_t lo = pack_bf16x2(y[0], y[1]);
-                const uint32_t hi = pack_bf16x2(y[2], y[3]);
-                if (FULL || (p.vec_store && col0 + nl + 3 < p.N)) {
-                    uint2 w;
-                    w.x = lo;
-                    w.y = hi;
-                    *reinterpret_cast<uint2*>(orow + nl) = w;
-                } else {
-                    const uint16_t h[4] = {(uint16_t)lo, (uint16_t)(lo >> 16), (uint16_t)hi,
-                                           (uint16_t)(hi >> 16)};
-#pragma unroll
-                    for (int c = 0; c < 4; ++c)
-                        if (col0 + nl + c < p.N) orow[nl + c] = h[c];
-                }
-            }
-    }
-}
-
-template <int MI, int FM, int FN>
-__device__ __forceinline__ void store_tile(const typename Mfma<MI>::acc_t (&acc)[FN][FM],
-                                           const Params& p, int row0, int col0, int mbase,
-                                           int nbase, const float* epi_sa, const float* epi_sb,
-                                           const uint16_t* epi_bias, float s_pt, bool has_bias,
-                                           int lane) {
-    // Derive every epilogue address from an opaque copy of the lane id, so the
-    // compiler cannot hoist them out of the tile loop and keep them live (in
-    // registers the K loop needs) across it.
-    asm volatile("" : "+v"(lane));
-    const bool full = p.vec_store && row0 + mbase + FM * MI <= p.M &&
-                      col0 + nbase + FN * MI <= p.N;   // wave-uniform
-#define FP8MM_EPI(RW, BIAS, FULL)                                                               \
-    store_tile_impl<MI, FM, FN, RW, BIAS, FULL>(acc, p, row0, col0, mbase, nbase, epi_sa, epi_sb, \
-                                                epi_bias, s_pt, lane)
-    if (full) {
-        if (p.rowwise) {
-            if (has_bias) FP8MM_EPI(true, true, true); else FP8MM_EPI(true, false, true);
-        } else {
-            if (has_bias) FP8MM_EPI(false, true, true); else FP8MM_EPI(false, false, true);
-        }
-    } else {
-        if (p.rowwise) {
-            if (has_bias) FP8MM_EPI(true, true, false); else FP8MM_EPI(true, false, false);
-        } else {
-            if (has_bias) FP8MM_EPI(false, true, false); else FP8MM_EPI(false, false, false);
-        }
-    }
-#undef FP8MM_EPI
-}
-
-// Staged epilogue of the generic kernel, first half: each wave converts its
-// FM x FN blocks (y = acc * s, or fma(acc, s, bias); RNE to bf16) and writes
-// them into a row-major copy of the whole BM x BN tile in LDS.  Row r of that
-// copy has STG_CHUNKS 16-byte chunks; chunk c sits at position (c + r) mod
-// STG_CHUNKS, so the lanes of one MFMA block, which hold one column run each
-// of consecutive rows, write to different banks.  Rows and columns outside
-// the output are converted too (from zero accumulators) and never stored.
-template <class C, bool RW, bool BIAS>
-__device__ __forceinline__ void stage_tile_impl(
-    const typename Mfma<C::MI_>::acc_t (&acc)[C::FN][C::FM], uint8_t* stg, int mbase, int nbase,
-    const float* epi_sa, const float* epi_sb, const uint16_t* epi_bias, float s_pt, int lane) {
-    constexpr int MI = C::MI_;
-    constexpr int G = Mfma<MI>::NACC / 4;
-    constexpr int NCH = C::STG_CHUNKS;
-    float sa_r[C::FM];
-#pragma unroll
-    for (int j = 0; j < C::FM; ++j) sa_r[j] = RW ? epi_sa[mbase + j * MI + lane % MI] : s_pt;
-    // Column runs outermost: each run's scales and bias are read once and
-    // stay live only while its FM row blocks are written.
-#pragma unroll
-    for (int i = 0; i < C::FN; ++i)
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-            const int nl = nbase + i * MI + (MI == 32 ? 8 * g + 4 * (lane / 32) : 4 * (lane / 16));
-            v4f sb_r;
-            uint2 b_r;
-            if constexpr (RW) sb_r = *reinterpret_cast<const v4f*>(epi_sb + nl);
-            if constexpr (BIAS) b_r = *reinterpret_cast<const uint2*>(epi_bias + nl);
-            const int byte = nl * 2;   // a multiple of 8: one half of a chunk
-#pragma unroll
-            for (int j = 0; j < C::FM; ++j) {
-                const int ml = mbase + j * MI + lane % MI;
-                float y[4];
-#pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    const float sc = RW ? sa_r[j] * sb_r[c] : s_pt;
-                    const float v = acc[i][j][4 * g + c];
-                    if constexpr (BIAS) {
-                        const uint32_t bw = c < 2 ? b_r.x : b_r.y;
-                        const float bv = __uint_as_float(c % 2 == 0 ? bw << 16 : bw & 0xffff0000u);
-                        y[c] = __builtin_fmaf(v, sc, bv);
-                    } else {
-                        y[c] = v * sc;
-                    }
-                }
-                uint2 w;
-                w.x = pack_bf16x2(y[0], y[1]);
-                w.y = pack_bf16x2(y[2], y[3]);
-                *reinterpret_cast<uint2*>(stg + ml * (NCH * 16) + (((byte >> 4) + ml) % NCH) * 16 +
-                                          (byte & 15)) = w;
-            }
-        }
-}
-
-// Second half: the workgroup stores the staged tile row by row, consecutive
-// lanes on consecutive W-byte pieces of a row, so each store instruction
-// writes whole runs of a row instead of a few bytes of many rows.  W is the
-// widest piece every row start allows: 16 (N % 8 == 0, out 16-byte aligned),
-// 4 (N even, out 4-byte aligned) or 2.  Only rows and columns inside the
-// output are written.
-template <class C, int W>
-__device__ __forceinline__ void store_staged(const uint8_t* stg, const Params& p, int row0, int col0,
-                                             int tid) {
-    constexpr int NCH = C::STG_CHUNKS;
-    constexpr int CW = C::BN_ * 2 / W;               // pieces per row
-    constexpr int TOTAL = C::BM_ * CW;
-    constexpr int ITERS = (TOTAL + C::THREADS - 1) / C::THREADS;
-    const int rows = min(C::BM_, p.M - row0);
-    const int pieces = min(CW, (p.N - col0) * 2 / W);   // W divides 2 * N here
-#pragma unroll 4
-    for (int it = 0; it < ITERS; ++it) {
-        const int q = tid + it * C::THREADS;
-        const int r = q / CW;
-        const int cw = q - r * CW;
-        if (q >= TOTAL || r >= rows || cw >= pieces) continue;
-        const int byte = cw * W;
-        const uint8_t* src = stg + r * (NCH * 16) + (((byte >> 4) + r) % NCH) * 16 + (byte & 15);
-        uint16_t* dst = p.out + (size_t)(row0 + r) * p.N + col0 + byte / 2;
-        if constexpr (W == 16)
-            *reinterpret_cast<v4i*>(dst) = *reinterpret_cast<const v4i*>(src);
-        else if constexpr (W == 4)
-            *reinterpret_cast<uint32_t*>(dst) = *reinterpret_cast<const uint32_t*>(src);
-        else
-            *dst = *reinterpret_cast<const uint16_t*>(src);
-    }
-}
-
-template <class C>
-__device__ __forceinline__ void stage_and_store(
-    const typename Mfma<C::MI_>::acc_t (&acc)[C::FN][C::FM], uint8_t* stg, const Params& p,
-    int row0, int col0, int mbase, int nbase, const float* epi_sa, const float* epi_sb,
-    const uint16_t* epi_bias, float s_pt, bool has_bias, int lane, int tid) {
-    // As in store_tile: opaque lane id, so the addresses are not kept live
-    // across the K loop.
-    asm volatile("" : "+v"(lane));
-    if (p.rowwise) {
-        if (has_bias)
-            stage_tile_impl<C, true, true>(acc, stg, mbase, nbase, epi_sa, epi_sb, epi_bias, s_pt, lane);
-        else
-            stage_tile_impl<C, true, false>(acc, stg, mbase, nbase, epi_sa, epi_sb, epi_bias, s_pt, lane);
-    } else {
-        if (has_bias)
-            stage_tile_impl<C, false, true>(acc, stg, mbase, nbase, epi_sa, epi_sb, epi_bias, s_pt, lane);
-        else
-            stage_tile_impl<C, false, false>(acc, stg, mbase, nbase, epi_sa, epi_sb, epi_bias, s_pt, lane);
-    }
-    barrier_lds();
-    if (p.vec16)
-        store_staged<C, 16>(stg, p, row0, col0, tid);
-    else if (p.vec4)
-        store_staged<C, 4>(stg, p, row0, col0, tid);
-    else
-        store_staged<C, 2>(stg, p, row0, col0, tid);
-}
-
-// One K stage (BK bytes of K) of the software pipeline.  The fragments of
-// the stage's first K step are already in buffer CUR0.  Each step first
-// issues the LDS reads of the next step into the other buffer, then the MFMAs
-// of this step.  At the last step, if another stage follows (HAS_NEXT), the
-// wave waits for its own loads of that stage, joins the barrier (after which
-// every wave's reads of this stage are done and every wave's loads of the next
-// stage have landed), refills this stage's buffer with the slice STAGES ahead,
-// and reads the next stage's first fragments.
-template <class C, int CUR0, bool HAS_NEXT>
-__device__ __forceinline__ void run_stage(typename Mfma<C::MI_>::acc_t (&acc)[C::FN][C::FM],
-                                          v8i (&fa)[2][C::FM], v8i (&fb)[2][C::FN], uint8_t* smem,
-                                          int kt, int k_iters, __amdgpu_buffer_rsrc_t ra,
-                                          __amdgpu_buffer_rsrc_t rb, int ld, int klim, int wave,
-                                          int wm, int wn, int lane) {
-    using F = Mfma<C::MI_>;
-    constexpr int S = C::STAGES_;
-    const uint8_t* st = smem + (kt % S) * C::STAGE_BYTES;
-#pragma unroll
-    for (int ks = 0; ks < C::NKS; ++ks) {
-        const int cur = (CUR0 + ks) & 1;
-        if (ks + 1 < C::NKS) {
-            read_frags<C>(fa[cur ^ 1], fb[cur ^ 1], st, ks + 1, wm, wn, lane);
-        } else if (HAS_NEXT) {
-            if constexpr (C::INTERLEAVE) {
-                // Every earlier stage issued exactly LOADS loads per wave (dead
-                // ones read out of range), so slice kt+1 has landed once the
-                // S-2 newest slices' loads remain.
-                wait_vmcnt<C::LOADS * (S - 2)>();
-                barrier_lds();
-                // The buffer just released is refilled with slice kt+S.
-                // MFMA-bound tiles: the loads are spread between this step's
-                // MFMAs; issued as one burst they stall the wave in the memory
-                // pipeline's queue while the MFMA unit idles.
-                read_frags<C>(fa[cur ^ 1], fb[cur ^ 1], smem + ((kt + 1) % S) * C::STAGE_BYTES, 0,
-                              wm, wn, lane);
-                __builtin_amdgcn_sched_barrier(0);
-                int l = lane;
-                asm volatile("" : "+v"(l));
-                mfma_with_loads<C, 0>(acc, fa[cur], fb[cur], smem + (kt % S) * C::STAGE_BYTES, ra,
-                                      rb, ld, klim, (kt + S) * C::BK_, wave, l, kt + S < k_iters);
-                continue;
-            } else {
-                // Memory-bound tiles: the loads go out first, as early as
-                // possible, and only for slices that exist.  Loads issued so
-                // far cover slices up to min(kt+S-1, k_iters-1) (the prologue
-                // may add dead ones past the end); slice kt+1 has landed once
-                // the S-2 newest slices remain, near the end once none do.
-                if (kt + S - 1 < k_iters) wait_vmcnt<C::LOADS * (S - 2)>();
-                else wait_vmcnt<0>();
-                barrier_lds();
-                if (kt + S < k_iters)
-                    load_stage<C>(smem + (kt % S) * C::STAGE_BYTES, ra, rb, ld, klim,
-                                  (kt + S) * C::BK_, wave, lane);
-                read_frags<C>(fa[cur ^ 1], fb[cur ^ 1], smem + ((kt + 1) % S) * C::STAGE_BYTES, 0,
-                              wm, wn, lane);
-            }
-        }
-        // Keep the compiler from sinking the LDS reads below the MFMAs: they
-        // must be in flight while the MFMAs of this step run.
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int i = 0; i < C::FN; ++i)
-#pragma unroll
-            for (int j = 0; j < C::FM; ++j) acc[i][j] = F::run(fb[cur][i], fa[cur][j], acc[i][j]);
-        __builtin_amdgcn_sched_barrier(0);
-    }
-}
-
-template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int STAGES, int MI, int GROUP_M,
-          bool NT_B>
-__global__ void __launch_bounds__(WAVES_M * WAVES_N * kWave)
-fp8_gemm_kernel(Params p) {
-    using C = Cfg<BM, BN, BK, WAVES_M, WAVES_N, STAGES, MI, GROUP_M, NT_B>;
-    using F = Mfma<MI>;
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS_BYTES];
-
-    const int tid = threadIdx.x;
-    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-    const int lane = tid % kWave;
-    const int wm = wave / WAVES_N;
-    const int wn = wave % WAVES_N;
-
-    // Renumber workgroups so that the ones on one XCD get consecutive ids.
-    const int G = gridDim.x;
-    int wg = blockIdx.x;
-    if (G % kXcds == 0) wg = (blockIdx.x % kXcds) * (G / kXcds) + blockIdx.x / kXcds;
-
-    const float s_pt = p.rowwise ? 0.f : p.scale_a[0] * p.scale_b[0];
-    float* epi_sa = reinterpret_cast<float*>(smem + C::MAIN_BYTES);
-    float* epi_sb = epi_sa + BM;
-    uint16_t* epi_bias = reinterpret_cast<uint16_t*>(epi_sb + BN);
-    const bool has_bias = p.bias != nullptr;
-
-    __shared__ unsigned arrival;
-    const int num_units = p.num_tiles * p.splits;
-    for (int u = wg; u < num_units; u += G) {
-        const int t = u / p.splits;             // the splits of a tile are neighbours
-        const int split = u - t * p.splits;
-        int pm, pn;
-        tile_coords(t, p.tiles_m, p.tiles_n, GROUP_M, pm, pn);
-        const int row0 = pm * BM;
-        const int col0 = pn * BN;
-        // This unit's K range, as whole BK slices; the buffer resources start at
-        // its first byte so the stage code sees a K range beginning at 0.
-        const int kb = split * p.k_chunk;
-        const int k_iters = max(0, min(p.k_chunk, p.k_iters - kb));
-        const int kskip = kb * BK;
-        const int klim = p.K - kskip;
-        const uint32_t rows_a = (uint32_t)min(BM, p.M - row0);
-        const uint32_t rows_b = (uint32_t)min(BN, p.N - col0);
-        const __amdgpu_buffer_rsrc_t ra =
-            make_rsrc(p.A + (size_t)row0 * p.K + kskip, rows_a * (uint32_t)p.K - (uint32_t)kskip);
-        const __amdgpu_buffer_rsrc_t rb =
-            make_rsrc(p.B + (size_t)col0 * p.K + kskip, rows_b * (uint32_t)p.K - (uint32_t)kskip);
-
-        // Every wave must be done with the LDS of the previous tile before
-        // this tile's loads start.  The previous tile's output stores may
-        // still be in flight: vector memory operations are counted together,
-        // and loads return in order among themselves, so a wait for "at most
-        // n outstanding" still covers every load older than the last n; the
-        // stores only make the first wait of the tile longer.
-        barrier_lds();
-
-        // This tile's scales and bias, fetched now into registers and moved to
-        // LDS after the K loop (their latency hides under the loop).
-        float sa_v[C::NSA], sb_v[C::NSB];
-        uint16_t bias_v[C::NSB];
-#pragma unroll
-        for (int i = 0; i < C::NSA; ++i) {
-            const int r = tid + i * C::THREADS;
-            sa_v[i] = (p.rowwise && r < BM && row0 + r < p.M) ? p.scale_a[row0 + r] : 0.f;
-        }
-#pragma unroll
-        for (int i = 0; i < C::NSB; ++i) {
-            const int c = tid + i * C::THREADS;
-            const bool ok = c < BN && col0 + c < p.N;
-            sb_v[i] = (p.rowwise && ok) ? p.scale_b[col0 + c] : 0.f;
-            bias_v[i] = (has_bias && ok) ? p.bias[col0 + c] : (uint16_t)0;
-        }
-
-        typename F::acc_t acc[C::FN][C::FM];
-#pragma unroll
-        for (int i = 0; i < C::FN; ++i)
-#pragma unroll
-            for (int j = 0; j < C::FM; ++j)
-#pragma unroll
-                for (int v = 0; v < F::NACC; ++v) acc[i][j][v] = 0.f;
-
-        // Fill every stage buffer; the buffer of stage kt is refilled with
-        // slice kt + STAGES once stage kt has been read.
-#pragma unroll
-        for (int s = 0; s < STAGES; ++s)
-            load_stage<C>(smem + s * C::STAGE_BYTES, ra, rb, p.K, s < k_iters ? klim : 0, s * BK,
-                          wave, lane);
-
-        // Software pipeline over K steps: the operand fragments of step q+1 are
-        // read from LDS while the MFMAs of step q run.  At the last step of a
-        // stage the wave first makes the next stage visible (own loads landed,
-        // barrier), recycles the stage it has just finished reading for the
-        // loads STAGES slices ahead, and reads the next stage's first fragments;
-        // the barrier therefore sits under the tail of the previous MFMAs.
-        v8i fa[2][C::FM], fb[2][C::FN];
-        wait_vmcnt<C::LOADS * (STAGES - 1)>();   // stage 0 landed (S-1 newer slices may not)
-        barrier_lds();
-        if (k_iters > 0) read_frags<C>(fa[0], fb[0], smem, 0, wm, wn, lane);
-
-        // Every stage but the last hands over to the next one; the fragment
-        // parity of each stage is a compile-time constant.
-        int kt = 0;
-        if (k_iters > 0) {
-            if constexpr (C::NKS % 2 == 0) {
-                for (; kt + 1 < k_iters; ++kt)
-                    run_stage<C, 0, true>(acc, fa, fb, smem, kt, k_iters, ra, rb, p.K, klim, wave, wm,
-                                          wn, lane);
-                run_stage<C, 0, false>(acc, fa, fb, smem, kt, k_iters, ra, rb, p.K, klim, wave, wm, wn,
-                                       lane);
-            } else {
-                for (; kt + 2 < k_iters; kt += 2) {
-                    run_stage<C, 0, true>(acc, fa, fb, smem, kt, k_iters, ra, rb, p.K, klim, wave, wm,
-                                          wn, lane);
-                    run_stage<C, 1, true>(acc, fa, fb, smem, kt + 1, k_iters, ra, rb, p.K, klim, wave,
-                                          wm, wn, lane);
-                }
-                if (kt + 1 < k_iters) {
-                    run_stage<C, 0, true>(acc, fa, fb, smem, kt, k_iters, ra, rb, p.K, klim, wave, wm,
-                                          wn, lane);
-                    run_stage<C, 1, false>(acc, fa, fb, smem, kt + 1, k_iters, ra, rb, p.K, klim, wave,
-                                           wm, wn, lane);
-                } else {
-                    run_stage<C, 0, false>(acc, fa, fb, smem, kt, k_iters, ra, rb, p.K, klim, wave, wm,
-                                           wn, lane);
-                }
-            }
-        }
-
-        if constexpr (C::SPLIT_OK) if (p.splits > 1) {
-            // Publish this unit's partial tile (lane-major, so each store and
-            // load below is a 256-byte run per wave) and count the arrival.
-            // Partials travel with agent-coherent stores and loads (written
-            // through the XCD's L2, read past it), so a unit on one XCD sees
-            // another XCD's partials without writing back or invalidating
-            // whole L2s; the stores have completed (vmcnt 0) before the
-            // arrival is counted.
-            float* mine = p.partials + (size_t)u * (BM * BN);
-#pragma unroll
-            for (int i = 0; i < C::FN; ++i)
-#pragma unroll
-                for (int j = 0; j < C::FM; ++j)
-#pragma unroll
-                    for (int v = 0; v < F::NACC; ++v)
-                        __hip_atomic_store(mine + ((i * C::FM + j) * F::NACC + v) * C::THREADS + tid,
-                                           acc[i][j][v], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            wait_vmcnt<0>();
-            __syncthreads();
-            if (tid == 0)
-                arrival = __hip_atomic_fetch_add(&p.counters[t], 1u, __ATOMIC_RELAXED,
-                                                 __HIP_MEMORY_SCOPE_AGENT);
-            __syncthreads();
-            // Only the last of the tile's units goes on; it adds the partials in
-            // split order (deterministic whatever the arrival order).
-            if (arrival != (unsigned)(p.splits - 1)) continue;
-            if (tid == 0)
-                __hip_atomic_store(&p.counters[t], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            typename F::acc_t sum[C::FN][C::FM];
-#pragma unroll
-            for (int i = 0; i < C::FN; ++i)
-#pragma unroll
-                for (int j = 0; j < C::FM; ++j)
-#pragma unroll
-                    for (int v = 0; v < F::NACC; ++v) sum[i][j][v] = 0.f;
-            const float* tile_parts = p.partials + (size_t)t * p.splits * (BM * BN);
-            for (int q = 0; q < p.splits; ++q) {
-                const float* part = tile_parts + (size_t)q * (BM * BN);
-#pragma unroll
-                for (int i = 0; i < C::FN; ++i)
-#pragma unroll
-                    for (int j = 0; j < C::FM; ++j)
-#pragma unroll
-                        for (int v = 0; v < F::NACC; ++v) {
-                            const float x =
-                                q == split
-                                    ? acc[i][j][v]
-                                    : __hip_atomic_load(
-                                          part + ((i * C::FM + j) * F::NACC + v) * C::THREADS + tid,
-                                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                            sum[i][j][v] += x;
-                        }
-            }
-#pragma unroll
-            for (int i = 0; i < C::FN; ++i)
-#pragma unroll
-                for (int j = 0; j < C::FM; ++j) acc[i][j] = sum[i][j];
-        }
-
-        // Epilogue parameters into LDS (beside the stage buffers).
-        if (p.rowwise || has_bias) {
-#pragma unroll
-            for (int i = 0; i < C::NSA; ++i) {
-                const int r = tid + i * C::THREADS;
-                if (r < BM) epi_sa[r] = sa_v[i];
-            }
-#pragma unroll
-            for (int i = 0; i < C::NSB; ++i) {
-                const int c = tid + i * C::THREADS;
-                if (c < BN) {
-                    epi_sb[c] = sb_v[i];
-                    epi_bias[c] = bias_v[i];
-                }
-            }
-        }
-        // The output tile is staged in the stage buffers: every wave must be
-        // done reading the last stage, and every load (including the trailing
-        // ones of slices past the end) must have landed.
-        wait_vmcnt<0>();
-        barrier_lds();
-        stage_and_store<C>(acc, smem, p, row0, col0, wm * C::WTM, wn * C::WTN, epi_sa, epi_sb,
-                           epi_bias, s_pt, has_bias, lane, tid);
-    }
-}
-
-// ------------------------------------------------------ ping-pong kernel ---
-//
-// 256 x 256 output tiles, K slices of 128 bytes, 8 waves in two groups of four
-// with one wave of each group on every SIMD (waves w and w+4 share SIMD w).
-// Group 1 runs one phase behind group 0, so on every SIMD one wave issues the
-// 16 MFMAs of a K slice from registers while the other reads its fragments of
-// that slice from LDS and issues global -> LDS loads; at the end of each phase a
-// workgroup barrier swaps the roles.  Wave (g, q) computes rows g*128 .. +128
-// and columns q*64 .. +64 of the tile with fp32 accumulators in registers.
-//
-// Two LDS stage buffers, slice s in buffer s % 2, each holding the slice's A
-// rows 0-127 ("A-top", read only by group 0), A rows 128-255 ("A-bottom", read
-// only by group 1) and B (read by both).  Group 0 reads slice s in phase 2s,
-// group 1 in phase 2s+1.  The loads are issued in memory phases only, 8 per wave
-// per phase:
-//   phase 2s   (group 0): B of slice s+1        (its buffer was last read in 2s-1)
-//   phase 2s+1 (group 1): A-bottom of slice s+1 (last read in 2s-1) and A-top of
-//                         slice s+2             (last read in 2s)
-// and each wave waits for its own loads (vmcnt 0) at the end of its next
-// compute phase, before the barrier after which the data is first read.
-// Between tiles, group 0 issues the next tile's first slices and its
-// epilogue parameters right after its last compute phase, then writes its
-// outputs while group 1 finishes.
-namespace pp {
-constexpr int BM = 256, BN = 256, BK = 128;
-constexpr int WAVES = 8;
-constexpr int THREADS = WAVES * kWave;
-constexpr int CPR = BK / 16;                        // 16-byte chunks per LDS row
-constexpr int A_BYTES = BM * BK;                    // 32 KiB
-constexpr int HALF_A = A_BYTES / 2;                 // A-top / A-bottom, 16 KiB
-constexpr int STAGE_BYTES = (BM + BN) * BK;         // 64 KiB
-constexpr int MAIN_BYTES = 2 * STAGE_BYTES;
-constexpr int FM = 4, FN = 2;                       // 32 x 32 blocks per wave
-constexpr int KSTEPS = BK / Mfma<32>::KSTEP;        // 2 MFMA K steps per slice
-constexpr int NOFF = 8;                             // load row groups per wave
-constexpr int EPI_BYTES = BM * 4 + BN * 4 + BN * 2; // row scales, column scales, bias
-// Output staging: group 0's waves use 4 KiB each after the parameters; group 1's
-// waves use the A-bottom part of stage buffer 1, which is idle while they write
-// their outputs (the next tile's first loads fill buffer 0 and buffer 1's A-top).
-constexpr int STG_BYTES = 4096;
-constexpr int STG0 = MAIN_BYTES + 2 * EPI_BYTES;
-constexpr int STG1 = STAGE_BYTES + HALF_A;
-constexpr int LDS_BYTES = STG0 + 4 * STG_BYTES;
-static_assert(LDS_BYTES <= 160 * 1024, "gfx950 LDS is 160 KiB per workgroup");
-static_assert(4 * STG_BYTES <= HALF_A, "group 1 staging fits in the A-bottom half");
-}  // namespace pp
-
-// Per-lane load offsets of wave q (0..3 within its group): offset i covers LDS
-// block q + 4i (rows 8*(q + 4i) .. +8 of a 256-row panel, 1 KiB); lane l fills
-// position l % 8 of row 8*(q + 4i) + l / 8 with logical chunk (l % 8) ^
-// swizzle(row).  Row bits 0..3 are the same for every i, so is the chunk.
-struct PpLoads {
-    uint32_t off[pp::NOFF];   // row * K + chunk * 16
-    uint32_t cbyte;           // chunk * 16
-    uint32_t bot;             // 128 * K: A-bottom rows relative to A-top rows
-};
-
-__device__ __forceinline__ void pp_dma(__amdgpu_buffer_rsrc_t r, uint8_t* dst, uint32_t off,
-                                       uint32_t k0, bool inside) {
-    dma16(r, dst, inside ? off : kOutOfRange, k0);
-}
-
-// Loads of slice s (K bytes s*BK ..) into stage buffer buf.  In the K-tail
-// slice, lanes whose chunk lies at or past K read zeros (offset beyond the
-// record limit).
-__device__ __forceinline__ void pp_load_b(uint8_t* smem, int buf, int q, int s,
-                                          __amdgpu_buffer_rsrc_t rb, const PpLoads& L, int K) {
-    const uint32_t k0 = (uint32_t)s * pp::BK;
-    const bool inside = k0 + L.cbyte < (uint32_t)K;
-    uint8_t* st = smem + buf * pp::STAGE_BYTES + pp::A_BYTES;
-#pragma unroll
-    for (int i = 0; i < pp::NOFF; ++i) pp_dma(rb, st + (q + 4 * i) * 1024, L.off[i], k0, inside);
-}
-
-template <bool BOTTOM>
-__device__ __forceinline__ void pp_load_a_half(uint8_t* smem, int buf, int q, int s,
-                                               __amdgpu_buffer_rsrc_t ra, const PpLoads& L, int K) {
-    const uint32_t k0 = (uint32_t)s * pp::BK;
-    const bool inside = k0 + L.cbyte < (uint32_t)K;
-    uint8_t* st = smem + buf * pp::STAGE_BYTES + (BOTTOM ? pp::HALF_A : 0);
-#pragma unroll
-    for (int i = 0; i < pp::NOFF / 2; ++i)
-        pp_dma(ra, st + (q + 4 * i) * 1024, L.off[i] + (BOTTOM ? L.bot : 0u), k0, inside);
-}
-
-// Fragments of one slice for wave (grp, q): A rows grp*128 + j*32 + l, B rows
-// q*64 + i*32 + l; lanes 32..63 take K bytes 32..63 of each 64-byte step.
-__device__ __forceinline__ void pp_read(v8i (&fa)[pp::KSTEPS][pp::FM],
-                                        v8i (&fb)[pp::KSTEPS][pp::FN], const uint8_t* st, int grp,
-                                        int q, int lane) {
-    // Addresses are recomputed here from an opaque copy of the lane id: kept
-    // live across the loop they would cost registers the fragments need.
-    int l = lane % 32;
-    int lh = lane / 32;
-    asm volatile("" : "+v"(l), "+v"(lh));
-#pragma unroll
-    for (int ks = 0; ks < pp::KSTEPS; ++ks) {
-        const int c0 = ks * 4 + lh * 2;
-#pragma unroll
-        for (int j = 0; j < pp::FM; ++j)
-            fa[ks][j] = read_frag<pp::CPR>(st, grp * 128 + j * 32, l, c0);
-#pragma unroll
-        for (int i = 0; i < pp::FN; ++i)
-            fb[ks][i] = read_frag<pp::CPR>(st + pp::A_BYTES, q * 64 + i * 32, l, c0);
-    }
-}
-
-// The 16 MFMAs of one slice, from registers only.
-__device__ __forceinline__ void pp_compute(v16f (&acc)[pp::FN][pp::FM],
-                                           const v8i (&fa)[pp::KSTEPS][pp::FM],
-                                           const v8i (&fb)[pp::KSTEPS][pp::FN]) {
-#pragma unroll
-    for (int ks = 0; ks < pp::KSTEPS; ++ks)
-#pragma unroll
-        for (int i = 0; i < pp::FN; ++i)
-#pragma unroll
-            for (int j = 0; j < pp::FM; ++j)
-                acc[i][j] = Mfma<32>::run(fb[ks][i], fa[ks][j], acc[i][j]);
-}
-
-struct PpTile {
-    int row0, col0;
-    __amdgpu_buffer_rsrc_t ra, rb;
-};
-
-__device__ __forceinline__ PpTile pp_tile(const Params& p, int t, int group_m) {
-    PpTile T;
-    int pm, pn;
-    tile_coords(t, p.tiles_m, p.tiles_n, group_m, pm, pn);
-    T.row0 = pm * pp::BM;
-    T.col0 = pn * pp::BN;
-    const uint32_t rows_a = (uint32_t)min(pp::BM, p.M - T.row0);
-    const uint32_t rows_b = (uint32_t)min(pp::BN, p.N - T.col0);
-    T.ra = make_rsrc(p.A + (size_t)T.row0 * p.K, rows_a * (uint32_t)p.K);
-    T.rb = make_rsrc(p.B + (size_t)T.col0 * p.K, rows_b * (uint32_t)p.K);
-    return T;
-}
-
-// A tile's first loads, all from group 0 (wave q): its first K slice (s0)
-// whole and A-top of its second (s1); plus the tile's epilogue parameters (thread q*64 + lane takes row /
-// column q*64 + lane) into the given LDS area.
-__device__ __forceinline__ void pp_tile_start(uint8_t* smem, const Params& p, const PpTile& T,
-                                              const PpLoads& L, int q, int lane, int s0, int s1,
-                                              bool need_epi, bool has_bias, float* epi_sa,
-                                              float* epi_sb, uint16_t* epi_bias) {
-    pp_load_b(smem, 0, q, s0, T.rb, L, p.K);
-    pp_load_a_half<false>(smem, 0, q, s0, T.ra, L, p.K);
-    pp_load_a_half<true>(smem, 0, q, s0, T.ra, L, p.K);
-    if (p.k_iters > 1) pp_load_a_half<false>(smem, 1, q, s1, T.ra, L, p.K);
-    if (need_epi) {
-        const int r = q * kWave + lane;   // 0..255
-        float pa = 0.f, pb = 0.f;
-        uint16_t pbias = 0;
-        if (p.rowwise) {
-            pa = T.row0 + r < p.M ? p.scale_a[T.row0 + r] : 0.f;
-            pb = T.col0 + r < p.N ? p.scale_b[T.col0 + r] : 0.f;
-        }
-        if (has_bias && T.col0 + r < p.N) pbias = p.bias[T.col0 + r];
-        epi_sa[r] = pa;
-        epi_sb[r] = pb;
-        epi_bias[r] = pbias;
-    }
-}
-
-// Epilogue of wave (g, q) of the ping-pong kernel through a private 4 KiB LDS
-// area: each 32 x 64 block row of its outputs is written to LDS in the MFMA
-// layout (row l % 32, 4 columns per lane) and read back as 8 rows x 128 bytes
-// per instruction, so every global store writes 8 whole 128-byte lines
-// (instead of 32 pieces of 16 bytes).  LDS operations of one wave complete in
-// order, so no barrier is needed.  In the LDS area, 16-byte chunk c of row r
-// sits at c ^ ((r >> 1) & 7) (at most 2-way bank conflicts on the writes).
-// Falls back to store_tile where the block is not wholly inside the output or
-// 16-byte stores are not allowed.
-template <bool RW, bool BIAS>
-__device__ __forceinline__ void pp_store_staged(const v16f (&acc)[pp::FN][pp::FM], const Params& p,
-                                                int row0, int col0, int mbase, int nbase,
-                                                const float* epi_sa, const float* epi_sb,
-                                                const uint16_t* epi_bias, float s_pt, int lane,
-                                                uint8_t* stg) {
-    constexpr int FM = pp::FM, FN = pp::FN;
-    float sa_r[FM];
-    v4f sb_r[FN][4];
-    uint2 b_r[FN][4];
-    const int h = lane / 32;
-#pragma unroll
-    for (int j = 0; j < FM; ++j) sa_r[j] = RW ? epi_sa[mbase + j * 32 + lane % 32] : s_pt;
-#pragma unroll
-    for (int i = 0; i < FN; ++i)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const int nl = nbase + i * 32 + 8 * g + 4 * h;
-            if constexpr (RW) sb_r[i][g] = *reinterpret_cast<const v4f*>(epi_sb + nl);
-            if constexpr (BIAS) b_r[i][g] = *reinterpret_cast<const uint2*>(epi_bias + nl);
-        }
-    const int r = lane % 32;
-#pragma unroll
-    for (int j = 0; j < FM; ++j) {
-#pragma unroll
-        for (int i = 0; i < FN; ++i)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                float y[4];
-#pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    const float sc = RW ? sa_r[j] * sb_r[i][g][c] : s_pt;
-                    const float v = acc[i][j][4 * g + c];
-                    if constexpr (BIAS) {
-                        const uint32_t bw = c < 2 ? b_r[i][g].x : b_r[i][g].y;
-                        const float bv = __uint_as_float(c % 2 == 0 ? bw << 16 : bw & 0xffff0000u);
-                        y[c] = __builtin_fmaf(v, sc, bv);
-                    } else {
-                        y[c] = v * sc;
-                    }
-                }
-                uint2 w;
-                w.x = pack_bf16x2(y[0], y[1]);
-                w.y = pack_bf16x2(y[2], y[3]);
-                const int cpos = (i * 4 + g) ^ ((r >> 1) & 7);
-                *reinterpret_cast<uint2*>(stg + r * 128 + cpos * 16 + h * 8) = w;
-            }
-#pragma unroll
-        for (int pass = 0; pass < 4; ++pass) {
-            const int rr = pass * 8 + lane / 8;
-            const int cc = lane % 8;
-            const v4i v = *reinterpret_cast<const v4i*>(stg + rr * 128 + ((cc ^ ((rr >> 1) & 7)) * 16));
-            uint16_t* dst = p.out + (size_t)(row0 + mbase + j * 32 + rr) * p.N + col0 + nbase + cc * 8;
-            *reinterpret_cast<v4i*>(dst) = v;
-        }
-    }
-}
-
-__device__ __forceinline__ void pp_store(const v16f (&acc)[pp::FN][pp::FM], const Params& p,
-                                         int row0, int col0, int mbase, int nbase,
-                                         const float* epi_sa, const float* epi_sb,
-                                         const uint16_t* epi_bias, float s_pt, bool has_bias,
-                                         int lane, uint8_t* stg) {
-    asm volatile("" : "+v"(lane));
-    const bool full = p.vec16 && row0 + mbase + pp::FM * 32 <= p.M &&
-                      col0 + nbase + pp::FN * 32 <= p.N;   // wave-uniform
-    if (!full) {
-        store_tile<32, pp::FM, pp::FN>(acc, p, row0, col0, mbase, nbase, epi_sa, epi_sb, epi_bias,
-                                       s_pt, has_bias, lane);
-        return;
-    }
-    if (p.rowwise) {
-        if (has_bias)
-            pp_store_staged<true, true>(acc, p, row0, col0, mbase, nbase, epi_sa, epi_sb, epi_bias,
-                                        s_pt, lane, stg);
-        else
-            pp_store_staged<true, false>(acc, p, row0, col0, mbase, nbase, epi_sa, epi_sb, epi_bias,
-                                         s_pt, lane, stg);
-    } else {
-        if (has_bias)
-            pp_store_staged<false, true>(acc, p, row0, col0, mbase, nbase, epi_sa, epi_sb, epi_bias,
-                                         s_pt, lane, stg);
-        else
-            pp_store_staged<false, false>(acc, p, row0, col0, mbase, nbase, epi_sa, epi_sb,
-                                          epi_bias, s_pt, lane, stg);
-    }
-}
-
-template <int GROUP_M>
-__global__ void __launch_bounds__(pp::THREADS) fp8_gemm_pp_kernel(Params p) {
-    using namespace pp;
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[LDS_BYTES];
-
-    const int tid = threadIdx.x;
-    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-    const int lane = tid % kWave;
-    const int grp = wave / 4;
-    const int q = wave % 4;
-
-    const int G = gridDim.x;
-    int wg = blockIdx.x;
-    if (G % kXcds == 0) wg = (blockIdx.x % kXcds) * (G / kXcds) + blockIdx.x / kXcds;
-    if (wg >= p.num_tiles) return;   // whole workgroup
-    // The workgroups of XCD x walk K starting at slice x * k_iters / 8 (and
-    // wrap): the XCDs finish their tiles at different times, so the output
-    // stores of the whole GPU do not all arrive at once.  The 32 workgroups of
-    // one XCD stay in step and keep sharing the slices in its L2.
-    const int k_iters = p.k_iters;
-    const int rot = G % kXcds == 0 ? (int)(blockIdx.x % kXcds) * k_iters / kXcds : 0;
-    auto slice = [&](int step) { return step + rot < k_iters ? step + rot : step + rot - k_iters; };
-
-    PpLoads L;
-    L.cbyte = (uint32_t)(((lane % 8) ^ chunk_swizzle<CPR>((q & 1) * 8 + lane / 8)) * 16);
-#pragma unroll
-    for (int i = 0; i < NOFF; ++i)
-        L.off[i] = (uint32_t)((8 * (q + 4 * i) + lane / 8) * p.K) + L.cbyte;
-    L.bot = 128u * (uint32_t)p.K;
-
-    const float s_pt = p.rowwise ? 0.f : p.scale_a[0] * p.scale_b[0];
-    const bool has_bias = p.bias != nullptr;
-    const bool need_epi = p.rowwise || has_bias;
-    auto epi_area = [&](int parity, float*& sa, float*& sb, uint16_t*& bias) {
-        sa = reinterpret_cast<float*>(smem + MAIN_BYTES + parity * EPI_BYTES);
-        sb = sa + BM;
-        bias = reinterpret_cast<uint16_t*>(sb + BN);
-    };
-
-    int parity = 0;
-    PpTile T = pp_tile(p, wg, GROUP_M);
-    if (grp == 0) {
-        float *sa, *sb;
-        uint16_t* bias;
-        epi_area(0, sa, sb, bias);
-        pp_tile_start(smem, p, T, L, q, lane, slice(0), slice(1), need_epi, has_bias, sa, sb, bias);
-        wait_vmcnt<0>();
-    }
-    barrier_lds();
-    __builtin_amdgcn_sched_barrier(0);
-
-    for (int t = wg; t < p.num_tiles; t += G, parity ^= 1) {
-        v16f acc[FN][FM];
-#pragma unroll
-        for (int i = 0; i < FN; ++i)
-#pragma unroll
-            for (int j = 0; j < FM; ++j) acc[i][j] = v16f{};
-        v8i fa[KSTEPS][FM], fb[KSTEPS][FN];
-        float *epi_sa, *epi_sb;
-        uint16_t* epi_bias;
-        epi_area(parity, epi_sa, epi_sb, epi_bias);
-
-        if (grp == 0) {
-            for (int s = 0; s < k_iters; ++s) {
-                // memory phase 2s: fragments of slice s, B of slice s+1
-                pp_read(fa, fb, smem + (s & 1) * STAGE_BYTES, 0, q, lane);
-                if (s + 1 < k_iters) pp_load_b(smem, (s + 1) & 1, q, slice(s + 1), T.rb, L, p.K);
-                barrier_lds();
-                __builtin_amdgcn_sched_barrier(0);
-                // compute phase 2s+1
-                pp_compute(acc, fa, fb);
-                __builtin_amdgcn_sched_barrier(0);
-                wait_vmcnt<0>();
-                barrier_lds();
-                __builtin_amdgcn_sched_barrier(0);
-            }
-            // Between tiles: the next tile's first loads and parameters (every
-            // stage buffer is free: group 1 is in its last compute phase), then
-            // this tile's outputs.
-            const int tn = t + G;
-            const PpTile T0 = T;
-            if (tn < p.num_tiles) {
-                T = pp_tile(p, tn, GROUP_M);
-                float *sa, *sb;
-                uint16_t* bias;
-                epi_area(parity ^ 1, sa, sb, bias);
-                pp_tile_start(smem, p, T, L, q, lane, slice(0), slice(1), need_epi, has_bias, sa, sb,
-                              bias);
-            }
-            pp_store(acc, p, T0.row0, T0.col0, 0, q * 64, epi_sa, epi_sb, epi_bias, s_pt, has_bias,
-                     lane, smem + STG0 + q * STG_BYTES);
-            wait_vmcnt<0>();
-            barrier_lds();   // pairs with group 1's last barrier of the tile
-            __builtin_amdgcn_sched_barrier(0);
-        } else {
-            __builtin_amdgcn_s_barrier();   // one phase behind group 0
-            __builtin_amdgcn_sched_barrier(0);
-            for (int s = 0; s < k_iters; ++s) {
-                // memory phase 2s+1: fragments of slice s, A-bottom of s+1, A-top of s+2
-                pp_read(fa, fb, smem + (s & 1) * STAGE_BYTES, 1, q, lane);
-                if (s + 1 < k_iters)
-                    pp_load_a_half<true>(smem, (s + 1) & 1, q, slice(s + 1), T.ra, L, p.K);
-                if (s + 2 < k_iters)
-                    pp_load_a_half<false>(smem, s & 1, q, slice(s + 2), T.ra, L, p.K);
-                barrier_lds();
-                __builtin_amdgcn_sched_barrier(0);
-                // compute phase 2s+2
-                pp_compute(acc, fa, fb);
-                __builtin_amdgcn_sched_barrier(0);
-                wait_vmcnt<0>();
-                barrier_lds();
-                __builtin_amdgcn_sched_barrier(0);
-            }
-            pp_store(acc, p, T.row0, T.col0, 128, q * 64, epi_sa, epi_sb, epi_bias, s_pt, has_bias,
-                     lane, smem + STG1 + q * STG_BYTES);
-            if (t + G < p.num_tiles) T = pp_tile(p, t + G, GROUP_M);
-        }
-    }
-}
-
-template <int GROUP_M>
-void launch_pp(const Params& p, dim3 grid, hipStream_t stream) {
-    hipLaunchKernelGGL((fp8_gemm_pp_kernel<GROUP_M>), grid, dim3(pp::THREADS), 0, stream, p);
-}
 
 // ------------------------------------------------------------------ host ---
 
@@ -1243,45 +49,23 @@ struct ConfigInfo {
     int threads;
     int lds_bytes;
     int occupancy;   // workgroups per CU the persistent grid assumes
-    void (*launch)(const Params&, dim3, hipStream_t);
-    // The same tiles with B loaded non-temporally, for grids with a single row
-    // of tiles (B is then read once); null where not compiled.
-    void (*launch_stream)(const Params&, dim3, hipStream_t);
 };
 
-template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int STAGES, int MI, int GROUP_M,
-          bool NT_B>
-void launch_cfg(const Params& p, dim3 grid, hipStream_t stream) {
-    using C = Cfg<BM, BN, BK, WAVES_M, WAVES_N, STAGES, MI, GROUP_M, NT_B>;
-    hipLaunchKernelGGL((fp8_gemm_kernel<BM, BN, BK, WAVES_M, WAVES_N, STAGES, MI, GROUP_M, NT_B>),
-                       grid, dim3(C::THREADS), 0, stream, p);
-}
-
-#define FP8MM_CFG(name, BM, BN, BK, WMW, WNW, ST, MI, GM, STREAM)                                 \
-    ConfigInfo {                                                                                  \
-        name, BM, BN, BK, Cfg<BM, BN, BK, WMW, WNW, ST, MI, GM>::SPLIT_OK,                        \
-            Cfg<BM, BN, BK, WMW, WNW, ST, MI, GM>::THREADS,                                       \
-            Cfg<BM, BN, BK, WMW, WNW, ST, MI, GM>::LDS_BYTES, 1,                                  \
-            &launch_cfg<BM, BN, BK, WMW, WNW, ST, MI, GM, false>,                                 \
-            STREAM ? &launch_cfg<BM, BN, BK, WMW, WNW, ST, MI, GM, true> : nullptr                \
-    }
+#define FP8MM_CFG_INFO(name, BM, BN, BK, WMW, WNW, ST, MI, GM)                               \
+    ConfigInfo{name, BM, BN, BK, Cfg<BM, BN, BK, WMW, WNW, ST, MI, GM>::SPLIT_OK,             \
+               Cfg<BM, BN, BK, WMW, WNW, ST, MI, GM>::THREADS,                                \
+               Cfg<BM, BN, BK, WMW, WNW, ST, MI, GM>::LDS_BYTES, 1},
 
 // Ids are the positions in this table (the C ABI's config_id).
-const ConfigInfo kConfigs[] = {
-    FP8MM_CFG("bm128_bn128_bk128_w2x2_s3_mfma32", 128, 128, 128, 2, 2, 3, 32, 8, true),
-    FP8MM_CFG("bm16_bn64_bk256_w1x4_s4_mfma16", 16, 64, 256, 1, 4, 4, 16, 8, true),
-    FP8MM_CFG("bm16_bn112_bk256_w1x7_s4_mfma16", 16, 112, 256, 1, 7, 4, 16, 8, true),
-    FP8MM_CFG("bm16_bn32_bk512_w1x2_s6_mfma16", 16, 32, 512, 1, 2, 6, 16, 8, true),
-    FP8MM_CFG("bm64_bn64_bk128_w4x1_s8_mfma16", 64, 64, 128, 4, 1, 8, 16, 8, true),
-    FP8MM_CFG("bm64_bn112_bk256_w1x7_s3_mfma16", 64, 112, 256, 1, 7, 3, 16, 8, true),
-    FP8MM_CFG("bm64_bn64_bk256_w1x4_s4_mfma16", 64, 64, 256, 1, 4, 4, 16, 8, true),
-    FP8MM_CFG("bm128_bn128_bk128_w2x2_s4_mfma32", 128, 128, 128, 2, 2, 4, 32, 8, true),
-    FP8MM_CFG("bm128_bn128_bk128_w2x4_s4_mfma32", 128, 128, 128, 2, 4, 4, 32, 8, true),
-    FP8MM_CFG("bm256_bn256_bk128_w2x4_s2_mfma32", 256, 256, 128, 2, 4, 2, 32, 8, false),
+const ConfigInfo kConfigs[kNumConfigs] = {
+    FP8MM_GENERIC_CONFIGS(FP8MM_CFG_INFO)
     ConfigInfo{"pp_bm256_bn256_bk128_w8_mfma32", pp::BM, pp::BN, pp::BK, false, pp::THREADS,
-               pp::LDS_BYTES, 1, &launch_pp<8>, nullptr},
+               pp::LDS_BYTES, 1},
 };
-constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
+#undef FP8MM_CFG_INFO
+
+// Launch wrappers by operand formats, then configuration.
+LaunchPair* const kLaunch[kFormats] = {kLaunchF0, kLaunchF1, kLaunchF2, kLaunchF3};
 constexpr int kMidConfig = 8;         // "bm128_bn128_bk128_w2x4_s4_mfma32"
 constexpr int kSkinny16x64 = 1;       // "bm16_bn64_bk256_w1x4_s4_mfma16"
 constexpr int kSkinny16x112 = 2;      // "bm16_bn112_bk256_w1x7_s4_mfma16"
@@ -1445,14 +229,19 @@ const char* fp8_scaled_mm_status_string(int s) {
         case FP8MM_ERR_LAUNCH: return "kernel launch failed";
         case FP8MM_ERR_CONFIG: return "unknown tile configuration or split count";
         case FP8MM_ERR_WORKSPACE: return "workspace smaller than fp8_scaled_mm_workspace_size()";
+        case FP8MM_ERR_FORMAT: return "unknown operand format (FP8MM_E4M3FN or FP8MM_E5M2)";
         default: return "unknown status";
     }
 }
 
-int fp8_scaled_mm_with_plan(const void* A, const void* B, const float* scale_a,
-                            const float* scale_b, const void* bias, void* out, int64_t M, int64_t N,
-                            int64_t K, int mode, struct ihipStream_t* stream, int config_id,
-                            int splits, void* workspace, int64_t workspace_size) {
+int fp8_scaled_mm_typed(const void* A, int a_format, const void* B, int b_format,
+                        const float* scale_a, const float* scale_b, const void* bias, void* out,
+                        int64_t M, int64_t N, int64_t K, int mode, struct ihipStream_t* stream,
+                        int config_id, int splits, void* workspace, int64_t workspace_size) {
+    if ((a_format != FP8MM_E4M3FN && a_format != FP8MM_E5M2) ||
+        (b_format != FP8MM_E4M3FN && b_format != FP8MM_E5M2))
+        return FP8MM_ERR_FORMAT;
+    const int fmt = (a_format == FP8MM_E5M2 ? 1 : 0) | (b_format == FP8MM_E5M2 ? 2 : 0);
     int st = validate(A, B, scale_a, scale_b, bias, out, M, N, K, mode);
     if (st != FP8MM_OK) return st;
     if (config_id >= kNumConfigs) return FP8MM_ERR_CONFIG;
@@ -1511,10 +300,19 @@ int fp8_scaled_mm_with_plan(const void* A, const void* B, const float* scale_a,
 
     const dim3 grid((unsigned)grid_for(cfg, M, N, sp, cus));
     (void)hipGetLastError();  // clear a stale error from earlier, unrelated calls
-    if (p.tiles_m == 1 && c.launch_stream) c.launch_stream(p, grid, hs);
-    else c.launch(p, grid, hs);
+    const LaunchPair& l = kLaunch[fmt][cfg];
+    if (p.tiles_m == 1 && l.stream) l.stream(p, grid, hs);
+    else l.plain(p, grid, hs);
     if (hipGetLastError() != hipSuccess) return FP8MM_ERR_LAUNCH;
     return FP8MM_OK;
+}
+
+int fp8_scaled_mm_with_plan(const void* A, const void* B, const float* scale_a,
+                            const float* scale_b, const void* bias, void* out, int64_t M, int64_t N,
+                            int64_t K, int mode, struct ihipStream_t* stream, int config_id,
+                            int splits, void* workspace, int64_t workspace_size) {
+    return fp8_scaled_mm_typed(A, FP8MM_E4M3FN, B, FP8MM_E4M3FN, scale_a, scale_b, bias, out, M, N,
+                               K, mode, stream, config_id, splits, workspace, workspace_size);
 }
 
 int fp8_scaled_mm_with_config(const void* A, const void* B, const float* scale_a,

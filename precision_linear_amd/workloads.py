@@ -8,11 +8,14 @@ done with torch's CPU casts, exactly as the input recipe of the gist
 "matmul_fp8.py" (a-r-r-o-w), functions `get_scale` and `benchmark`, prepares
 its operands: amax -> scale = amax / 448 -> x / scale -> clamp to +-448 ->
 cast to e4m3fn.  The clamp matters because torch's e4m3fn cast does not
-saturate (anything at or above 464 in magnitude becomes NaN).
+saturate (anything at or above 464 in magnitude becomes NaN).  The gist's
+benchmark also takes float8_e5m2 operands; those use 57344 (the e5m2 finfo
+maximum) in place of 448 and torch's e5m2 cast.
 
 Layouts produced (all C-contiguous numpy arrays):
-  a        uint8  [M, K]   e4m3fn codes, K fastest
-  b        uint8  [N, K]   e4m3fn codes, K fastest (the "TN" layout: the
+  a        uint8  [M, K]   float8 codes (e4m3fn unless the workload says
+                           e5m2), K fastest
+  b        uint8  [N, K]   float8 codes, K fastest (the "TN" layout: the
                            K x N column-major operand of the pages, stored
                            as its N x K transpose)
   scale_a  float32 [1] (per-tensor) or [M] (row-wise)
@@ -35,6 +38,8 @@ PER_TENSOR = 0
 ROWWISE = 1
 MODE_NAMES = {PER_TENSOR: "per_tensor", ROWWISE: "rowwise"}
 E4M3_MAX = 448.0
+E5M2_MAX = 57344.0
+FORMATS = ("e4m3fn", "e5m2")
 BASE_SEED = 42
 
 
@@ -47,6 +52,8 @@ class Workload:
     mode: int            # PER_TENSOR or ROWWISE
     recipe: str          # "normal", "skinny", "codes"
     bias: bool = False
+    a_format: str = "e4m3fn"
+    b_format: str = "e4m3fn"
 
     @property
     def flops(self) -> int:
@@ -62,8 +69,8 @@ class Workload:
         return self.M * self.K + self.N * self.K + sa + sb + bias + 2 * self.M * self.N
 
 
-def _wl(name, M, N, K, mode, recipe, bias=False):
-    return Workload(name, M, N, K, mode, recipe, bias)
+def _wl(name, M, N, K, mode, recipe, bias=False, a_format="e4m3fn", b_format="e4m3fn"):
+    return Workload(name, M, N, K, mode, recipe, bias, a_format, b_format)
 
 
 # The synthetic workloads: square shapes with N(0,1) inputs quantised by amax,
@@ -89,6 +96,14 @@ WORKLOADS = {w.name: w for w in [
     for m in (512, 1152, 2304, 4608)
     for (k, n) in ((3072, 12288), (12288, 3072))
     for mode in (PER_TENSOR, ROWWISE)
+] + [
+    # e5m2 operands (the gist's other float8 dtype), and mixed e4m3fn x e5m2
+    _wl(f"fmt_{m}x{n}x{k}_{fa}_{fb}_{MODE_NAMES[mode]}", m, n, k, mode, recipe,
+        a_format=fa, b_format=fb)
+    for (m, n, k, recipe) in ((2048, 2048, 2048, "normal"), (8192, 8192, 8192, "normal"),
+                              (4095, 4097, 96, "codes"))
+    for (fa, fb) in (("e5m2", "e5m2"), ("e4m3fn", "e5m2"), ("e5m2", "e4m3fn"))
+    for mode in (PER_TENSOR, ROWWISE)
 ]}
 
 
@@ -100,6 +115,8 @@ class Inputs:
     scale_b: np.ndarray
     bias: Optional[np.ndarray]
     mode: int
+    a_format: str = "e4m3fn"
+    b_format: str = "e4m3fn"
 
     @property
     def shape(self):
@@ -152,30 +169,40 @@ def _bf16_normal(key, tensor_id, shape, std=1.0) -> np.ndarray:
     return torch.from_numpy(x).to(torch.bfloat16).to(torch.float32).numpy()
 
 
-def _quantise(x: np.ndarray, rowwise: bool):
-    """amax/448 scale (whole tensor or per row of the K-fastest layout),
-    then x/scale clamped to +-448 and cast to e4m3fn by torch."""
+def _quantise(x: np.ndarray, rowwise: bool, fmt: str = "e4m3fn"):
+    """amax/qmax scale (whole tensor or per row of the K-fastest layout),
+    then x/scale clamped to +-qmax and cast by torch; qmax = 448 (e4m3fn) or
+    57344 (e5m2)."""
     torch = _torch()
+    qmax = E4M3_MAX if fmt == "e4m3fn" else E5M2_MAX
+    dtype = torch.float8_e4m3fn if fmt == "e4m3fn" else torch.float8_e5m2
     t = torch.from_numpy(x)
     if rowwise:
         amax = t.abs().amax(dim=1)
     else:
         amax = t.abs().amax().reshape(1)
     amax = torch.where(amax > 0, amax, torch.ones_like(amax))
-    scale = amax / torch.tensor(E4M3_MAX, dtype=torch.float32)
-    q = (t / (scale[:, None] if rowwise else scale)).clamp(-E4M3_MAX, E4M3_MAX)
-    codes = q.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    scale = amax / torch.tensor(qmax, dtype=torch.float32)
+    q = (t / (scale[:, None] if rowwise else scale)).clamp(-qmax, qmax)
+    codes = q.to(dtype).view(torch.uint8).numpy()
     return np.ascontiguousarray(codes), scale.numpy().astype(np.float32)
 
 
-# The 254 byte codes of e4m3fn that are not NaN (0x7F and 0xFF are NaN).
-_NON_NAN_CODES = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+# The finite byte codes of each format: e4m3fn has NaN at 0x7F and 0xFF; e5m2
+# has infinities and NaNs wherever the exponent field is all ones.
+_FINITE_CODES = {
+    "e4m3fn": np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8),
+    "e5m2": np.array([c for c in range(256) if (c & 0x7C) != 0x7C], dtype=np.uint8),
+}
+_NON_NAN_CODES = _FINITE_CODES["e4m3fn"]
 
 
-def _codes(key, tensor_id, shape, zero_frac=0.01) -> np.ndarray:
+def _codes(key, tensor_id, shape, zero_frac=0.01, fmt="e4m3fn") -> np.ndarray:
+    pool = _FINITE_CODES[fmt]
+
     def fill(i, shp):
         rng = _rng(key, tensor_id, i)
-        c = _NON_NAN_CODES[rng.integers(0, _NON_NAN_CODES.size, size=shp, dtype=np.int64)]
+        c = pool[rng.integers(0, pool.size, size=shp, dtype=np.int64)]
         c[rng.random(shp, dtype=np.float32) < zero_frac] = 0
         return c
     return _blocked(shape, fill)
@@ -186,18 +213,20 @@ def _log_uniform_scales(rng, n) -> np.ndarray:
 
 
 def make_inputs(M: int, N: int, K: int, mode: int, recipe: str, bias: bool = False,
-                key: int = 0) -> Inputs:
+                key: int = 0, a_format: str = "e4m3fn", b_format: str = "e4m3fn") -> Inputs:
     """Seeded inputs for an (M, N, K) problem.  `key` selects the stream."""
     rowwise = mode == ROWWISE
+    if a_format not in FORMATS or b_format not in FORMATS:
+        raise ValueError(f"formats must be among {FORMATS}")
     if recipe in ("normal", "skinny"):
         a_f = _bf16_normal(key, 0, (M, K))
         b_f = _bf16_normal(key, 1, (N, K), std=0.02 if recipe == "skinny" else 1.0)
-        a, sa = _quantise(a_f, rowwise)
-        b, sb = _quantise(b_f, rowwise)
+        a, sa = _quantise(a_f, rowwise, a_format)
+        b, sb = _quantise(b_f, rowwise, b_format)
         del a_f, b_f
     elif recipe == "codes":
-        a = _codes(key, 0, (M, K))
-        b = _codes(key, 1, (N, K))
+        a = _codes(key, 0, (M, K), fmt=a_format)
+        b = _codes(key, 1, (N, K), fmt=b_format)
         sa = _log_uniform_scales(_rng(key, 2), M if rowwise else 1)
         sb = _log_uniform_scales(_rng(key, 3), N if rowwise else 1)
     else:
@@ -205,7 +234,7 @@ def make_inputs(M: int, N: int, K: int, mode: int, recipe: str, bias: bool = Fal
     bias_bits = None
     if bias:
         bias_bits = _bf16_bits_normal(_rng(key, 4), N)
-    return Inputs(a, b, sa, sb, bias_bits, mode)
+    return Inputs(a, b, sa, sb, bias_bits, mode, a_format, b_format)
 
 
 def bf16_matrix_bits(rows: int, cols: int, key: int, std: float = 1.0) -> np.ndarray:
@@ -228,4 +257,5 @@ def workload_key(name: str) -> int:
 
 def make_workload(name: str) -> Inputs:
     w = WORKLOADS[name]
-    return make_inputs(w.M, w.N, w.K, w.mode, w.recipe, w.bias, key=workload_key(name))
+    return make_inputs(w.M, w.N, w.K, w.mode, w.recipe, w.bias, key=workload_key(name),
+                       a_format=w.a_format, b_format=w.b_format)

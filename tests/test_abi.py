@@ -39,8 +39,8 @@ def test_exports_every_declared_function(L):
 
 
 def test_status_strings(L):
-    for s in range(8):
-        assert binding.status_string(s)
+    for s in range(10):
+        assert binding.status_string(s) != "unknown status"
     assert binding.status_string(99) == "unknown status"
 
 
@@ -179,3 +179,48 @@ def test_quantize_status_strings(L):
     for s in range(7):
         assert L.fp8_quantize_status_string(s)
     assert L.fp8_quantize_status_string(42) == b"unknown status"
+
+
+# ---- operand formats -----------------------------------------------------------
+
+def tcall(L, fa=0, fb=0, M=64, N=64, K=64, mode=0, cfg=-1, A=P, B=P):
+    return L.fp8_scaled_mm_typed(A, fa, B, fb, P, P, None, P, M, N, K, mode, None, cfg, 0, None, 0)
+
+
+@pytest.mark.parametrize("fa,fb", [(2, 0), (0, 2), (-1, 0), (0, -1), (7, 7)])
+def test_typed_rejects_unknown_formats(L, fa, fb):
+    assert tcall(L, fa, fb) == binding.ERR_FORMAT
+    assert tcall(L, fa, fb, M=0) == binding.ERR_FORMAT      # checked before anything else
+
+
+def test_typed_validates_like_the_plain_entry(L):
+    for fa, fb in ((1, 1), (0, 1), (1, 0)):
+        assert tcall(L, fa, fb, K=40) == binding.ERR_SHAPE
+        assert tcall(L, fa, fb, A=P + 8) == binding.ERR_ALIGN
+        assert tcall(L, fa, fb, mode=5) == binding.ERR_MODE
+        assert tcall(L, fa, fb, M=0) == binding.OK
+        assert tcall(L, fa, fb, cfg=10 ** 6) == binding.ERR_CONFIG
+    assert binding.status_string(binding.ERR_FORMAT).startswith("unknown operand format")
+
+
+def test_python_binding_rejects_bad_formats():
+    import torch
+    a = torch.zeros(4, 32, dtype=torch.uint8)
+    with pytest.raises(ValueError):
+        binding.fp8_scaled_mm(a, a, a, a, a_format="e3m4")
+    with pytest.raises(ValueError):
+        binding.fp8_scaled_mm(a.view(torch.float8_e5m2), a, a, a, a_format="e4m3fn")
+    x = torch.zeros(4, 32, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        binding.fp8_quantize(x, fmt="e4m3")
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(mode=2), binding.Q_ERR_MODE), (dict(cols=24), binding.Q_ERR_SHAPE),
+    (dict(x=None), binding.Q_ERR_NULL), (dict(q=P + 4), binding.Q_ERR_ALIGN),
+])
+def test_quantize_e5m2_rejects_bad_arguments(L, kw, code):
+    args = dict(x=P, q=P, scale=P, rows=64, cols=64, mode=1)
+    args.update(kw)
+    assert L.fp8_quantize_e5m2(args["x"], args["q"], args["scale"], args["rows"], args["cols"],
+                               args["mode"], None) == code

@@ -1,6 +1,6 @@
-"""GPU parity of the dynamic e4m3fn quantiser (fp8_quantize_e4m3, through the C
-ABI via the ctypes binding) against the CPU oracle: codes and scales bit for
-bit."""
+"""GPU parity of the dynamic float8 quantisers (fp8_quantize_e4m3 and
+fp8_quantize_e5m2, through the C ABI via the ctypes binding) against the CPU
+oracle: codes and scales bit for bit."""
 import numpy as np
 import pytest
 import torch
@@ -12,23 +12,26 @@ from parity import compare
 pytestmark = pytest.mark.gpu
 PT, RW = oracle.PER_TENSOR, oracle.ROWWISE
 DEV = "cuda:0"
+FMTS = ["e4m3fn", "e5m2"]
+OFMT = {"e4m3fn": oracle.E4M3FN, "e5m2": oracle.E5M2}
+QMAX = {"e4m3fn": 448.0, "e5m2": 57344.0}
 
 
 def bf16_bits(x):
     return torch.from_numpy(np.asarray(x, np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
 
 
-def run(bits, mode):
+def run(bits, mode, fmt="e4m3fn"):
     x = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(DEV)
-    print(f"[quantize] shape={bits.shape} mode={mode}", flush=True)
-    q, s = binding.fp8_quantize(x, mode)
+    print(f"[quantize] shape={bits.shape} mode={mode} fmt={fmt}", flush=True)
+    q, s = binding.fp8_quantize(x, mode, fmt=fmt)
     torch.cuda.synchronize()
     return q.cpu().numpy(), s.cpu().numpy()
 
 
-def check(bits, mode):
-    q, s = run(bits, mode)
-    rq, rs = oracle.quantize_e4m3(bits, mode)
+def check(bits, mode, fmt="e4m3fn"):
+    q, s = run(bits, mode, fmt)
+    rq, rs = oracle.quantize(bits, mode, OFMT[fmt])
     assert np.array_equal(s.view(np.uint32), rs.view(np.uint32)), "scales differ"
     bad = np.argwhere(q != rq)
     assert bad.size == 0, (f"{len(bad)} codes differ, first at {tuple(bad[0])}: "
@@ -46,33 +49,49 @@ def _normal(rows, cols, seed, spread=True):
 
 # cols: one 4096-element chunk, a ragged second chunk, the register-resident
 # 7-8 chunks (28672) and a row too long for registers (40960)
+@pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("mode", [PT, RW])
 @pytest.mark.parametrize("rows,cols", [(1, 16), (3, 48), (37, 4096), (19, 4112), (8, 16384),
                                        (5, 28672), (3, 40960), (300, 272)])
-def test_random_matrices_bitexact(rows, cols, mode):
-    check(_normal(rows, cols, rows * 7 + cols), mode)
+def test_random_matrices_bitexact(rows, cols, mode, fmt):
+    check(_normal(rows, cols, rows * 7 + cols), mode, fmt)
 
 
-def test_every_in_range_bf16_value_converts_like_the_oracle():
-    # per-tensor amax 448 gives scale 1, so y = x: every bf16 value in
-    # [-448, 448] (ties, subnormals, -0) goes through the conversion as is
+@pytest.mark.parametrize("fmt", FMTS)
+def test_every_in_range_bf16_value_converts_like_the_oracle(fmt):
+    # per-tensor amax = qmax gives scale 1, so y = x: every bf16 value in
+    # [-qmax, qmax] (ties, subnormals, -0) goes through the conversion as is
     allb = np.arange(65536, dtype=np.uint32)
     v = (allb << 16).view(np.float32)
-    keep = np.isfinite(v) & (np.abs(v) <= 448.0)
+    keep = np.isfinite(v) & (np.abs(v) <= QMAX[fmt])
     bits = allb[keep].astype(np.uint16)
-    bits = np.concatenate([bits, np.full((-len(bits)) % 16, 0x43E0, np.uint16)])   # pad with 448
-    q, s = check(bits.reshape(-1, 16), PT)
+    pad = bf16_bits([QMAX[fmt]])[0]
+    bits = np.concatenate([bits, np.full((-len(bits)) % 16, pad, np.uint16)])   # pad with qmax
+    q, s = check(bits.reshape(-1, 16), PT, fmt)
     assert s[0] == 1.0
 
 
-def test_every_finite_bf16_value_with_a_huge_amax():
-    # amax = the largest bf16: x/s spans underflow to zero, e4m3 subnormals and 448
+@pytest.mark.parametrize("fmt", FMTS)
+def test_every_finite_bf16_value_with_a_huge_amax(fmt):
+    # amax = the largest bf16: x/s spans underflow to zero, subnormals and qmax
     allb = np.arange(65536, dtype=np.uint32)
     v = (allb << 16).view(np.float32)
     bits = allb[np.isfinite(v)].astype(np.uint16)
     bits = np.concatenate([bits, np.zeros((-len(bits)) % 16, np.uint16)])
-    check(bits.reshape(-1, 16), PT)
-    check(bits.reshape(-1, 256), RW)
+    check(bits.reshape(-1, 16), PT, fmt)
+    check(bits.reshape(-1, 256), RW, fmt)
+
+
+def test_e5m2_zero_rows_and_signed_zeros():
+    x = np.array(_normal(6, 64, 3).view(np.int16), np.int16).view(np.uint16).copy()
+    x[1] = 0x0000
+    x[2] = 0x8000
+    x[3, 5] = 0x8000
+    x[4] = 0
+    x[4, 7] = bf16_bits([[-3.0]])[0, 0]
+    q, s = check(x, RW, "e5m2")
+    assert s[1] == 0 and s[2] == 0 and np.all(q[1] == 0) and np.all(q[2] == 0)
+    assert q[4, 7] == 0xFB and q[3, 5] == 0x80
 
 
 def test_zero_rows_and_signed_zeros():
@@ -110,20 +129,21 @@ def test_repeated_calls_are_identical():
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
 
 
+@pytest.mark.parametrize("fa,fb", [("e4m3fn", "e4m3fn"), ("e5m2", "e5m2"), ("e4m3fn", "e5m2")])
 @pytest.mark.parametrize("mode", [PT, RW])
-def test_quantize_then_multiply(mode):
+def test_quantize_then_multiply(mode, fa, fb):
     # the quantiser's outputs are the multiply's inputs: A (M x K) and B (N x K)
     M, N, K = 96, 160, 512
     xa, xb = _normal(M, K, 21, spread=False), _normal(N, K, 22, spread=False)
     ta = torch.from_numpy(xa.view(np.int16)).view(torch.bfloat16).to(DEV)
     tb = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).to(DEV)
-    qa, sa = binding.fp8_quantize(ta, mode)
-    qb, sb = binding.fp8_quantize(tb, mode)
-    out = binding.fp8_scaled_mm(qa, qb, sa, sb, mode=mode)
+    qa, sa = binding.fp8_quantize(ta, mode, fmt=fa)
+    qb, sb = binding.fp8_quantize(tb, mode, fmt=fb)
+    out = binding.fp8_scaled_mm(qa, qb, sa, sb, mode=mode, a_format=fa, b_format=fb)
     torch.cuda.synchronize()
-    ra, rsa = oracle.quantize_e4m3(xa, mode)
-    rb, rsb = oracle.quantize_e4m3(xb, mode)
+    ra, rsa = oracle.quantize(xa, mode, OFMT[fa])
+    rb, rsb = oracle.quantize(xb, mode, OFMT[fb])
     assert np.array_equal(qa.cpu().numpy(), ra) and np.array_equal(qb.cpu().numpy(), rb)
-    ref = oracle.scaled_mm(ra, rb, rsa, rsb, None, mode)
+    ref = oracle.scaled_mm(ra, rb, rsa, rsb, None, mode, a_format=OFMT[fa], b_format=OFMT[fb])
     nbad, worst, first = compare(out.view(torch.int16).cpu().numpy().view(np.uint16), ref)
     assert nbad == 0, (nbad, worst, first)
