@@ -13,7 +13,10 @@ The JSON line also carries
   cpu_baseline  the CPU oracle timed on a bounded sample (a block of output
                 rows of the same problem) on this host's cores;
   secondary     the skinny inference shapes (row-wise + bias, HBM-bound) with
-                the MALL flushed before every launch, reported in HBM GB/s.
+                the MALL flushed before every launch, reported in HBM GB/s; the
+                gist's mid-size shape sweep, the ragged shapes and the e5m2 /
+                mixed-format 8192^3 multiplies in TFLOP/s; the quantisers in
+                HBM GB/s.
 """
 import argparse
 import hashlib
@@ -30,7 +33,7 @@ sys.path.insert(0, ROOT)
 METRIC = "FP8 scaled-GEMM TFLOP/s and % of dense-FP8 MFMA peak (per-tensor, row-wise)"
 PEAK_FP8_TFLOPS = 5000.0      # MI355X dense FP8 MFMA (no sparsity)
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
-KERNEL_SRC = os.path.join(ROOT, "precision_linear_amd", "csrc", "fp8_scaled_mm.hip")
+KERNEL_SRC = os.path.join(ROOT, "precision_linear_amd", "csrc", "fp8_gemm_kernels.h")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_sq8192.txt")
 
 
@@ -65,7 +68,8 @@ class Problem:
     def launch(self):
         from precision_linear_amd import binding
         binding.fp8_scaled_mm(self.a, self.b, self.sa, self.sb, self.bias, out=self.out,
-                              mode=self.w.mode)
+                              mode=self.w.mode, a_format=self.w.a_format,
+                              b_format=self.w.b_format)
 
 
 def cpu_baseline(problem, target_s=12.0):
@@ -141,26 +145,56 @@ def skinny_results(dev, reps=20):
     return res
 
 
-QUANT_SHAPES = [(8192, 8192, "rowwise"), (8192, 8192, "per_tensor"), (128, 28672, "rowwise")]
+QUANT_SHAPES = [(8192, 8192, "rowwise", "e4m3fn"), (8192, 8192, "per_tensor", "e4m3fn"),
+                (128, 28672, "rowwise", "e4m3fn"), (8192, 8192, "rowwise", "e5m2")]
 
 
-def gist_results(dev, reps=20):
-    """The gist's mid-size shape sweep (MFMA-bound), operands resident in HBM."""
+def resident_results(dev, names, reps=20):
+    """Multiplies with operands resident in HBM: TFLOP/s and, against the
+    binding roofline max(flops / MFMA peak, bytes / HBM peak), the fraction
+    of that bound."""
     import torch
     from precision_linear_amd import workloads as wl
     res = []
-    for name in [n for n in wl.WORKLOADS if n.startswith("gist")]:
+    for name in names:
         p = Problem(name, dev)
         time_launches(p, 3)
         ts = sorted(time_launches(p, reps))
         t50 = ts[len(ts) // 2] * 1e-3
         tf = p.w.flops / t50 / 1e12
+        t_mfma = p.w.flops / (PEAK_FP8_TFLOPS * 1e12)
+        t_hbm = p.w.algorithmic_bytes / (PEAK_HBM_GBS * 1e9)
         res.append({"workload": name, "M": p.w.M, "N": p.w.N, "K": p.w.K,
+                    "formats": f"{p.w.a_format}x{p.w.b_format}",
                     "us_p50": round(t50 * 1e6, 2), "tflops": round(tf, 1),
-                    "frac_mfma": round(tf / PEAK_FP8_TFLOPS, 4)})
+                    "frac_mfma": round(tf / PEAK_FP8_TFLOPS, 4),
+                    "bound": "mfma" if t_mfma >= t_hbm else "hbm",
+                    "frac_roofline": round(max(t_mfma, t_hbm) / t50, 4)})
         del p
         torch.cuda.empty_cache()
     return res
+
+
+def gist_results(dev, reps=20):
+    """The gist's mid-size shape sweep (MFMA-bound), operands resident in HBM."""
+    from precision_linear_amd import workloads as wl
+    return resident_results(dev, [n for n in wl.WORKLOADS if n.startswith("gist")], reps)
+
+
+def ragged_results(dev, reps=20):
+    """The ragged shapes (raw e4m3fn codes, log-uniform scales); the K = 32
+    and K = 96 ones are bound by the output write."""
+    from precision_linear_amd import workloads as wl
+    names = [n for n in wl.WORKLOADS if n.startswith("ragged")
+             and not (n.startswith("ragged_16384") and n.endswith("rowwise"))]
+    return resident_results(dev, names, reps)
+
+
+def format_results(dev, reps=20):
+    """8192^3 row-wise with e5m2 operands and with mixed e4m3fn x e5m2."""
+    from precision_linear_amd import workloads as wl
+    names = [n for n in wl.WORKLOADS if n.startswith("fmt_8192x8192x8192") and n.endswith("rowwise")]
+    return resident_results(dev, names, reps)
 
 
 def quant_results(dev, reps=20):
@@ -173,16 +207,16 @@ def quant_results(dev, reps=20):
     from precision_linear_amd import workloads as wl
     flush = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
     res = []
-    for rows, cols, mode in QUANT_SHAPES:
+    for rows, cols, mode, fmt in QUANT_SHAPES:
         bits = wl.bf16_matrix_bits(rows, cols, key=wl.workload_key(f"quant_{rows}x{cols}"))
         x = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
-        q, s = binding.fp8_quantize(x, mode)
+        q, s = binding.fp8_quantize(x, mode, fmt=fmt)
         evs = []
         for i in range(reps + 3):
             evict_caches(flush)
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
-            binding.fp8_quantize(x, mode, q=q, scale=s)
+            binding.fp8_quantize(x, mode, q=q, scale=s, fmt=fmt)
             e1.record()
             if i >= 3:
                 evs.append((e0, e1))
@@ -191,7 +225,7 @@ def quant_results(dev, reps=20):
         t50 = ts[len(ts) // 2] * 1e-3
         nbytes = 3 * rows * cols + 4 * (rows if mode == "rowwise" else 1)
         gbs = nbytes / t50 / 1e9
-        res.append({"workload": f"quantize_e4m3_{mode}_{rows}x{cols}", "rows": rows, "cols": cols,
+        res.append({"workload": f"quantize_{fmt}_{mode}_{rows}x{cols}", "rows": rows, "cols": cols,
                     "us_p50": round(t50 * 1e6, 2), "hbm_gbs": round(gbs, 1),
                     "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)})
         del x, q, s
@@ -311,7 +345,8 @@ def main():
                      "traffic": traffic},
     }
     if not args.no_secondary:
-        line["secondary"] = skinny_results(dev) + gist_results(dev) + quant_results(dev)
+        line["secondary"] = (skinny_results(dev) + gist_results(dev) + ragged_results(dev)
+                             + format_results(dev) + quant_results(dev))
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(probs[0])
     print(json.dumps(line), flush=True)
