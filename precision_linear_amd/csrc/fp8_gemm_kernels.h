@@ -73,8 +73,8 @@ struct LaunchPair {
 constexpr int kFormats = 4;
 
 // The generic kernel's tile configurations, in config-id order:
-// X(name, BM, BN, BK, WAVES_M, WAVES_N, STAGES, MFMA size, GROUP_M).  The
-// ping-pong kernel follows them as the last id.
+// X(name, BM, BN, BK, WAVES_M, WAVES_N, STAGES, MFMA size, GROUP_M).  Ids 0..9
+// are the first list, id 10 is the ping-pong kernel, ids 11.. the second list.
 #define FP8MM_GENERIC_CONFIGS(X)                                                   \
     X("bm128_bn128_bk128_w2x2_s3_mfma32", 128, 128, 128, 2, 2, 3, 32, 8)           \
     X("bm16_bn64_bk256_w1x4_s4_mfma16", 16, 64, 256, 1, 4, 4, 16, 8)               \
@@ -86,8 +86,18 @@ constexpr int kFormats = 4;
     X("bm128_bn128_bk128_w2x2_s4_mfma32", 128, 128, 128, 2, 2, 4, 32, 8)           \
     X("bm128_bn128_bk128_w2x4_s4_mfma32", 128, 128, 128, 2, 4, 4, 32, 8)           \
     X("bm256_bn256_bk128_w2x4_s2_mfma32", 256, 256, 128, 2, 4, 2, 32, 8)
+// Wide tiles for skinny problems (few rows, many columns): less of each
+// workgroup's load traffic goes to the A rows every tile re-reads.
+#define FP8MM_GENERIC_CONFIGS_2(X)                                                 \
+    X("bm16_bn128_bk256_w1x4_s4_mfma16", 16, 128, 256, 1, 4, 4, 16, 8)             \
+    X("bm64_bn256_bk128_w1x8_s3_mfma16", 64, 256, 128, 1, 8, 3, 16, 8)             \
+    X("bm64_bn224_bk128_w1x7_s3_mfma16", 64, 224, 128, 1, 7, 3, 16, 8)             \
+    X("bm128_bn256_bk128_w2x4_s3_mfma32", 128, 256, 128, 2, 4, 3, 32, 8)           \
+    X("bm128_bn224_bk128_w1x7_s3_mfma32", 128, 224, 128, 1, 7, 3, 32, 8)
 constexpr int kNumGenericConfigs = 10;
-constexpr int kNumConfigs = kNumGenericConfigs + 1;
+constexpr int kPingPongId = kNumGenericConfigs;
+constexpr int kNumGenericConfigs2 = 5;
+constexpr int kNumConfigs = kNumGenericConfigs + 1 + kNumGenericConfigs2;
 
 // One table per format pair, defined in fp8_gemm_f<k>.hip.  Not const: a
 // const namespace-scope variable would also be emitted for the device, where
@@ -398,6 +408,68 @@ __device__ __forceinline__ void wait_vmcnt() {
     // expcnt [6:4] and lgkmcnt [11:8] left at their maxima (no wait).
     static_assert(N >= 0 && N <= 63, "vmcnt range");
     __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Split-K partial tiles travel between workgroups, possibly on different XCDs
+// whose L2s are not coherent with each other, as 16-byte buffer stores and
+// loads with the sc1 cache policy (written through the L2, read past it).
+// They are compiler builtins, so the compiler counts them and batches the
+// loads (an atomic load per float would be waited for one by one).
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+constexpr int kPolicyCoherent = 16;   // cache-policy bit sc1
+
+// acc (FN x FM blocks of NACC fp32 per lane) as 16-byte chunks: chunk c holds
+// elements 4g .. 4g+3 of block (i, j), c = (i * FM + j) * (NACC / 4) + g.
+template <int FN, int FM, class A>
+__device__ __forceinline__ v4f acc_chunk(const A (&acc)[FN][FM], int c) {
+    constexpr int G = sizeof(A) / 16;
+    const int i = c / (FM * G), j = (c / G) % FM, g = c % G;
+    return v4f{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+}
+
+template <int FN, int FM, class A>
+__device__ __forceinline__ void acc_chunk_add(A (&acc)[FN][FM], int c, v4f x) {
+    constexpr int G = sizeof(A) / 16;
+    const int i = c / (FM * G), j = (c / G) % FM, g = c % G;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[i][j][4 * g + e] += x[e];
+}
+
+// This thread's share of a partial tile of `bytes` bytes at base: chunk c at
+// byte (c * stride + idx) * 16 (each wave writes and reads 1 KiB runs).
+template <int FN, int FM, class A>
+__device__ __forceinline__ void partial_publish(const A (&acc)[FN][FM], float* base, int stride,
+                                                int idx, uint32_t bytes) {
+    constexpr int NC = FN * FM * (int)(sizeof(A) / 16);
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(base, bytes);
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, acc_chunk<FN, FM>(acc, c)), r,
+                                               (c * stride + idx) * 16, 0, kPolicyCoherent);
+}
+
+// acc += this thread's share of a partial tile (same layout).  Loads go out
+// in batches of up to 16 chunks, all issued before the first add (the
+// scheduling barrier keeps the compiler from trading that for registers by
+// waiting on one load at a time).
+template <int FN, int FM, class A>
+__device__ __forceinline__ void partial_accumulate(A (&acc)[FN][FM], const float* base, int stride,
+                                                   int idx, uint32_t bytes) {
+    constexpr int NC = FN * FM * (int)(sizeof(A) / 16);
+    constexpr int B = NC < 16 ? NC : 16;
+    static_assert(NC % B == 0, "whole batches");
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(base, bytes);
+#pragma unroll
+    for (int b = 0; b < NC; b += B) {
+        v4u x[B];
+#pragma unroll
+        for (int k = 0; k < B; ++k)
+            x[k] = __builtin_amdgcn_raw_buffer_load_b128(r, ((b + k) * stride + idx) * 16, 0,
+                                                         kPolicyCoherent);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int k = 0; k < B; ++k) acc_chunk_add<FN, FM>(acc, b + k, __builtin_bit_cast(v4f, x[k]));
+    }
 }
 
 // Two fp32 -> bf16 conversions, round to nearest even, packed low | high << 16
@@ -826,22 +898,10 @@ fp8_gemm_kernel(Params p) {
         }
 
         if constexpr (C::SPLIT_OK) if (p.splits > 1) {
-            // Publish this unit's partial tile (lane-major, so each store and
-            // load below is a 256-byte run per wave) and count the arrival.
-            // Partials travel with agent-coherent stores and loads (written
-            // through the XCD's L2, read past it), so a unit on one XCD sees
-            // another XCD's partials without writing back or invalidating
-            // whole L2s; the stores have completed (vmcnt 0) before the
-            // arrival is counted.
-            float* mine = p.partials + (size_t)u * (BM * BN);
-#pragma unroll
-            for (int i = 0; i < C::FN; ++i)
-#pragma unroll
-                for (int j = 0; j < C::FM; ++j)
-#pragma unroll
-                    for (int v = 0; v < F::NACC; ++v)
-                        __hip_atomic_store(mine + ((i * C::FM + j) * F::NACC + v) * C::THREADS + tid,
-                                           acc[i][j][v], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            // Publish this unit's partial tile and count the arrival; the
+            // stores have completed (vmcnt 0) before the arrival is counted.
+            partial_publish<C::FN, C::FM>(acc, p.partials + (size_t)u * (BM * BN), C::THREADS, tid,
+                                          BM * BN * 4);
             wait_vmcnt<0>();
             __syncthreads();
             if (tid == 0)
@@ -853,35 +913,16 @@ fp8_gemm_kernel(Params p) {
             if (arrival != (unsigned)(p.splits - 1)) continue;
             if (tid == 0)
                 __hip_atomic_store(&p.counters[t], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            typename F::acc_t sum[C::FN][C::FM];
 #pragma unroll
             for (int i = 0; i < C::FN; ++i)
 #pragma unroll
                 for (int j = 0; j < C::FM; ++j)
 #pragma unroll
-                    for (int v = 0; v < F::NACC; ++v) sum[i][j][v] = 0.f;
+                    for (int v = 0; v < F::NACC; ++v) acc[i][j][v] = 0.f;
             const float* tile_parts = p.partials + (size_t)t * p.splits * (BM * BN);
-            for (int q = 0; q < p.splits; ++q) {
-                const float* part = tile_parts + (size_t)q * (BM * BN);
-#pragma unroll
-                for (int i = 0; i < C::FN; ++i)
-#pragma unroll
-                    for (int j = 0; j < C::FM; ++j)
-#pragma unroll
-                        for (int v = 0; v < F::NACC; ++v) {
-                            const float x =
-                                q == split
-                                    ? acc[i][j][v]
-                                    : __hip_atomic_load(
-                                          part + ((i * C::FM + j) * F::NACC + v) * C::THREADS + tid,
-                                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                            sum[i][j][v] += x;
-                        }
-            }
-#pragma unroll
-            for (int i = 0; i < C::FN; ++i)
-#pragma unroll
-                for (int j = 0; j < C::FM; ++j) acc[i][j] = sum[i][j];
+            for (int q = 0; q < p.splits; ++q)
+                partial_accumulate<C::FN, C::FM>(acc, tile_parts + (size_t)q * (BM * BN), C::THREADS,
+                                                 tid, BM * BN * 4);
         }
 
         // Epilogue parameters into LDS (beside the stage buffers).
@@ -1031,15 +1072,28 @@ __device__ __forceinline__ void pp_compute(v16f (&acc)[pp::FN][pp::FM],
                 acc[i][j] = Mfma<32>::template run<FMT>(fb[ks][i], fa[ks][j], acc[i][j]);
 }
 
+// One work unit: output tile t and its K slices kb .. kb + n - 1 (the whole
+// K range without split-K; one of `splits` consecutive ranges with it).  The
+// unit walks its slices starting at kb + rot and wraps (see the kernel head).
 struct PpTile {
     int row0, col0;
+    int t, kb, n, rot;
     __amdgpu_buffer_rsrc_t ra, rb;
 };
 
-__device__ __forceinline__ PpTile pp_tile(const Params& p, int t, int group_m) {
+__device__ __forceinline__ int pp_slice(const PpTile& T, int step) {
+    const int s = step + T.rot;
+    return T.kb + (s < T.n ? s : s - T.n);
+}
+
+__device__ __forceinline__ PpTile pp_tile(const Params& p, int u, int group_m, int xcd) {
     PpTile T;
+    T.t = u / p.splits;
+    T.kb = (u - T.t * p.splits) * p.k_chunk;
+    T.n = min(p.k_chunk, p.k_iters - T.kb);   // >= 1: the host leaves no empty unit
+    T.rot = xcd * T.n / kXcds;
     int pm, pn;
-    tile_coords(t, p.tiles_m, p.tiles_n, group_m, pm, pn);
+    tile_coords(T.t, p.tiles_m, p.tiles_n, group_m, pm, pn);
     T.row0 = pm * pp::BM;
     T.col0 = pn * pp::BN;
     const uint32_t rows_a = (uint32_t)min(pp::BM, p.M - T.row0);
@@ -1049,17 +1103,18 @@ __device__ __forceinline__ PpTile pp_tile(const Params& p, int t, int group_m) {
     return T;
 }
 
-// A tile's first loads, all from group 0 (wave q): its first K slice (s0)
-// whole and A-top of its second (s1); plus the tile's epilogue parameters (thread q*64 + lane takes row /
-// column q*64 + lane) into the given LDS area.
+// A unit's first loads, all from group 0 (wave q): its first K slice whole
+// and A-top of its second; plus the tile's epilogue parameters (thread
+// q*64 + lane takes row / column q*64 + lane) into the given LDS area.
 __device__ __forceinline__ void pp_tile_start(uint8_t* smem, const Params& p, const PpTile& T,
-                                              const PpLoads& L, int q, int lane, int s0, int s1,
-                                              bool need_epi, bool has_bias, float* epi_sa,
-                                              float* epi_sb, uint16_t* epi_bias) {
+                                              const PpLoads& L, int q, int lane, bool need_epi,
+                                              bool has_bias, float* epi_sa, float* epi_sb,
+                                              uint16_t* epi_bias) {
+    const int s0 = pp_slice(T, 0);
     pp_load_b(smem, 0, q, s0, T.rb, L, p.K);
     pp_load_a_half<false>(smem, 0, q, s0, T.ra, L, p.K);
     pp_load_a_half<true>(smem, 0, q, s0, T.ra, L, p.K);
-    if (p.k_iters > 1) pp_load_a_half<false>(smem, 1, q, s1, T.ra, L, p.K);
+    if (T.n > 1) pp_load_a_half<false>(smem, 1, q, pp_slice(T, 1), T.ra, L, p.K);
     if (need_epi) {
         const int r = q * kWave + lane;   // 0..255
         float pa = 0.f, pb = 0.f;
@@ -1172,6 +1227,39 @@ __device__ __forceinline__ void pp_store(const v16f (&acc)[pp::FN][pp::FM], cons
     }
 }
 
+// Split-K for one wave of the ping-pong kernel.  The wave publishes its fp32
+// partial of unit u (each store is a 1 KiB run) and counts
+// its arrival on the counter of (tile, wave); the wave that arrives last sums
+// the partials of all the tile's units in split order into acc (the same sum
+// whatever the arrival order) and returns true: it runs the epilogue.  The
+// other waves return false.  Partials travel with agent-coherent stores and
+// loads (through the XCD's L2 to memory and back), and the stores have
+// completed (vmcnt 0) before the arrival is counted.  The last wave leaves
+// the counter at zero for the next launch.  Each wave works alone: no
+// workgroup barrier is involved.
+__device__ __forceinline__ bool pp_split_fixup(v16f (&acc)[pp::FN][pp::FM], const Params& p,
+                                               int u, int t, int wave, int lane) {
+    constexpr int PER_WAVE = pp::FN * pp::FM * 16 * kWave;   // floats
+    partial_publish<pp::FN, pp::FM>(acc, p.partials + ((size_t)u * pp::WAVES + wave) * PER_WAVE,
+                                    kWave, lane, PER_WAVE * 4);
+    wait_vmcnt<0>();
+    unsigned* counter = p.counters + (size_t)t * pp::WAVES + wave;
+    unsigned old = 0;
+    if (lane == 0) old = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    old = __builtin_amdgcn_readfirstlane(old);
+    if (old != (unsigned)(p.splits - 1)) return false;
+    if (lane == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+    for (int i = 0; i < pp::FN; ++i)
+#pragma unroll
+        for (int j = 0; j < pp::FM; ++j) acc[i][j] = v16f{};
+    for (int q = 0; q < p.splits; ++q)
+        partial_accumulate<pp::FN, pp::FM>(
+            acc, p.partials + ((size_t)(t * p.splits + q) * pp::WAVES + wave) * PER_WAVE, kWave, lane,
+            PER_WAVE * 4);
+    return true;
+}
+
 template <int GROUP_M, int FMT>
 __global__ void __launch_bounds__(pp::THREADS) fp8_gemm_pp_kernel(Params p) {
     using namespace pp;
@@ -1186,14 +1274,14 @@ __global__ void __launch_bounds__(pp::THREADS) fp8_gemm_pp_kernel(Params p) {
     const int G = gridDim.x;
     int wg = blockIdx.x;
     if (G % kXcds == 0) wg = (blockIdx.x % kXcds) * (G / kXcds) + blockIdx.x / kXcds;
-    if (wg >= p.num_tiles) return;   // whole workgroup
-    // The workgroups of XCD x walk K starting at slice x * k_iters / 8 (and
-    // wrap): the XCDs finish their tiles at different times, so the output
-    // stores of the whole GPU do not all arrive at once.  The 32 workgroups of
-    // one XCD stay in step and keep sharing the slices in its L2.
-    const int k_iters = p.k_iters;
-    const int rot = G % kXcds == 0 ? (int)(blockIdx.x % kXcds) * k_iters / kXcds : 0;
-    auto slice = [&](int step) { return step + rot < k_iters ? step + rot : step + rot - k_iters; };
+    const int num_units = p.num_tiles * p.splits;
+    if (wg >= num_units) return;   // whole workgroup
+    // The workgroups of XCD x walk a unit's K slices starting x/8 of the way
+    // in (and wrap): the XCDs finish their tiles at different times, so the
+    // output stores of the whole GPU do not all arrive at once.  The 32
+    // workgroups of one XCD stay in step and keep sharing the slices in its L2.
+    const int xcd = G % kXcds == 0 ? (int)(blockIdx.x % kXcds) : 0;
+    const bool split = p.splits > 1;
 
     PpLoads L;
     L.cbyte = (uint32_t)(((lane % 8) ^ chunk_swizzle<CPR>((q & 1) * 8 + lane / 8)) * 16);
@@ -1212,18 +1300,18 @@ __global__ void __launch_bounds__(pp::THREADS) fp8_gemm_pp_kernel(Params p) {
     };
 
     int parity = 0;
-    PpTile T = pp_tile(p, wg, GROUP_M);
+    PpTile T = pp_tile(p, wg, GROUP_M, xcd);
     if (grp == 0) {
         float *sa, *sb;
         uint16_t* bias;
         epi_area(0, sa, sb, bias);
-        pp_tile_start(smem, p, T, L, q, lane, slice(0), slice(1), need_epi, has_bias, sa, sb, bias);
+        pp_tile_start(smem, p, T, L, q, lane, need_epi, has_bias, sa, sb, bias);
         wait_vmcnt<0>();
     }
     barrier_lds();
     __builtin_amdgcn_sched_barrier(0);
 
-    for (int t = wg; t < p.num_tiles; t += G, parity ^= 1) {
+    for (int u = wg; u < num_units; u += G, parity ^= 1) {
         v16f acc[FN][FM];
 #pragma unroll
         for (int i = 0; i < FN; ++i)
@@ -1235,10 +1323,10 @@ __global__ void __launch_bounds__(pp::THREADS) fp8_gemm_pp_kernel(Params p) {
         epi_area(parity, epi_sa, epi_sb, epi_bias);
 
         if (grp == 0) {
-            for (int s = 0; s < k_iters; ++s) {
+            for (int s = 0; s < T.n; ++s) {
                 // memory phase 2s: fragments of slice s, B of slice s+1
                 pp_read(fa, fb, smem + (s & 1) * STAGE_BYTES, 0, q, lane);
-                if (s + 1 < k_iters) pp_load_b(smem, (s + 1) & 1, q, slice(s + 1), T.rb, L, p.K);
+                if (s + 1 < T.n) pp_load_b(smem, (s + 1) & 1, q, pp_slice(T, s + 1), T.rb, L, p.K);
                 barrier_lds();
                 __builtin_amdgcn_sched_barrier(0);
                 // compute phase 2s+1
@@ -1248,34 +1336,35 @@ __global__ void __launch_bounds__(pp::THREADS) fp8_gemm_pp_kernel(Params p) {
                 barrier_lds();
                 __builtin_amdgcn_sched_barrier(0);
             }
-            // Between tiles: the next tile's first loads and parameters (every
+            // Between units: the next unit's first loads and parameters (every
             // stage buffer is free: group 1 is in its last compute phase), then
-            // this tile's outputs.
-            const int tn = t + G;
+            // this unit's outputs (with split-K, only from the tile's last
+            // arriving unit).
+            const int un = u + G;
             const PpTile T0 = T;
-            if (tn < p.num_tiles) {
-                T = pp_tile(p, tn, GROUP_M);
+            if (un < num_units) {
+                T = pp_tile(p, un, GROUP_M, xcd);
                 float *sa, *sb;
                 uint16_t* bias;
                 epi_area(parity ^ 1, sa, sb, bias);
-                pp_tile_start(smem, p, T, L, q, lane, slice(0), slice(1), need_epi, has_bias, sa, sb,
-                              bias);
+                pp_tile_start(smem, p, T, L, q, lane, need_epi, has_bias, sa, sb, bias);
             }
-            pp_store(acc, p, T0.row0, T0.col0, 0, q * 64, epi_sa, epi_sb, epi_bias, s_pt, has_bias,
-                     lane, smem + STG0 + q * STG_BYTES);
+            if (!split || pp_split_fixup(acc, p, u, T0.t, wave, lane))
+                pp_store(acc, p, T0.row0, T0.col0, 0, q * 64, epi_sa, epi_sb, epi_bias, s_pt,
+                         has_bias, lane, smem + STG0 + q * STG_BYTES);
             wait_vmcnt<0>();
             barrier_lds();   // pairs with group 1's last barrier of the tile
             __builtin_amdgcn_sched_barrier(0);
         } else {
             __builtin_amdgcn_s_barrier();   // one phase behind group 0
             __builtin_amdgcn_sched_barrier(0);
-            for (int s = 0; s < k_iters; ++s) {
+            for (int s = 0; s < T.n; ++s) {
                 // memory phase 2s+1: fragments of slice s, A-bottom of s+1, A-top of s+2
                 pp_read(fa, fb, smem + (s & 1) * STAGE_BYTES, 1, q, lane);
-                if (s + 1 < k_iters)
-                    pp_load_a_half<true>(smem, (s + 1) & 1, q, slice(s + 1), T.ra, L, p.K);
-                if (s + 2 < k_iters)
-                    pp_load_a_half<false>(smem, s & 1, q, slice(s + 2), T.ra, L, p.K);
+                if (s + 1 < T.n)
+                    pp_load_a_half<true>(smem, (s + 1) & 1, q, pp_slice(T, s + 1), T.ra, L, p.K);
+                if (s + 2 < T.n)
+                    pp_load_a_half<false>(smem, s & 1, q, pp_slice(T, s + 2), T.ra, L, p.K);
                 barrier_lds();
                 __builtin_amdgcn_sched_barrier(0);
                 // compute phase 2s+2
@@ -1285,9 +1374,10 @@ __global__ void __launch_bounds__(pp::THREADS) fp8_gemm_pp_kernel(Params p) {
                 barrier_lds();
                 __builtin_amdgcn_sched_barrier(0);
             }
-            pp_store(acc, p, T.row0, T.col0, 128, q * 64, epi_sa, epi_sb, epi_bias, s_pt, has_bias,
-                     lane, smem + STG1 + q * STG_BYTES);
-            if (t + G < p.num_tiles) T = pp_tile(p, t + G, GROUP_M);
+            if (!split || pp_split_fixup(acc, p, u, T.t, wave, lane))
+                pp_store(acc, p, T.row0, T.col0, 128, q * 64, epi_sa, epi_sb, epi_bias, s_pt,
+                         has_bias, lane, smem + STG1 + q * STG_BYTES);
+            if (u + G < num_units) T = pp_tile(p, u + G, GROUP_M, xcd);
         }
     }
 }
@@ -1322,5 +1412,6 @@ void launch_cfg(const Params& p, dim3 grid, hipStream_t stream) {
     namespace fp8mm {                                                             \
     LaunchPair NAME[kNumConfigs] = {                                              \
         FP8MM_GENERIC_CONFIGS(FP8MM_PAIR_F(FMT))                                  \
-        LaunchPair{&launch_pp<8, FMT>, nullptr}};                                 \
+        LaunchPair{&launch_pp<8, FMT>, nullptr},                                  \
+        FP8MM_GENERIC_CONFIGS_2(FP8MM_PAIR_F(FMT))};                              \
     }

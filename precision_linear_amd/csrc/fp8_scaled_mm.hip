@@ -59,8 +59,9 @@ struct ConfigInfo {
 // Ids are the positions in this table (the C ABI's config_id).
 const ConfigInfo kConfigs[kNumConfigs] = {
     FP8MM_GENERIC_CONFIGS(FP8MM_CFG_INFO)
-    ConfigInfo{"pp_bm256_bn256_bk128_w8_mfma32", pp::BM, pp::BN, pp::BK, false, pp::THREADS,
+    ConfigInfo{"pp_bm256_bn256_bk128_w8_mfma32", pp::BM, pp::BN, pp::BK, true, pp::THREADS,
                pp::LDS_BYTES, 1},
+    FP8MM_GENERIC_CONFIGS_2(FP8MM_CFG_INFO)
 };
 #undef FP8MM_CFG_INFO
 
@@ -72,7 +73,7 @@ constexpr int kSkinny16x112 = 2;      // "bm16_bn112_bk256_w1x7_s4_mfma16"
 constexpr int kSkinny64x112 = 5;      // "bm64_bn112_bk256_w1x7_s3_mfma16"
 constexpr int kSkinny64x64 = 6;       // "bm64_bn64_bk256_w1x4_s4_mfma16"
 constexpr int kSkinny128x128 = 8;     // "bm128_bn128_bk128_w2x4_s4_mfma32"
-constexpr int kPingPongConfig = 10;   // "pp_bm256_bn256_bk128_w8_mfma32"
+constexpr int kPingPongConfig = kPingPongId;   // "pp_bm256_bn256_bk128_w8_mfma32"
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -127,7 +128,12 @@ int validate(const void* A, const void* B, const float* sa, const float* sb, con
 }
 
 // Split-K factor for a configuration: only when the tile grid leaves most of
-// the 256 CUs idle, and never below 8 K slices per split.
+// the 256 CUs idle, and never below 8 K slices per split.  The ping-pong
+// kernel's 256 x 256 fp32 partials (256 KiB per unit, written and read back
+// through memory) cost about as much as 20-30 of its K slices, so it splits
+// at most 3 ways and only into units of at least 40 slices (measured on
+// MI355X: 2304 x 3072 x 12288 goes from 112 to 88 us with 2 units of 48
+// slices, while 8191 x 1000 x 4160 gets slower with 2 units of 17).
 int choose_splits(int cfg, int64_t M, int64_t N, int64_t K) {
     const ConfigInfo& c = kConfigs[cfg];
     if (!c.split_ok) return 1;
@@ -135,8 +141,10 @@ int choose_splits(int cfg, int64_t M, int64_t N, int64_t K) {
     const int64_t k_iters = cdiv(K, c.bk);
     if (tiles >= 160) return 1;
     int64_t s = 256 / tiles;
-    if (s > k_iters / 8) s = k_iters / 8;
-    if (s > 16) s = 16;
+    const bool pp = cfg == kPingPongConfig;
+    const int64_t min_slices = pp ? 40 : 8;
+    if (s > k_iters / min_slices) s = k_iters / min_slices;
+    if (s > (pp ? 3 : 16)) s = pp ? 3 : 16;
     return s < 1 ? 1 : (int)s;
 }
 
@@ -148,12 +156,30 @@ int64_t grid_for(int cfg, int64_t M, int64_t N, int splits, int cus) {
 }
 
 // Workspace layout of a split plan: a fixed block of arrival counters (one per
-// tile, room for kMaxSplitTiles) followed by one fp32 partial tile per work
-// unit.  The counter block sits at the same place for every plan, so a
-// workspace reused by plans of different shapes never finds stale partials
-// where it expects zero counters.
-constexpr int64_t kMaxSplitTiles = 65536;
-constexpr int64_t kCounterBytes = kMaxSplitTiles * 4;
+// tile in the generic kernel, one per tile and wave in the ping-pong kernel,
+// room for kMaxCounters) followed by one fp32 partial tile per work unit.
+// The counter block sits at the same place for every plan, so a workspace
+// reused by plans of different shapes never finds stale partials where it
+// expects zero counters.
+constexpr int64_t kMaxCounters = 65536;
+constexpr int64_t kCounterBytes = kMaxCounters * 4;
+
+int counters_per_tile(int cfg) { return cfg == kPingPongConfig ? pp::WAVES : 1; }
+
+// The split count a plan uses: `requested` (> 0) or the automatic choice,
+// at most the number of K slices, then the smallest count with the same
+// units of ceil(k_iters / splits) slices (so no unit is empty); 1 where the
+// configuration cannot split or its counters would not fit.
+int plan_splits(int cfg, int64_t M, int64_t N, int64_t K, int requested) {
+    const ConfigInfo& c = kConfigs[cfg];
+    const int64_t k_iters = cdiv(K, c.bk);
+    int64_t sp = requested > 0 ? requested : choose_splits(cfg, M, N, K);
+    if (sp > k_iters) sp = k_iters;
+    const int64_t tiles = cdiv(M, c.bm) * cdiv(N, c.bn);
+    if (!c.split_ok || tiles * counters_per_tile(cfg) > kMaxCounters) sp = 1;
+    if (sp > 1) sp = cdiv(k_iters, cdiv(k_iters, sp));
+    return (int)sp;
+}
 
 int64_t workspace_bytes(int cfg, int64_t M, int64_t N, int splits) {
     if (splits <= 1) return 0;
@@ -250,10 +276,8 @@ int fp8_scaled_mm_typed(const void* A, int a_format, const void* B, int b_format
     const int cfg = config_id >= 0 ? config_id : choose_config(M, N, K, mode, bias != nullptr);
     const ConfigInfo& c = kConfigs[cfg];
     const int64_t k_iters = cdiv(K, c.bk);
-    int sp = splits > 0 ? splits : choose_splits(cfg, M, N, K);
-    if (sp > k_iters) sp = (int)k_iters;
+    const int sp = plan_splits(cfg, M, N, K, splits);
     const int64_t tiles = cdiv(M, c.bm) * cdiv(N, c.bn);
-    if (tiles > kMaxSplitTiles || !c.split_ok) sp = 1;
     if (tiles * sp > INT32_MAX) return FP8MM_ERR_SHAPE;
     const int64_t ws_need = workspace_bytes(cfg, M, N, sp);
     if (workspace && workspace_size < ws_need) return FP8MM_ERR_WORKSPACE;
@@ -335,9 +359,7 @@ int fp8_scaled_mm_select_splits(int64_t M, int64_t N, int64_t K, int mode, int h
     if (mode != FP8MM_PER_TENSOR && mode != FP8MM_ROWWISE) return -1;
     if (M <= 0 || N <= 0 || K < 16 || K % 16 != 0 || config_id >= kNumConfigs) return -1;
     const int cfg = config_id >= 0 ? config_id : choose_config(M, N, K, mode, has_bias);
-    const int sp = choose_splits(cfg, M, N, K);
-    const int64_t k_iters = cdiv(K, kConfigs[cfg].bk);
-    return sp > k_iters ? (int)k_iters : sp;
+    return plan_splits(cfg, M, N, K, 0);
 }
 
 int64_t fp8_scaled_mm_workspace_size(int64_t M, int64_t N, int64_t K, int mode, int has_bias,
@@ -345,13 +367,7 @@ int64_t fp8_scaled_mm_workspace_size(int64_t M, int64_t N, int64_t K, int mode, 
     if (mode != FP8MM_PER_TENSOR && mode != FP8MM_ROWWISE) return -1;
     if (M <= 0 || N <= 0 || K < 16 || K % 16 != 0 || config_id >= kNumConfigs) return 0;
     const int cfg = config_id >= 0 ? config_id : choose_config(M, N, K, mode, has_bias);
-    int sp = splits > 0 ? splits : choose_splits(cfg, M, N, K);
-    const int64_t k_iters = cdiv(K, kConfigs[cfg].bk);
-    if (sp > k_iters) sp = (int)k_iters;
-    if (cdiv(M, kConfigs[cfg].bm) * cdiv(N, kConfigs[cfg].bn) > kMaxSplitTiles ||
-        !kConfigs[cfg].split_ok)
-        sp = 1;
-    return workspace_bytes(cfg, M, N, sp);
+    return workspace_bytes(cfg, M, N, plan_splits(cfg, M, N, K, splits));
 }
 
 }  // extern "C"
