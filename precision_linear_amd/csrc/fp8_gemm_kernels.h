@@ -986,7 +986,7 @@ constexpr int MAIN_BYTES = 2 * STAGE_BYTES;
 constexpr int FM = 4, FN = 2;                       // 32 x 32 blocks per wave
 constexpr int KSTEPS = BK / Mfma<32>::KSTEP;        // 2 MFMA K steps per slice
 constexpr int NOFF = 8;                             // load row groups per wave
-constexpr int EPI_BYTES = BM * 4 + BN * 4 + BN * 2; // row scales, column scales, bias
+constexpr int EPI_BYTES = BM * 4 + BN * 4 + 1024;  // row scales, column scales, bias (1 KiB slot)
 // Output staging: group 0's waves use 4 KiB each after the parameters; group 1's
 // waves use the A-bottom part of stage buffer 1, which is idle while they write
 // their outputs (the next tile's first loads fill buffer 0 and buffer 1's A-top).
@@ -1075,6 +1075,17 @@ __device__ __forceinline__ void pp_compute(v16f (&acc)[pp::FN][pp::FM],
 // One work unit: output tile t and its K slices kb .. kb + n - 1 (the whole
 // K range without split-K; one of `splits` consecutive ranges with it).  The
 // unit walks its slices starting at kb + rot and wraps (see the kernel head).
+// This lane's id, recomputed (two VALU instructions) wherever the ping-pong
+// kernel needs it: volatile, so the compiler neither merges the calls nor
+// keeps the value live across the K loop (register pressure there made it
+// spill lane-derived values, and each reload of a spill waited for every
+// outstanding load, next tile's slices included).
+__device__ __forceinline__ int pp_lane() {
+    int l;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+    return l;
+}
+
 struct PpTile {
     int row0, col0;
     int t, kb, n, rot;
@@ -1103,31 +1114,33 @@ __device__ __forceinline__ PpTile pp_tile(const Params& p, int u, int group_m, i
     return T;
 }
 
-// A unit's first loads, all from group 0 (wave q): its first K slice whole
-// and A-top of its second; plus the tile's epilogue parameters (thread
-// q*64 + lane takes row / column q*64 + lane) into the given LDS area.
-__device__ __forceinline__ void pp_tile_start(uint8_t* smem, const Params& p, const PpTile& T,
-                                              const PpLoads& L, int q, int lane, bool need_epi,
+// A unit's epilogue parameters (256 row scales, 256 column scales, 256 bias
+// values) go global -> LDS as three wave-wide 16-byte loads (waves 0, 1, 2 of
+// group 0), like the operand slices: no register holds them and nothing waits
+// for them until the vmcnt waits that cover the slices.  Entries past the
+// last row or column read as zero or as whatever follows in LDS; the
+// epilogue never uses them.  The bias slot is 1 KiB so a full wave fits.
+__device__ __forceinline__ void pp_params_dma(const Params& p, const PpTile& T, int q, int lane,
                                               bool has_bias, float* epi_sa, float* epi_sb,
                                               uint16_t* epi_bias) {
+    const uint32_t off = (uint32_t)lane * 16;
+    if (q == 0 && p.rowwise)
+        dma16(make_rsrc(p.scale_a + T.row0, (uint32_t)min(pp::BM, p.M - T.row0) * 4), epi_sa, off, 0);
+    if (q == 1 && p.rowwise)
+        dma16(make_rsrc(p.scale_b + T.col0, (uint32_t)min(pp::BN, p.N - T.col0) * 4), epi_sb, off, 0);
+    if (q == 2 && has_bias)
+        dma16(make_rsrc(p.bias + T.col0, (uint32_t)min(pp::BN, p.N - T.col0) * 2), epi_bias, off, 0);
+}
+
+// A unit's first loads, all from group 0 (wave q): its first K slice whole
+// and A-top of its second.
+__device__ __forceinline__ void pp_tile_start(uint8_t* smem, const Params& p, const PpTile& T,
+                                              const PpLoads& L, int q) {
     const int s0 = pp_slice(T, 0);
     pp_load_b(smem, 0, q, s0, T.rb, L, p.K);
     pp_load_a_half<false>(smem, 0, q, s0, T.ra, L, p.K);
     pp_load_a_half<true>(smem, 0, q, s0, T.ra, L, p.K);
     if (T.n > 1) pp_load_a_half<false>(smem, 1, q, pp_slice(T, 1), T.ra, L, p.K);
-    if (need_epi) {
-        const int r = q * kWave + lane;   // 0..255
-        float pa = 0.f, pb = 0.f;
-        uint16_t pbias = 0;
-        if (p.rowwise) {
-            pa = T.row0 + r < p.M ? p.scale_a[T.row0 + r] : 0.f;
-            pb = T.col0 + r < p.N ? p.scale_b[T.col0 + r] : 0.f;
-        }
-        if (has_bias && T.col0 + r < p.N) pbias = p.bias[T.col0 + r];
-        epi_sa[r] = pa;
-        epi_sb[r] = pb;
-        epi_bias[r] = pbias;
-    }
 }
 
 // Epilogue of wave (g, q) of the ping-pong kernel through a private 4 KiB LDS
@@ -1197,7 +1210,11 @@ __device__ __forceinline__ void pp_store_staged(const v16f (&acc)[pp::FN][pp::FM
     }
 }
 
-__device__ __forceinline__ void pp_store(const v16f (&acc)[pp::FN][pp::FM], const Params& p,
+// Returns true when it took the staged path, which issues exactly
+// kPpStagedStores global stores (the caller's vmcnt arithmetic relies on it).
+constexpr int kPpStagedStores = pp::FM * 4;
+
+__device__ __forceinline__ bool pp_store(const v16f (&acc)[pp::FN][pp::FM], const Params& p,
                                          int row0, int col0, int mbase, int nbase,
                                          const float* epi_sa, const float* epi_sb,
                                          const uint16_t* epi_bias, float s_pt, bool has_bias,
@@ -1208,7 +1225,7 @@ __device__ __forceinline__ void pp_store(const v16f (&acc)[pp::FN][pp::FM], cons
     if (!full) {
         store_tile<32, pp::FM, pp::FN>(acc, p, row0, col0, mbase, nbase, epi_sa, epi_sb, epi_bias,
                                        s_pt, has_bias, lane);
-        return;
+        return false;
     }
     if (p.rowwise) {
         if (has_bias)
@@ -1225,6 +1242,7 @@ __device__ __forceinline__ void pp_store(const v16f (&acc)[pp::FN][pp::FM], cons
             pp_store_staged<false, false>(acc, p, row0, col0, mbase, nbase, epi_sa, epi_sb,
                                           epi_bias, s_pt, lane, stg);
     }
+    return true;
 }
 
 // Split-K for one wave of the ping-pong kernel.  The wave publishes its fp32
@@ -1305,7 +1323,8 @@ __global__ void __launch_bounds__(pp::THREADS) fp8_gemm_pp_kernel(Params p) {
         float *sa, *sb;
         uint16_t* bias;
         epi_area(0, sa, sb, bias);
-        pp_tile_start(smem, p, T, L, q, lane, need_epi, has_bias, sa, sb, bias);
+        if (need_epi) pp_params_dma(p, T, q, pp_lane(), has_bias, sa, sb, bias);
+        pp_tile_start(smem, p, T, L, q);
         wait_vmcnt<0>();
     }
     barrier_lds();
@@ -1325,7 +1344,7 @@ __global__ void __launch_bounds__(pp::THREADS) fp8_gemm_pp_kernel(Params p) {
         if (grp == 0) {
             for (int s = 0; s < T.n; ++s) {
                 // memory phase 2s: fragments of slice s, B of slice s+1
-                pp_read(fa, fb, smem + (s & 1) * STAGE_BYTES, 0, q, lane);
+                pp_read(fa, fb, smem + (s & 1) * STAGE_BYTES, 0, q, pp_lane());
                 if (s + 1 < T.n) pp_load_b(smem, (s + 1) & 1, q, pp_slice(T, s + 1), T.rb, L, p.K);
                 barrier_lds();
                 __builtin_amdgcn_sched_barrier(0);
@@ -1336,23 +1355,34 @@ __global__ void __launch_bounds__(pp::THREADS) fp8_gemm_pp_kernel(Params p) {
                 barrier_lds();
                 __builtin_amdgcn_sched_barrier(0);
             }
-            // Between units: the next unit's first loads and parameters (every
+            // Between units: the next unit's parameters and first loads (every
             // stage buffer is free: group 1 is in its last compute phase), then
             // this unit's outputs (with split-K, only from the tile's last
-            // arriving unit).
+            // arriving unit).  Nothing waits for the next unit's loads before
+            // the outputs are written, and the final wait lets the output
+            // stores drain: on this architecture vector memory operations
+            // retire in issue order, so "at most kPpStagedStores outstanding"
+            // means every load issued before the stores has landed.
             const int un = u + G;
             const PpTile T0 = T;
             if (un < num_units) {
                 T = pp_tile(p, un, GROUP_M, xcd);
-                float *sa, *sb;
-                uint16_t* bias;
-                epi_area(parity ^ 1, sa, sb, bias);
-                pp_tile_start(smem, p, T, L, q, lane, need_epi, has_bias, sa, sb, bias);
+                if (need_epi) {
+                    float *sa, *sb;
+                    uint16_t* bias;
+                    epi_area(parity ^ 1, sa, sb, bias);
+                    pp_params_dma(p, T, q, pp_lane(), has_bias, sa, sb, bias);
+                }
+                pp_tile_start(smem, p, T, L, q);
             }
-            if (!split || pp_split_fixup(acc, p, u, T0.t, wave, lane))
-                pp_store(acc, p, T0.row0, T0.col0, 0, q * 64, epi_sa, epi_sb, epi_bias, s_pt,
-                         has_bias, lane, smem + STG0 + q * STG_BYTES);
-            wait_vmcnt<0>();
+            bool staged = false;
+            if (!split || pp_split_fixup(acc, p, u, T0.t, wave, pp_lane()))
+                staged = pp_store(acc, p, T0.row0, T0.col0, 0, q * 64, epi_sa, epi_sb, epi_bias,
+                                  s_pt, has_bias, pp_lane(), smem + STG0 + q * STG_BYTES);
+            if (staged)
+                wait_vmcnt<kPpStagedStores>();
+            else
+                wait_vmcnt<0>();
             barrier_lds();   // pairs with group 1's last barrier of the tile
             __builtin_amdgcn_sched_barrier(0);
         } else {
@@ -1360,7 +1390,7 @@ __global__ void __launch_bounds__(pp::THREADS) fp8_gemm_pp_kernel(Params p) {
             __builtin_amdgcn_sched_barrier(0);
             for (int s = 0; s < T.n; ++s) {
                 // memory phase 2s+1: fragments of slice s, A-bottom of s+1, A-top of s+2
-                pp_read(fa, fb, smem + (s & 1) * STAGE_BYTES, 1, q, lane);
+                pp_read(fa, fb, smem + (s & 1) * STAGE_BYTES, 1, q, pp_lane());
                 if (s + 1 < T.n)
                     pp_load_a_half<true>(smem, (s + 1) & 1, q, pp_slice(T, s + 1), T.ra, L, p.K);
                 if (s + 2 < T.n)
@@ -1374,9 +1404,9 @@ __global__ void __launch_bounds__(pp::THREADS) fp8_gemm_pp_kernel(Params p) {
                 barrier_lds();
                 __builtin_amdgcn_sched_barrier(0);
             }
-            if (!split || pp_split_fixup(acc, p, u, T.t, wave, lane))
-                pp_store(acc, p, T.row0, T.col0, 128, q * 64, epi_sa, epi_sb, epi_bias, s_pt,
-                         has_bias, lane, smem + STG1 + q * STG_BYTES);
+            if (!split || pp_split_fixup(acc, p, u, T.t, wave, pp_lane()))
+                (void)pp_store(acc, p, T.row0, T.col0, 128, q * 64, epi_sa, epi_sb, epi_bias, s_pt,
+                               has_bias, pp_lane(), smem + STG1 + q * STG_BYTES);
             if (u + G < num_units) T = pp_tile(p, u + G, GROUP_M, xcd);
         }
     }
