@@ -93,10 +93,11 @@ constexpr int kFormats = 4;
     X("bm64_bn256_bk128_w1x8_s3_mfma16", 64, 256, 128, 1, 8, 3, 16, 8)             \
     X("bm64_bn224_bk128_w1x7_s3_mfma16", 64, 224, 128, 1, 7, 3, 16, 8)             \
     X("bm128_bn256_bk128_w2x4_s3_mfma32", 128, 256, 128, 2, 4, 3, 32, 8)           \
-    X("bm128_bn224_bk128_w1x7_s3_mfma32", 128, 224, 128, 1, 7, 3, 32, 8)
+    X("bm128_bn224_bk128_w1x7_s3_mfma32", 128, 224, 128, 1, 7, 3, 32, 8)           \
+    X("bm128_bn128_bk128_w2x2_s2_mfma32", 128, 128, 128, 2, 2, 2, 32, 8)
 constexpr int kNumGenericConfigs = 10;
 constexpr int kPingPongId = kNumGenericConfigs;
-constexpr int kNumGenericConfigs2 = 5;
+constexpr int kNumGenericConfigs2 = 6;
 constexpr int kNumConfigs = kNumGenericConfigs + 1 + kNumGenericConfigs2;
 
 // One table per format pair, defined in fp8_gemm_f<k>.hip.  Not const: a
@@ -272,6 +273,10 @@ struct Cfg {
     static_assert(CPR == 4 || CPR == 8 || CPR == 16 || CPR == 32, "BK must be 64..512");
     static_assert(A_BYTES % 1024 == 0 && B_BYTES % 1024 == 0, "stages are whole 1 KiB blocks");
     static_assert(LDS_BYTES <= 160 * 1024, "gfx950 LDS is 160 KiB per workgroup");
+    // Workgroups per CU the persistent grid is sized for: two where two fit
+    // in the 160 KiB of LDS (small-K tiles: one workgroup's output stores then
+    // overlap the other's loads), else one.
+    static constexpr int OCCUPANCY = LDS_BYTES * 2 <= 160 * 1024 ? 2 : 1;
     static_assert(STAGES >= 2, "at least double buffering");
     static_assert(BN % 8 == 0 && BM * BN * 2 <= MAIN_BYTES, "the output tile fits the stage buffers");
     static_assert(LOADS * (STAGES - 1) <= 63, "vmcnt counts up to 63");
@@ -772,7 +777,8 @@ __device__ __forceinline__ void run_stage(typename Mfma<C::MI_>::acc_t (&acc)[C:
 
 template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int STAGES, int MI, int GROUP_M,
           bool NT_B, int FMT>
-__global__ void __launch_bounds__(WAVES_M * WAVES_N * kWave)
+__global__ void __launch_bounds__(WAVES_M * WAVES_N * kWave,
+                                  (Cfg<BM, BN, BK, WAVES_M, WAVES_N, STAGES, MI, GROUP_M>::OCCUPANCY))
 fp8_gemm_kernel(Params p) {
     using C = Cfg<BM, BN, BK, WAVES_M, WAVES_N, STAGES, MI, GROUP_M, NT_B, FMT>;
     using F = Mfma<MI>;

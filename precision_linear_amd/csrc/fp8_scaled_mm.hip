@@ -54,7 +54,8 @@ struct ConfigInfo {
 #define FP8MM_CFG_INFO(name, BM, BN, BK, WMW, WNW, ST, MI, GM)                               \
     ConfigInfo{name, BM, BN, BK, Cfg<BM, BN, BK, WMW, WNW, ST, MI, GM>::SPLIT_OK,             \
                Cfg<BM, BN, BK, WMW, WNW, ST, MI, GM>::THREADS,                                \
-               Cfg<BM, BN, BK, WMW, WNW, ST, MI, GM>::LDS_BYTES, 1},
+               Cfg<BM, BN, BK, WMW, WNW, ST, MI, GM>::LDS_BYTES,                              \
+               Cfg<BM, BN, BK, WMW, WNW, ST, MI, GM>::OCCUPANCY},
 
 // Ids are the positions in this table (the C ABI's config_id).
 const ConfigInfo kConfigs[kNumConfigs] = {
@@ -74,13 +75,14 @@ constexpr int kSkinny64x112 = 5;      // "bm64_bn112_bk256_w1x7_s3_mfma16"
 constexpr int kSkinny64x64 = 6;       // "bm64_bn64_bk256_w1x4_s4_mfma16"
 constexpr int kSkinny128x128 = 8;     // "bm128_bn128_bk128_w2x4_s4_mfma32"
 constexpr int kPingPongConfig = kPingPongId;   // "pp_bm256_bn256_bk128_w8_mfma32"
+constexpr int kTwoPerCuConfig = 16;   // "bm128_bn128_bk128_w2x2_s2_mfma32", two workgroups per CU
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 int choose_splits(int cfg, int64_t M, int64_t N, int64_t K);
 
 int choose_config(int64_t M, int64_t N, int64_t K, int mode, int has_bias) {
-    (void)K; (void)mode; (void)has_bias;
+    (void)mode; (void)has_bias;
     // Skinny problems (M <= 128) are HBM-bound on B: tiles as tall as M and
     // 112 columns wide when that gives about one tile per CU (N = 28672 is
     // 256 x 112), else narrower tiles whose K reduction is split until the
@@ -90,12 +92,24 @@ int choose_config(int64_t M, int64_t N, int64_t K, int mode, int has_bias) {
     if (M <= 16) return wide ? kSkinny16x112 : kSkinny16x64;
     if (M <= 64) return wide ? kSkinny64x112 : kSkinny64x64;
     if (M <= 128) return kSkinny128x128;
-    // 256 x 256 tiles on the ping-pong kernel from about 96 tiles on (it beats
-    // 128 x 128 tiles down to there on MI355X even with CUs idle), when rows
-    // of the output allow its 16-byte stores; else 128 x 128 tiles (8 waves),
-    // with split-K when even those leave CUs idle.
+    // Large grids: 256 x 256 tiles on the ping-pong kernel (needs N % 8 == 0
+    // for its 16-byte output rows), also from about 96 tiles on when K is
+    // long enough for it to split K.  Other grids of at least 384 tiles of
+    // 128 x 128: those tiles with two workgroups per CU, so one's stores
+    // overlap the other's loads.  Then the ping-pong kernel down to about 96
+    // tiles (it beats 128 x 128 tiles down to there even with CUs idle), else
+    // 128 x 128 tiles on 8 waves with split-K when they leave CUs idle.  All
+    // from same-box A/B sweeps on MI355X (e.g. 512 x 12288 x 3072: 28.6 us
+    // two-per-CU vs 34.2 us ping-pong; 8191 x 1000 x 4160: 44.5 vs 47.5 us;
+    // 4095 x 4097 x 96: 26.7 vs 29.0 us on 8 waves).
     const int64_t big_tiles = cdiv(M, 256) * cdiv(N, 256);
-    if (big_tiles >= 96 && N % 8 == 0) return kPingPongConfig;
+    const int64_t tiles128 = cdiv(M, 128) * cdiv(N, 128);
+    const bool pp_ok = N % 8 == 0;
+    if (pp_ok && big_tiles >= 192) return kPingPongConfig;
+    if (pp_ok && big_tiles >= 96 && choose_splits(kPingPongConfig, M, N, K) > 1)
+        return kPingPongConfig;
+    if (tiles128 >= 384) return kTwoPerCuConfig;
+    if (pp_ok && big_tiles >= 96) return kPingPongConfig;
     return kMidConfig;
 }
 

@@ -107,7 +107,7 @@ def test_grid_size_is_persistent(L):
     n = L.fp8_scaled_mm_num_configs()
     for c in range(n):
         g = L.fp8_scaled_mm_grid_size(c, 8192, 8192, 256)
-        assert 1 <= g <= 256
+        assert g in (256, 512)        # one or two workgroups per CU
         assert L.fp8_scaled_mm_grid_size(c, 1, 1, 256) == 1
     assert L.fp8_scaled_mm_grid_size(0, 0, 5, 256) == 0
 
