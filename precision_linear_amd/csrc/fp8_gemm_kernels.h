@@ -714,12 +714,20 @@ __device__ __forceinline__ void stage_and_store(
 // every wave's reads of this stage are done and every wave's loads of the next
 // stage have landed), refills this stage's buffer with the slice STAGES ahead,
 // and reads the next stage's first fragments.
+// K offset of logical slice s of a unit that walks its k_iters slices from
+// slice rot on (and wraps).  Past the end (s >= k_iters: dead loads, which
+// read out of range anyway) the value is only kept in range of an int.
+__device__ __forceinline__ int slice_k0(int s, int rot, int k_iters, int bk) {
+    const int x = s + rot;
+    return (x >= k_iters ? x - k_iters : x) * bk;
+}
+
 template <class C, int CUR0, bool HAS_NEXT>
 __device__ __forceinline__ void run_stage(typename Mfma<C::MI_>::acc_t (&acc)[C::FN][C::FM],
                                           v8i (&fa)[2][C::FM], v8i (&fb)[2][C::FN], uint8_t* smem,
                                           int kt, int k_iters, __amdgpu_buffer_rsrc_t ra,
                                           __amdgpu_buffer_rsrc_t rb, int ld, int klim, int wave,
-                                          int wm, int wn, int lane) {
+                                          int wm, int wn, int lane, int rot) {
     using F = Mfma<C::MI_>;
     constexpr int S = C::STAGES_;
     const uint8_t* st = smem + (kt % S) * C::STAGE_BYTES;
@@ -745,7 +753,8 @@ __device__ __forceinline__ void run_stage(typename Mfma<C::MI_>::acc_t (&acc)[C:
                 int l = lane;
                 asm volatile("" : "+v"(l));
                 mfma_with_loads<C, 0>(acc, fa[cur], fb[cur], smem + (kt % S) * C::STAGE_BYTES, ra,
-                                      rb, ld, klim, (kt + S) * C::BK_, wave, l, kt + S < k_iters);
+                                      rb, ld, klim, slice_k0(kt + S, rot, k_iters, C::BK_), wave, l,
+                                      kt + S < k_iters);
                 continue;
             } else {
                 // Memory-bound tiles: the loads go out first, as early as
@@ -758,7 +767,7 @@ __device__ __forceinline__ void run_stage(typename Mfma<C::MI_>::acc_t (&acc)[C:
                 barrier_lds();
                 if (kt + S < k_iters)
                     load_stage<C>(smem + (kt % S) * C::STAGE_BYTES, ra, rb, ld, klim,
-                                  (kt + S) * C::BK_, wave, lane);
+                                  slice_k0(kt + S, rot, k_iters, C::BK_), wave, lane);
                 read_frags<C>(fa[cur ^ 1], fb[cur ^ 1], smem + ((kt + 1) % S) * C::STAGE_BYTES, 0,
                               wm, wn, lane);
             }
@@ -816,6 +825,12 @@ fp8_gemm_kernel(Params p) {
         const int k_iters = max(0, min(p.k_chunk, p.k_iters - kb));
         const int kskip = kb * BK;
         const int klim = p.K - kskip;
+        // With a single row of tiles (the skinny shapes) every workgroup reads
+        // the same A rows while streaming its own B rows: each workgroup
+        // starts at its own K slice (and wraps), so the workgroups of an XCD
+        // do not all ask its L2 for the same lines of A at the same moment.
+        const int rot = (C::STREAM_B && k_iters > 1) ? (int)(((int64_t)wg * k_iters) / G) % k_iters
+                                                      : 0;
         const uint32_t rows_a = (uint32_t)min(BM, p.M - row0);
         const uint32_t rows_b = (uint32_t)min(BN, p.N - col0);
         const __amdgpu_buffer_rsrc_t ra =
@@ -860,7 +875,8 @@ fp8_gemm_kernel(Params p) {
         // slice kt + STAGES once stage kt has been read.
 #pragma unroll
         for (int s = 0; s < STAGES; ++s)
-            load_stage<C>(smem + s * C::STAGE_BYTES, ra, rb, p.K, s < k_iters ? klim : 0, s * BK,
+            load_stage<C>(smem + s * C::STAGE_BYTES, ra, rb, p.K, s < k_iters ? klim : 0,
+                          slice_k0(s, rot, k_iters, BK),
                           wave, lane);
 
         // Software pipeline over K steps: the operand fragments of step q+1 are
@@ -881,24 +897,24 @@ fp8_gemm_kernel(Params p) {
             if constexpr (C::NKS % 2 == 0) {
                 for (; kt + 1 < k_iters; ++kt)
                     run_stage<C, 0, true>(acc, fa, fb, smem, kt, k_iters, ra, rb, p.K, klim, wave, wm,
-                                          wn, lane);
+                                          wn, lane, rot);
                 run_stage<C, 0, false>(acc, fa, fb, smem, kt, k_iters, ra, rb, p.K, klim, wave, wm, wn,
-                                       lane);
+                                       lane, rot);
             } else {
                 for (; kt + 2 < k_iters; kt += 2) {
                     run_stage<C, 0, true>(acc, fa, fb, smem, kt, k_iters, ra, rb, p.K, klim, wave, wm,
-                                          wn, lane);
+                                          wn, lane, rot);
                     run_stage<C, 1, true>(acc, fa, fb, smem, kt + 1, k_iters, ra, rb, p.K, klim, wave,
-                                          wm, wn, lane);
+                                          wm, wn, lane, rot);
                 }
                 if (kt + 1 < k_iters) {
                     run_stage<C, 0, true>(acc, fa, fb, smem, kt, k_iters, ra, rb, p.K, klim, wave, wm,
-                                          wn, lane);
+                                          wn, lane, rot);
                     run_stage<C, 1, false>(acc, fa, fb, smem, kt + 1, k_iters, ra, rb, p.K, klim, wave,
-                                           wm, wn, lane);
+                                           wm, wn, lane, rot);
                 } else {
                     run_stage<C, 0, false>(acc, fa, fb, smem, kt, k_iters, ra, rb, p.K, klim, wave, wm,
-                                           wn, lane);
+                                           wn, lane, rot);
                 }
             }
         }
