@@ -23,11 +23,15 @@
 //     passes run 4 workgroups per CU with several 32-byte groups in flight
 //     per thread (MI355X, 8192 x 8192: amax pass 42 -> 29 us, whole call
 //     84 -> 72 us).
-//   * Both modes spend much of their time in VALU work: the correctly rounded
-//     fp32 division is a dozen instructions per element.
-//   * The division is the correctly rounded fp32 one; the conversion is
-//     v_cvt_pk_fp8_f32 (e4m3) or v_cvt_pk_bf8_f32 (e5m2), round to nearest
-//     even; inputs are already clamped.
+//   * x / scale must be the correctly rounded fp32 quotient (the fp8 rounding
+//     that follows turns a one-ulp difference at a tie into another code).
+//     The IEEE division sequence is a dozen VALU instructions per element,
+//     which made both modes VALU-bound.  The scale is the same for a whole
+//     row (or matrix), so its correctly rounded reciprocal r is computed once
+//     and each element takes a multiply and two residual corrections (Div
+//     below: 5 VALU operations and a sign copy).
+//   * The conversion is v_cvt_pk_fp8_f32 (e4m3) or v_cvt_pk_bf8_f32 (e5m2),
+//     round to nearest even; inputs are already clamped.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -80,32 +84,80 @@ __device__ __forceinline__ float absmax16(const uint4 (&v)[2]) {
     return m;
 }
 
-template <int FMT>
-__device__ __forceinline__ float quant1(float x, float s) {
+// Correctly rounded x / s for many x and one s.
+//
+// r = RN(1/s) (IEEE division, once).  q0 = RN(x r) is within two ulps of x/s;
+// the residual e0 = x - s q0 (one fma) and q1 = RN(q0 + e0 r) bring the
+// quotient within one ulp; then, with r within half an ulp of 1/s and q1
+// within one ulp of x/s, the residual e1 = x - s q1 is exact and
+// RN(q1 + e1 r) = RN(x/s) (P. Markstein, "Computation of elementary functions
+// on the IBM RISC System/6000 processor", IBM J. Res. Dev. 34(1), 1990; the
+// final step of the IA-64 division sequences).  The argument needs the
+// residuals clear of the fp32 subnormal range and r finite, so the sequence
+// is taken only for 2^-60 <= s <= FLT_MAX.  There, every x that can reach a
+// nonzero float8 code (|x/s| >= 2^-17, half the smallest e5m2 subnormal) has
+// |x| >= 2^-77 and normal residuals, so its quotient is RN(x/s) exactly;
+// smaller quotients (subnormal x) may be off in the last fp32 bits but round
+// to +-0 in both formats either way.  Checked exhaustively on MI355X against
+// the IEEE division: every positive finite bf16 amax (s = amax / qmax) times
+// every finite bf16 x with |x| <= amax, both formats: no quotient with
+// |x/s| >= 2^-17 and no float8 code differs.  Elsewhere (s tiny, infinite or
+// NaN) the IEEE division is used.  The sign is copied from x, so -0 stays -0
+// (the corrections would turn it into +0).
+struct Div {
+    float s, r;
+    bool fast;
+};
+
+__device__ __forceinline__ Div make_div(float s) {
+    Div d;
+    d.s = s;
+    d.r = 1.f / s;
+    d.fast = s >= 0x1p-60f && s <= 3.4028234663852886e38f;
+    return d;
+}
+
+__device__ __forceinline__ float div_fast(float x, const Div& d) {
+    float q = x * d.r;
+    float e = fmaf(-d.s, q, x);
+    q = fmaf(e, d.r, q);
+    e = fmaf(-d.s, q, x);
+    q = fmaf(e, d.r, q);
+    return __builtin_copysignf(q, x);
+}
+
+template <int FMT, bool FAST>
+__device__ __forceinline__ float quant1(float x, const Div& d) {
     constexpr float kMax = Fp8Fmt<FMT>::kMax;
-    if (s == 0.f) return 0.f;
-    const float y = x / s;   // correctly rounded fp32 division
+    const float y = FAST ? div_fast(x, d) : x / d.s;
     return fminf(fmaxf(y, -kMax), kMax);
 }
 
 // 16 bf16 values -> 16 float8 codes (one 16-byte vector).
-template <int FMT>
-__device__ __forceinline__ uint4 quant16(const uint4 (&v)[2], float s) {
+template <int FMT, bool FAST>
+__device__ __forceinline__ uint4 quant16_impl(const uint4 (&v)[2], const Div& d) {
     uint32_t out[4];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
         const uint32_t w[4] = {v[h].x, v[h].y, v[h].z, v[h].w};
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
-            int packed = Fp8Fmt<FMT>::template cvt_pk<false>(quant1<FMT>(bf16_lo(w[2 * p]), s),
-                                                             quant1<FMT>(bf16_hi(w[2 * p]), s), 0);
-            packed = Fp8Fmt<FMT>::template cvt_pk<true>(quant1<FMT>(bf16_lo(w[2 * p + 1]), s),
-                                                        quant1<FMT>(bf16_hi(w[2 * p + 1]), s),
+            int packed = Fp8Fmt<FMT>::template cvt_pk<false>(
+                quant1<FMT, FAST>(bf16_lo(w[2 * p]), d), quant1<FMT, FAST>(bf16_hi(w[2 * p]), d), 0);
+            packed = Fp8Fmt<FMT>::template cvt_pk<true>(quant1<FMT, FAST>(bf16_lo(w[2 * p + 1]), d),
+                                                        quant1<FMT, FAST>(bf16_hi(w[2 * p + 1]), d),
                                                         packed);
             out[2 * h + p] = (uint32_t)packed;
         }
     }
     return uint4{out[0], out[1], out[2], out[3]};
+}
+
+// A row (or matrix) whose amax is 0 gets codes 0.
+template <int FMT>
+__device__ __forceinline__ uint4 quant16(const uint4 (&v)[2], const Div& d) {
+    if (d.s == 0.f) return uint4{0u, 0u, 0u, 0u};
+    return d.fast ? quant16_impl<FMT, true>(v, d) : quant16_impl<FMT, false>(v, d);
 }
 
 __device__ __forceinline__ void load16(const uint16_t* p, uint4 (&v)[2]) {
@@ -160,11 +212,12 @@ quant_rowwise_kernel(const uint16_t* __restrict__ x, uint8_t* __restrict__ q, fl
                 if (threadIdx.x + (int64_t)c * kThreads < groups) m = fmaxf(m, absmax16(v[c]));
             const float s = block_max(m, red) / Fp8Fmt<FMT>::kMax;
             if (threadIdx.x == 0) scale[r] = s;
+            const Div d = make_div(s);
             uint8_t* qr = q + r * cols;
 #pragma unroll
             for (int c = 0; c < CHUNKS; ++c) {
                 const int64_t g = threadIdx.x + (int64_t)c * kThreads;
-                if (g < groups) *reinterpret_cast<uint4*>(qr + g * kGroup) = quant16<FMT>(v[c], s);
+                if (g < groups) *reinterpret_cast<uint4*>(qr + g * kGroup) = quant16<FMT>(v[c], d);
             }
 #pragma unroll
             for (int c = 0; c < CHUNKS; ++c) {
@@ -184,10 +237,11 @@ quant_rowwise_kernel(const uint16_t* __restrict__ x, uint8_t* __restrict__ q, fl
             }
             const float s = block_max(m, red) / Fp8Fmt<FMT>::kMax;
             if (threadIdx.x == 0) scale[r] = s;
+            const Div d = make_div(s);
             for (int64_t g = threadIdx.x; g < groups; g += kThreads) {
                 uint4 v[2];
                 load16(xr + g * kGroup, v);
-                *reinterpret_cast<uint4*>(qr + g * kGroup) = quant16<FMT>(v, s);
+                *reinterpret_cast<uint4*>(qr + g * kGroup) = quant16<FMT>(v, d);
             }
         }
     }
@@ -235,7 +289,7 @@ template <int FMT>
 __global__ void __launch_bounds__(kThreads)
 quant_tensor_kernel(const uint16_t* __restrict__ x, uint8_t* __restrict__ q, int64_t groups,
                     const float* slot) {
-    const float s = slot[0] / Fp8Fmt<FMT>::kMax;
+    const Div d = make_div(slot[0] / Fp8Fmt<FMT>::kMax);
     constexpr int U = kQuantUnroll;
     const int64_t stride = (int64_t)gridDim.x * kThreads;
     int64_t g = blockIdx.x * (int64_t)kThreads + threadIdx.x;
@@ -245,12 +299,12 @@ quant_tensor_kernel(const uint16_t* __restrict__ x, uint8_t* __restrict__ q, int
         for (int u = 0; u < U; ++u) load16(x + (g + u * stride) * kGroup, v[u]);
 #pragma unroll
         for (int u = 0; u < U; ++u)
-            *reinterpret_cast<uint4*>(q + (g + u * stride) * kGroup) = quant16<FMT>(v[u], s);
+            *reinterpret_cast<uint4*>(q + (g + u * stride) * kGroup) = quant16<FMT>(v[u], d);
     }
     for (; g < groups; g += stride) {
         uint4 v[2];
         load16(x + g * kGroup, v);
-        *reinterpret_cast<uint4*>(q + g * kGroup) = quant16<FMT>(v, s);
+        *reinterpret_cast<uint4*>(q + g * kGroup) = quant16<FMT>(v, d);
     }
 }
 

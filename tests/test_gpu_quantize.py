@@ -82,6 +82,42 @@ def test_every_finite_bf16_value_with_a_huge_amax(fmt):
     check(bits.reshape(-1, 256), RW, fmt)
 
 
+def _rows_below_amax(amax_bits, cols, seed):
+    """Row r: amax_bits[r] itself, then random bf16 values of either sign whose
+    magnitude patterns are drawn uniformly from [0, amax_bits[r]] (so the row's
+    amax is exactly that value and x / scale sweeps every binade below it,
+    subnormals included)."""
+    rng = np.random.default_rng(seed)
+    out = np.empty((len(amax_bits), cols), np.uint16)
+    for r, a in enumerate(amax_bits):
+        mag = rng.integers(0, int(a) + 1, cols).astype(np.uint16)
+        sign = rng.integers(0, 2, cols).astype(np.uint16) << 15
+        out[r] = mag | sign
+        out[r, 0] = a
+    return out
+
+
+@pytest.mark.parametrize("cols", [8192, 65536])    # rows held in registers / read twice
+@pytest.mark.parametrize("fmt", FMTS)
+def test_division_over_the_scale_range(fmt, cols):
+    # x / scale must be the correctly rounded fp32 quotient for the codes to
+    # match: amax values across the whole positive finite bf16 range (scales
+    # from subnormal to ~2^119), densest around the 2^-60 scale at which the
+    # kernel changes its division method, each with a row of values below it
+    qmax = QMAX[fmt]
+    edge = int(bf16_bits([2.0 ** -60 * qmax])[0])
+    amax = np.unique(np.concatenate([
+        np.linspace(1, 0x7F7F, 40).astype(np.int64),
+        np.arange(edge - 12, edge + 13),
+        bf16_bits([1.0, qmax, 3.0e38, 1e-38, 2.0 ** -126]).astype(np.int64)])).astype(np.uint16)
+    rows = 24 if cols == 65536 else len(amax)
+    sel = amax if rows == len(amax) else amax[np.linspace(0, len(amax) - 1, rows).astype(int)]
+    bits = _rows_below_amax(sel, cols, seed=cols + len(fmt))
+    check(bits, RW, fmt)
+    for a in (sel[0], edge, sel[-1]):     # per-tensor: one scale for the whole matrix
+        check(_rows_below_amax(np.full(4, a, np.uint16), 4096, seed=int(a)), PT, fmt)
+
+
 def test_e5m2_zero_rows_and_signed_zeros():
     x = np.array(_normal(6, 64, 3).view(np.int16), np.int16).view(np.uint16).copy()
     x[1] = 0x0000
