@@ -16,7 +16,10 @@ The JSON line also carries
                 the MALL flushed before every launch, reported in HBM GB/s; the
                 gist's mid-size shape sweep, the ragged shapes and the e5m2 /
                 mixed-format 8192^3 multiplies in TFLOP/s; the quantisers in
-                HBM GB/s.
+                HBM GB/s;
+  vendor        the same operands through torch._scaled_mm (hipBLASLt on ROCm)
+                beside this library's kernel, same timing protocol, for the
+                headline and skinny shapes: context, not part of `value`.
 """
 import argparse
 import hashlib
@@ -197,6 +200,61 @@ def format_results(dev, reps=20):
     return resident_results(dev, names, reps)
 
 
+def vendor_results(dev, reps=20):
+    """torch._scaled_mm (hipBLASLt) on the very operands of the headline and
+    skinny workloads, timed beside this library's launch with the same
+    protocol (skinny: MALL flushed before every launch).  Where hipBLASLt
+    refuses a bias with row-wise scales, both sides run without the bias."""
+    import torch
+    from precision_linear_amd import workloads as wl
+    flush = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
+    names = ["sq8192_pt", "sq8192_rw"] + [n for n in wl.WORKLOADS if n.startswith("skinny")]
+    res = []
+    for name in names:
+        p = Problem(name, dev)
+        fl = flush if name.startswith("skinny") else None
+        a8 = p.a.view(torch.float8_e4m3fn)
+        b8 = p.b.view(torch.float8_e4m3fn)
+        if p.w.mode == wl.ROWWISE:
+            sa, sb = p.sa.view(-1, 1), p.sb.view(1, -1)
+        else:
+            sa, sb = p.sa, p.sb
+        entry = {"workload": name, "library": "torch._scaled_mm (hipBLASLt)"}
+
+        def vendor(bias):
+            return torch._scaled_mm(a8, b8.t(), scale_a=sa, scale_b=sb, bias=bias,
+                                    out_dtype=torch.bfloat16)
+        try:
+            try:
+                ref = vendor(p.bias)
+                use_bias = p.bias
+            except RuntimeError:
+                use_bias = None
+                ref = vendor(None)
+                p.bias = None
+            entry["bias"] = use_bias is not None
+
+            class V:
+                def launch(self):
+                    vendor(use_bias)
+            time_launches(V(), 3, fl)
+            tv = sorted(time_launches(V(), reps, fl))[reps // 2] * 1e-3
+            time_launches(p, 3, fl)
+            to = sorted(time_launches(p, reps, fl))[reps // 2] * 1e-3
+            torch.cuda.synchronize()
+            diff = (ref.float() - p.out.float()).abs().max().item()
+            scale = max(ref.float().abs().max().item(), 1e-30)
+            entry.update({"hipblaslt_us": round(tv * 1e6, 2), "ours_us": round(to * 1e6, 2),
+                          "speedup": round(tv / to, 3),
+                          "max_abs_diff_rel": float(f"{diff / scale:.3g}")})
+        except Exception as e:          # the library or this shape unavailable on the box
+            entry["error"] = f"{type(e).__name__}: {str(e)[:160]}"
+        res.append(entry)
+        del p
+        torch.cuda.empty_cache()
+    return res
+
+
 def quant_results(dev, reps=20):
     """The dynamic e4m3fn quantiser on seeded N(0,1) bf16 matrices (the producer
     of A and scale_a), with the MALL flushed before every launch.  Algorithmic
@@ -347,6 +405,7 @@ def main():
     if not args.no_secondary:
         line["secondary"] = (skinny_results(dev) + gist_results(dev) + ragged_results(dev)
                              + format_results(dev) + quant_results(dev))
+        line["vendor"] = vendor_results(dev)
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(probs[0])
     print(json.dumps(line), flush=True)
