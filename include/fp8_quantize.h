@@ -18,6 +18,8 @@
  *   B stored N x K, as B and scale_b).
  *
  *   x      rows x cols bf16, row-major (row stride cols elements), finite.
+ *          (Outside that contract: a NaN element is skipped by the amax and
+ *          comes out as a NaN code.)
  *   q      rows x cols e4m3fn codes (uint8), row-major.  Written in full.
  *   scale  1 (per-tensor) or rows (row-wise) fp32 values.  Written in full.
  *

@@ -31,7 +31,7 @@
 //     and each element takes a multiply and two residual corrections (Div
 //     below: 5 VALU operations and a sign copy).
 //   * The conversion is v_cvt_pk_fp8_f32 (e4m3) or v_cvt_pk_bf8_f32 (e5m2),
-//     round to nearest even; inputs are already clamped.
+//     round to nearest even; its inputs are within +-qmax (1 + 2^-23).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -102,8 +102,15 @@ __device__ __forceinline__ float absmax16(const uint4 (&v)[2]) {
 // the IEEE division: every positive finite bf16 amax (s = amax / qmax) times
 // every finite bf16 x with |x| <= amax, both formats: no quotient with
 // |x/s| >= 2^-17 and no float8 code differs.  Elsewhere (s tiny, infinite or
-// NaN) the IEEE division is used.  The sign is copied from x, so -0 stays -0
-// (the corrections would turn it into +0).
+// NaN) the IEEE division is used.  The residuals are formed negated,
+// e = s q - x, and subtracted, q - e r: the same values (rounding is
+// symmetric), but x = -0 then gives -0 where x - s q would give +0.
+//
+// On this path the clamp to +-qmax is not needed: |x| <= amax, so the
+// correctly rounded |x/s| is at most qmax (1 + 2^-23), which the float8
+// conversion rounds to qmax (checked in the same exhaustive run, against the
+// clamped IEEE quotient).  A NaN input (amax skips it) stays NaN, as it does
+// through the clamp of the gist's torch code.
 struct Div {
     float s, r;
     bool fast;
@@ -119,18 +126,21 @@ __device__ __forceinline__ Div make_div(float s) {
 
 __device__ __forceinline__ float div_fast(float x, const Div& d) {
     float q = x * d.r;
-    float e = fmaf(-d.s, q, x);
-    q = fmaf(e, d.r, q);
-    e = fmaf(-d.s, q, x);
-    q = fmaf(e, d.r, q);
-    return __builtin_copysignf(q, x);
+    float e = fmaf(d.s, q, -x);
+    q = fmaf(-e, d.r, q);
+    e = fmaf(d.s, q, -x);
+    return fmaf(-e, d.r, q);
 }
 
 template <int FMT, bool FAST>
 __device__ __forceinline__ float quant1(float x, const Div& d) {
     constexpr float kMax = Fp8Fmt<FMT>::kMax;
-    const float y = FAST ? div_fast(x, d) : x / d.s;
-    return fminf(fmaxf(y, -kMax), kMax);
+    if constexpr (FAST) {
+        return div_fast(x, d);
+    } else {
+        const float y = x / d.s;
+        return y != y ? y : fminf(fmaxf(y, -kMax), kMax);   // NaN passes, like torch's clamp
+    }
 }
 
 // 16 bf16 values -> 16 float8 codes (one 16-byte vector).

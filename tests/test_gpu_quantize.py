@@ -118,6 +118,30 @@ def test_division_over_the_scale_range(fmt, cols):
         check(_rows_below_amax(np.full(4, a, np.uint16), 4096, seed=int(a)), PT, fmt)
 
 
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("mode", [PT, RW])
+def test_nan_elements_give_nan_codes(fmt, mode):
+    # outside the finite-input contract: the amax skips a NaN, which comes out
+    # as a NaN code (as through torch's clamp); every other element is
+    # quantised as if the NaN were 0 (which leaves each amax unchanged)
+    bits = _normal(6, 4096, 21)
+    nan_pos = [(0, 5), (2, 4095), (3, 0), (3, 1), (5, 2048)]
+    for r, c in nan_pos:
+        bits[r, c] = 0x7FC0 if c % 2 == 0 else 0xFFC0
+    q, s = run(bits, mode, fmt)
+    clean = bits.copy()
+    for r, c in nan_pos:
+        clean[r, c] = 0
+    rq, rs = oracle.quantize(clean, mode, OFMT[fmt])
+    assert np.array_equal(s.view(np.uint32), rs.view(np.uint32))
+    mask = np.ones(bits.shape, bool)
+    for r, c in nan_pos:
+        mask[r, c] = False
+        code = int(q[r, c]) & 0x7F
+        assert (code == 0x7F) if fmt == "e4m3fn" else (code > 0x7C), hex(q[r, c])
+    assert np.array_equal(q[mask], rq[mask])
+
+
 def test_e5m2_zero_rows_and_signed_zeros():
     x = np.array(_normal(6, 64, 3).view(np.int16), np.int16).view(np.uint16).copy()
     x[1] = 0x0000
