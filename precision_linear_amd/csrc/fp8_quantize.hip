@@ -45,8 +45,8 @@ constexpr int kThreads = 256;
 constexpr int kGroup = 16;                      // elements per thread per chunk
 constexpr int kChunkElems = kThreads * kGroup;  // 4096
 // Per-tensor passes: groups of 16 elements each thread keeps in flight per
-// loop step, and workgroups per CU.  Fewer, busier workgroups also mean fewer
-// atomic maxima on the one amax word.
+// loop step, and workgroups per CU (measured on MI355X, 8192 x 8192: 4, 8,
+// 16 and 32 per CU within 4% of each other, 8 the fastest).
 constexpr int kAmaxUnroll = 4;
 constexpr int kQuantUnroll = 2;
 constexpr int kTensorBlocksPerCu = 8;
