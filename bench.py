@@ -306,6 +306,9 @@ def main():
     ap.add_argument("--profile-flush", action="store_true",
                     help="with --profile-gemm: read a 1 GiB buffer before every launch so "
                          "the operands come from HBM")
+    ap.add_argument("--profile-quant", type=int, default=0, metavar="N",
+                    help="only run each quantiser shape of the secondary list N times, the "
+                         "MALL flushed before every launch (kernel traces)")
     ap.add_argument("--profile-copy-mib", type=int, default=0, metavar="MIB",
                     help="only run one device-to-device copy of MIB MiB (counter calibration)")
     args = ap.parse_args()
@@ -328,6 +331,19 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes": src.numel()}))
+        return
+    if args.profile_quant:
+        flush = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
+        from precision_linear_amd import workloads as wl
+        for rows, cols, mode, fmt in QUANT_SHAPES:
+            bits = wl.bf16_matrix_bits(rows, cols, key=wl.workload_key(f"quant_{rows}x{cols}"))
+            x = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+            q, s = binding.fp8_quantize(x, mode, fmt=fmt)
+            for _ in range(args.profile_quant):
+                evict_caches(flush)
+                binding.fp8_quantize(x, mode, q=q, scale=s, fmt=fmt)
+            torch.cuda.synchronize()
+        print(json.dumps({"quantiser_launches": args.profile_quant, "shapes": len(QUANT_SHAPES)}))
         return
     if args.profile_gemm:
         p = Problem(args.profile_workload, dev)
