@@ -292,13 +292,25 @@ amax_kernel(const uint16_t* __restrict__ x, int64_t groups, float* partial) {
 }
 
 // Per-tensor pass 2 (one workgroup): amax = the maximum of the n partial
-// maxima; scale[0] = amax / qmax.
+// maxima (n <= kReduceMax: at most kReducePerThread per thread, all loaded
+// before any is used, so the pass costs one memory latency); scale[0] =
+// amax / qmax.
+constexpr int kReducePerThread = 16;
+constexpr int kReduceMax = kThreads * kReducePerThread;
+
 template <int FMT>
 __global__ void __launch_bounds__(kThreads)
 amax_reduce_kernel(const float* __restrict__ partial, int n, float* scale) {
     __shared__ float red[kThreads / 64];
+    float v[kReducePerThread];
+#pragma unroll
+    for (int j = 0; j < kReducePerThread; ++j) {
+        const int i = threadIdx.x + j * kThreads;
+        v[j] = i < n ? partial[i] : 0.f;
+    }
     float m = 0.f;
-    for (int i = threadIdx.x; i < n; i += kThreads) m = fmaxf(m, partial[i]);
+#pragma unroll
+    for (int j = 0; j < kReducePerThread; ++j) m = fmaxf(m, v[j]);
     m = block_max(m, red);
     if (threadIdx.x == 0) scale[0] = m / Fp8Fmt<FMT>::kMax;
 }
@@ -387,7 +399,8 @@ int quantize_impl(const void* x, void* q, float* scale, int64_t rows, int64_t co
     } else {
         const int64_t groups = rows * cols / kGroup;
         const int64_t want = (groups + kThreads - 1) / kThreads;
-        const int64_t cap = (int64_t)cus * kTensorBlocksPerCu;
+        int64_t cap = (int64_t)cus * kTensorBlocksPerCu;
+        if (cap > kReduceMax) cap = kReduceMax;   // one partial per thread slot of pass 2
         const unsigned grid = (unsigned)(want < cap ? want : cap);
         // The partial maxima go to the start of q (grid <= ceil(n / 4096)
         // workgroups, 4 bytes each, within q's n bytes), which pass 3 overwrites.
