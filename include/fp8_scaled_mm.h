@@ -39,7 +39,10 @@
  * grown (after synchronising that stream) when a larger one is needed; it is
  * freed only at process exit.  fp8_scaled_mm_with_plan accepts a caller
  * workspace instead and then allocates nothing.  Calls on different streams
- * never share a workspace.
+ * never share a workspace.  The library's own workspace is allocated and
+ * zero-filled (hipMalloc, hipMemset, a device synchronisation) during the
+ * first split call on a stream: code that captures that call into a HIP graph
+ * passes a workspace of its own, or makes one uncaptured call first.
  *
  * Execution: asynchronous on `stream` (a hipStream_t; NULL = the default
  * stream).  The call returns after the launch, without synchronising.
@@ -110,8 +113,9 @@ int fp8_scaled_mm_with_config(const void* A, const void* B, const float* scale_a
  * from the shape), split-K factor (splits == 0: chosen; 1: no split; at most
  * 64, clamped to the number of K slices), and workspace.  With a non-NULL
  * `workspace` (256-byte aligned, at least fp8_scaled_mm_workspace_size()
- * bytes, zero-filled before its first use; every call leaves it zero-filled
- * again) the library allocates nothing; with NULL it uses its own (see the
+ * bytes, zero-filled before its first use: its first 256 KiB are arrival
+ * counters, which every call leaves at zero again; the partial tiles after
+ * them need no initial value) the library allocates nothing; with NULL it uses its own (see the
  * workspace note above).  A caller workspace must not be used by two calls
  * that can run at the same time.  Results do not depend on which workgroup
  * finishes first: partial tiles are summed in split order. */
