@@ -135,6 +135,14 @@ def _as_codes(t: torch.Tensor, name: str, fmt) -> tuple:
     raise ValueError(f"{name} must be float8_e4m3fn, float8_e5m2 or uint8 codes, got {t.dtype}")
 
 
+def _same_device(ref: torch.Tensor, **tensors) -> None:
+    """Every given tensor (None skipped) must live on ref's GPU: the library
+    passes their pointers to kernels on that device."""
+    for name, t in tensors.items():
+        if t is not None and t.device != ref.device:
+            raise ValueError(f"{name} is on {t.device}, expected {ref.device}")
+
+
 def fp8_scaled_mm(a: torch.Tensor, b: torch.Tensor, scale_a: torch.Tensor, scale_b: torch.Tensor,
                   bias: torch.Tensor | None = None, out: torch.Tensor | None = None,
                   mode="per_tensor", config: int = -1, splits: int = 0,
@@ -167,6 +175,7 @@ def fp8_scaled_mm(a: torch.Tensor, b: torch.Tensor, scale_a: torch.Tensor, scale
         raise ValueError("a must be contiguous (row-major M x K)")
     if not (a.is_cuda and b.is_cuda and scale_a.is_cuda and scale_b.is_cuda):
         raise ValueError("all tensors must be on the GPU")
+    _same_device(a, b=b, scale_a=scale_a, scale_b=scale_b, bias=bias, out=out, workspace=workspace)
     for name, s in (("scale_a", scale_a), ("scale_b", scale_b)):
         if s.dtype != torch.float32 or not s.is_contiguous():
             raise ValueError(f"{name} must be contiguous float32")
@@ -216,6 +225,7 @@ def fp8_quantize(x: torch.Tensor, mode="rowwise", q: torch.Tensor | None = None,
         raise ValueError("x must be a contiguous 2-D bf16 GPU tensor")
     rows, cols = x.shape
     n_scale = 1 if m == PER_TENSOR else rows
+    _same_device(x, q=q, scale=scale)
     if q is None:
         q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
     elif q.dtype not in (torch.uint8, torch.float8_e4m3fn if f == E4M3FN else torch.float8_e5m2) \

@@ -384,3 +384,25 @@ def test_split_k_changing_plans_on_one_stream():
         got = out_bits(run_gpu_plan(inp, cfg, splits))
         ref = oracle.scaled_mm(inp.a, inp.b, inp.scale_a, inp.scale_b, None, PT)
         assert compare(got, ref)[0] == 0, (shape, splits)
+
+
+def test_tensors_on_another_device_are_refused():
+    # every pointer goes to a kernel on the operands' GPU: a host tensor
+    # anywhere in the call must be refused before anything is launched
+    inp = wl.make_inputs(64, 96, 128, RW, "codes", bias=True, key=5)
+    a, b = _to_dev(inp.a), _to_dev(inp.b)
+    sa, sb, bias = _to_dev(inp.scale_a), _to_dev(inp.scale_b), _to_dev(inp.bias)
+    cpu_out = torch.empty(64, 96, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        binding.fp8_scaled_mm(a, b, sa, sb, bias, out=cpu_out, mode=RW)
+    with pytest.raises(ValueError):
+        binding.fp8_scaled_mm(a, b, sa, sb, bias.cpu(), mode=RW)
+    with pytest.raises(ValueError):
+        binding.fp8_scaled_mm(a, b, sa, sb, bias, mode=RW, splits=2,
+                              workspace=torch.zeros(1 << 20, dtype=torch.uint8))
+    with pytest.raises(ValueError):
+        binding.fp8_scaled_mm(a, b, sa.cpu(), sb, bias, mode=RW)
+    out = binding.fp8_scaled_mm(a, b, sa, sb, bias, mode=RW)    # and the good call still works
+    torch.cuda.synchronize()
+    nbad, worst, first = compare(out_bits(out), ref_mm(inp))
+    assert nbad == 0

@@ -207,3 +207,14 @@ def test_quantize_then_multiply(mode, fa, fb):
     ref = oracle.scaled_mm(ra, rb, rsa, rsb, None, mode, a_format=OFMT[fa], b_format=OFMT[fb])
     nbad, worst, first = compare(out.view(torch.int16).cpu().numpy().view(np.uint16), ref)
     assert nbad == 0, (nbad, worst, first)
+
+
+def test_outputs_on_another_device_are_refused():
+    x = torch.from_numpy(_normal(8, 64, 4).view(np.int16)).view(torch.bfloat16).to(DEV)
+    with pytest.raises(ValueError):
+        binding.fp8_quantize(x, RW, q=torch.empty(8, 64, dtype=torch.uint8))
+    with pytest.raises(ValueError):
+        binding.fp8_quantize(x, PT, scale=torch.empty(1, dtype=torch.float32))
+    q, s = binding.fp8_quantize(x, RW)
+    torch.cuda.synchronize()
+    assert q.is_cuda and s.is_cuda
