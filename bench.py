@@ -313,8 +313,8 @@ def main():
                     help="only run one device-to-device copy of MIB MiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(the multiply shards by output columns with no exchange; see the design notes)",
+        print("bench.py measures one GPU only: the library has no multi-GPU path (the "
+              "multiply would shard by output columns, with no exchange between GPUs)",
               file=sys.stderr)
         sys.exit(2)
 
