@@ -12,8 +12,9 @@ The JSON line also carries
                 stream) against the dense-FP8 MFMA peak of MI355X;
   cpu_baseline  the CPU oracle timed on a bounded sample (a block of output
                 rows of the same problem) on this host's cores;
-  secondary     the skinny inference shapes (row-wise + bias, HBM-bound) with
-                the MALL flushed before every launch, reported in HBM GB/s; the
+  secondary     the skinny inference shapes (row-wise + bias, HBM-bound) and
+                their 8-way column shards, with the MALL flushed before every
+                launch, reported in HBM GB/s; the
                 gist's mid-size shape sweep, the ragged shapes and the e5m2 /
                 mixed-format 8192^3 multiplies in TFLOP/s; the quantisers in
                 HBM GB/s;
@@ -133,7 +134,7 @@ def skinny_results(dev, reps=20):
     from precision_linear_amd import workloads as wl
     flush = torch.ones(1 << 30, dtype=torch.uint8, device=dev)    # > 256 MB MALL
     res = []
-    for name in [n for n in wl.WORKLOADS if n.startswith("skinny")]:
+    for name in [n for n in wl.WORKLOADS if n.startswith(("skinny", "shard8"))]:
         p = Problem(name, dev)
         time_launches(p, 3, flush)
         ts = sorted(time_launches(p, reps, flush))
@@ -208,11 +209,12 @@ def vendor_results(dev, reps=20):
     import torch
     from precision_linear_amd import workloads as wl
     flush = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
-    names = ["sq8192_pt", "sq8192_rw"] + [n for n in wl.WORKLOADS if n.startswith("skinny")]
+    names = ["sq8192_pt", "sq8192_rw"] + [n for n in wl.WORKLOADS
+                                          if n.startswith(("skinny", "shard8"))]
     res = []
     for name in names:
         p = Problem(name, dev)
-        fl = flush if name.startswith("skinny") else None
+        fl = flush if name.startswith(("skinny", "shard8")) else None
         a8 = p.a.view(torch.float8_e4m3fn)
         b8 = p.b.view(torch.float8_e4m3fn)
         if p.w.mode == wl.ROWWISE:

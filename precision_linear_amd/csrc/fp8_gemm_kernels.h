@@ -87,17 +87,23 @@ constexpr int kFormats = 4;
     X("bm128_bn128_bk128_w2x4_s4_mfma32", 128, 128, 128, 2, 4, 4, 32, 8)           \
     X("bm256_bn256_bk128_w2x4_s2_mfma32", 256, 256, 128, 2, 4, 2, 32, 8)
 // Wide tiles for skinny problems (few rows, many columns): less of each
-// workgroup's load traffic goes to the A rows every tile re-reads.
+// workgroup's load traffic goes to the A rows every tile re-reads.  Then
+// narrow tiles for few rows and few columns (a column shard of a skinny
+// problem), split over K: the last unit of a tile reads every partial, so
+// smaller tiles make that fix-up cheaper.
 #define FP8MM_GENERIC_CONFIGS_2(X)                                                 \
     X("bm16_bn128_bk256_w1x4_s4_mfma16", 16, 128, 256, 1, 4, 4, 16, 8)             \
     X("bm64_bn256_bk128_w1x8_s3_mfma16", 64, 256, 128, 1, 8, 3, 16, 8)             \
     X("bm64_bn224_bk128_w1x7_s3_mfma16", 64, 224, 128, 1, 7, 3, 16, 8)             \
     X("bm128_bn256_bk128_w2x4_s3_mfma32", 128, 256, 128, 2, 4, 3, 32, 8)           \
     X("bm128_bn224_bk128_w1x7_s3_mfma32", 128, 224, 128, 1, 7, 3, 32, 8)           \
-    X("bm128_bn128_bk128_w2x2_s2_mfma32", 128, 128, 128, 2, 2, 2, 32, 8)
+    X("bm128_bn128_bk128_w2x2_s2_mfma32", 128, 128, 128, 2, 2, 2, 32, 8)           \
+    X("bm128_bn32_bk256_w4x2_s3_mfma16", 128, 32, 256, 4, 2, 3, 16, 8)             \
+    X("bm64_bn32_bk256_w4x2_s4_mfma16", 64, 32, 256, 4, 2, 4, 16, 8)               \
+    X("bm128_bn64_bk256_w4x2_s3_mfma16", 128, 64, 256, 4, 2, 3, 16, 8)
 constexpr int kNumGenericConfigs = 10;
 constexpr int kPingPongId = kNumGenericConfigs;
-constexpr int kNumGenericConfigs2 = 6;
+constexpr int kNumGenericConfigs2 = 9;
 constexpr int kNumConfigs = kNumGenericConfigs + 1 + kNumGenericConfigs2;
 
 // One table per format pair, defined in fp8_gemm_f<k>.hip.  Not const: a

@@ -74,6 +74,10 @@ constexpr int kSkinny16x112 = 2;      // "bm16_bn112_bk256_w1x7_s4_mfma16"
 constexpr int kSkinny64x112 = 5;      // "bm64_bn112_bk256_w1x7_s3_mfma16"
 constexpr int kSkinny64x64 = 6;       // "bm64_bn64_bk256_w1x4_s4_mfma16"
 constexpr int kSkinny128x128 = 8;     // "bm128_bn128_bk128_w2x4_s4_mfma32"
+constexpr int kNarrow16x32 = 3;       // "bm16_bn32_bk512_w1x2_s6_mfma16"
+constexpr int kNarrow128x32 = 17;     // "bm128_bn32_bk256_w4x2_s3_mfma16"
+constexpr int kNarrow64x32 = 18;      // "bm64_bn32_bk256_w4x2_s4_mfma16"
+constexpr int kNarrow128x64 = 19;     // "bm128_bn64_bk256_w4x2_s3_mfma16"
 constexpr int kPingPongConfig = kPingPongId;   // "pp_bm256_bn256_bk128_w8_mfma32"
 constexpr int kTwoPerCuConfig = 16;   // "bm128_bn128_bk128_w2x2_s2_mfma32", two workgroups per CU
 
@@ -88,10 +92,21 @@ int choose_config(int64_t M, int64_t N, int64_t K, int mode, int has_bias) {
     // 256 x 112), else narrower tiles whose K reduction is split until the
     // work units fill the CUs (choose_splits).  Chosen from measurements on
     // MI355X of the six skinny inference shapes.
+    // Few columns as well (under 2048, or under 8192 for 128 rows: the
+    // column shards of those shapes over 8 GPUs) take narrower tiles, split
+    // over K: the last unit of a tile sums every partial of it, and with
+    // s splits of a BM x BN tile that fix-up reads s * BM * BN * 4 bytes, so
+    // narrower tiles with more of them make it cheaper (MI355X: M=128,
+    // K=28672, N=1024: 128 x 128 with 16 splits 30.0 us, 128 x 32 with 8
+    // splits 21.8 us).
     const bool wide = cdiv(N, 112) >= 224;
-    if (M <= 16) return wide ? kSkinny16x112 : kSkinny16x64;
-    if (M <= 64) return wide ? kSkinny64x112 : kSkinny64x64;
-    if (M <= 128) return kSkinny128x128;
+    if (M <= 16) return wide ? kSkinny16x112 : (N < 2048 ? kNarrow16x32 : kSkinny16x64);
+    if (M <= 64) return wide ? kSkinny64x112 : (N < 2048 ? kNarrow64x32 : kSkinny64x64);
+    if (M <= 128) {
+        if (N < 2048) return kNarrow128x32;
+        if (N < 8192) return kNarrow128x64;
+        return kSkinny128x128;
+    }
     // Large grids: 256 x 256 tiles on the ping-pong kernel (needs N % 8 == 0
     // for its 16-byte output rows), also from about 96 tiles on when K is
     // long enough for it to split K.  Other grids of at least 384 tiles of

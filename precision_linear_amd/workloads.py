@@ -74,7 +74,8 @@ def _wl(name, M, N, K, mode, recipe, bias=False, a_format="e4m3fn", b_format="e4
 
 
 # The synthetic workloads: square shapes with N(0,1) inputs quantised by amax,
-# skinny inference shapes (activations N(0,1), weights N(0,0.02), bf16 bias),
+# skinny inference shapes (activations N(0,1), weights N(0,0.02), bf16 bias)
+# and their one-in-eight column shards,
 # ragged shapes whose operands are raw e4m3fn codes, and the gist's mid-size
 # shape sweep with N(0,1) inputs.
 WORKLOADS = {w.name: w for w in [
@@ -85,6 +86,11 @@ WORKLOADS = {w.name: w for w in [
 ] + [
     _wl(f"skinny_m{m}_k{k}_n{n}", m, n, k, ROWWISE, "skinny", True)
     for (k, n) in ((8192, 28672), (28672, 8192)) for m in (16, 64, 128)
+] + [
+    # one GPU's share of the skinny shapes when B (and its scales and bias)
+    # is split by output columns over 8 GPUs: N / 8 columns, A replicated
+    _wl(f"shard8_m{m}_k{k}_n{n}", m, n, k, ROWWISE, "skinny", True)
+    for (k, n) in ((8192, 3584), (28672, 1024)) for m in (16, 64, 128)
 ] + [
     _wl(f"ragged_{m}x{n}x{k}_{MODE_NAMES[mode]}", m, n, k, mode, "codes")
     for (m, n, k) in ((4096, 4096, 32), (4095, 4097, 96), (8191, 1000, 4160),
