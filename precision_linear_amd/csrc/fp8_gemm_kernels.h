@@ -483,6 +483,46 @@ __device__ __forceinline__ void partial_accumulate(A (&acc)[FN][FM], const float
     }
 }
 
+// acc += the partial tiles 0 .. splits-1 of one tile (stored one after the
+// other, tile_floats apart, each in the layout above), added in split order.
+// With few chunks per partial (small tiles) the loads of several partials go
+// out together, up to 16 chunks per batch: the sum is the same, and the
+// fix-up costs one memory latency per batch instead of one per partial.
+template <int FN, int FM, class A>
+__device__ __forceinline__ void partial_accumulate_all(A (&acc)[FN][FM], const float* tile_parts,
+                                                       int splits, int tile_floats, int stride,
+                                                       int idx) {
+    constexpr int NC = FN * FM * (int)(sizeof(A) / 16);
+    if constexpr (NC >= 8) {
+        for (int q = 0; q < splits; ++q)
+            partial_accumulate<FN, FM>(acc, tile_parts + (size_t)q * tile_floats, stride, idx,
+                                       (uint32_t)tile_floats * 4);
+    } else {
+        constexpr int QB = 16 / NC;    // partials per batch
+        const __amdgpu_buffer_rsrc_t r =
+            make_rsrc(tile_parts, (uint32_t)splits * (uint32_t)tile_floats * 4);
+        for (int q0 = 0; q0 < splits; q0 += QB) {
+            v4u x[QB][NC];
+#pragma unroll
+            for (int k = 0; k < QB; ++k)
+#pragma unroll
+                for (int c = 0; c < NC; ++c)
+                    x[k][c] = q0 + k < splits
+                                  ? __builtin_amdgcn_raw_buffer_load_b128(
+                                        r, (q0 + k) * tile_floats * 4 + (c * stride + idx) * 16, 0,
+                                        kPolicyCoherent)
+                                  : v4u{0u, 0u, 0u, 0u};
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int k = 0; k < QB; ++k)
+                if (q0 + k < splits)
+#pragma unroll
+                    for (int c = 0; c < NC; ++c)
+                        acc_chunk_add<FN, FM>(acc, c, __builtin_bit_cast(v4f, x[k][c]));
+        }
+    }
+}
+
 // Two fp32 -> bf16 conversions, round to nearest even, packed low | high << 16
 // (one v_cvt_pk_bf16_f32; fp32 denormals are kept, so the bf16 denormal range
 // rounds like the rest).
@@ -947,10 +987,8 @@ fp8_gemm_kernel(Params p) {
                 for (int j = 0; j < C::FM; ++j)
 #pragma unroll
                     for (int v = 0; v < F::NACC; ++v) acc[i][j][v] = 0.f;
-            const float* tile_parts = p.partials + (size_t)t * p.splits * (BM * BN);
-            for (int q = 0; q < p.splits; ++q)
-                partial_accumulate<C::FN, C::FM>(acc, tile_parts + (size_t)q * (BM * BN), C::THREADS,
-                                                 tid, BM * BN * 4);
+            partial_accumulate_all<C::FN, C::FM>(acc, p.partials + (size_t)t * p.splits * (BM * BN),
+                                                 p.splits, BM * BN, C::THREADS, tid);
         }
 
         // Epilogue parameters into LDS (beside the stage buffers).

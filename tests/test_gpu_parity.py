@@ -309,7 +309,9 @@ def _cfg(name):
 @pytest.mark.parametrize("config", ["bm128_bn128_bk128_w2x2_s3_mfma32", "bm16_bn64_bk256_w1x4_s4_mfma16",
                                     "bm64_bn64_bk128_w4x1_s8_mfma16", "bm64_bn112_bk256_w1x7_s3_mfma16",
                                     "bm64_bn64_bk256_w1x4_s4_mfma16", "bm128_bn128_bk128_w2x4_s4_mfma32",
-                                    "pp_bm256_bn256_bk128_w8_mfma32"])
+                                    "pp_bm256_bn256_bk128_w8_mfma32", "bm128_bn32_bk256_w4x2_s3_mfma16",
+                                    "bm64_bn32_bk256_w4x2_s4_mfma16", "bm128_bn64_bk256_w4x2_s3_mfma16",
+                                    "bm16_bn32_bk512_w1x2_s6_mfma16"])
 @pytest.mark.parametrize("splits", [2, 3, 4, 7])
 @pytest.mark.parametrize("mode", [PT, RW])
 @pytest.mark.parametrize("M", [150, 16])
