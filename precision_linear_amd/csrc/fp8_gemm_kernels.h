@@ -493,7 +493,7 @@ __device__ __forceinline__ void partial_accumulate_all(A (&acc)[FN][FM], const f
                                                        int splits, int tile_floats, int stride,
                                                        int idx) {
     constexpr int NC = FN * FM * (int)(sizeof(A) / 16);
-    if constexpr (NC >= 8) {
+    if constexpr (NC > 8) {
         for (int q = 0; q < splits; ++q)
             partial_accumulate<FN, FM>(acc, tile_parts + (size_t)q * tile_floats, stride, idx,
                                        (uint32_t)tile_floats * 4);
