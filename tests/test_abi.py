@@ -224,3 +224,34 @@ def test_quantize_e5m2_rejects_bad_arguments(L, kw, code):
     args.update(kw)
     assert L.fp8_quantize_e5m2(args["x"], args["q"], args["scale"], args["rows"], args["cols"],
                                args["mode"], None) == code
+
+
+# The plans chosen for the benchmarked shapes, each picked from measured
+# sweeps on MI355X: a change to the selection heuristics shows up here.
+PLANS = {
+    (8192, 8192, 8192): ("pp_bm256_bn256_bk128_w8_mfma32", 1),
+    (16, 28672, 8192): ("bm16_bn112_bk256_w1x7_s4_mfma16", 1),
+    (64, 28672, 8192): ("bm64_bn112_bk256_w1x7_s3_mfma16", 1),
+    (128, 28672, 8192): ("bm128_bn128_bk128_w2x4_s4_mfma32", 1),
+    (16, 8192, 28672): ("bm16_bn64_bk256_w1x4_s4_mfma16", 2),
+    (64, 8192, 28672): ("bm64_bn64_bk256_w1x4_s4_mfma16", 2),
+    (128, 8192, 28672): ("bm128_bn128_bk128_w2x4_s4_mfma32", 4),
+    (16, 3584, 8192): ("bm16_bn64_bk256_w1x4_s4_mfma16", 4),
+    (128, 3584, 8192): ("bm128_bn64_bk256_w4x2_s3_mfma16", 4),
+    (16, 1024, 28672): ("bm16_bn32_bk512_w1x2_s6_mfma16", 7),
+    (64, 1024, 28672): ("bm64_bn32_bk256_w4x2_s4_mfma16", 8),
+    (128, 1024, 28672): ("bm128_bn32_bk256_w4x2_s3_mfma16", 8),
+    (512, 12288, 3072): ("bm128_bn128_bk128_w2x2_s2_mfma32", 1),
+    (512, 3072, 12288): ("bm128_bn128_bk128_w2x2_s2_mfma32", 5),
+    (1152, 3072, 12288): ("bm128_bn128_bk128_w2x2_s2_mfma32", 2),
+    (2304, 3072, 12288): ("pp_bm256_bn256_bk128_w8_mfma32", 2),
+    (8191, 1000, 4160): ("bm128_bn128_bk128_w2x2_s2_mfma32", 1),
+}
+
+
+@pytest.mark.parametrize("shape", list(PLANS), ids=[f"{m}x{n}x{k}" for m, n, k in PLANS])
+def test_plans_of_benchmarked_shapes(L, shape):
+    names = binding.config_names()
+    M, N, K = shape
+    cfg = L.fp8_scaled_mm_select_config(M, N, K, 1, 1)
+    assert (names[cfg], L.fp8_scaled_mm_select_splits(M, N, K, 1, 1, -1)) == PLANS[shape]
