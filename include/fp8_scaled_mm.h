@@ -45,7 +45,9 @@
  * passes a workspace of its own, or makes one uncaptured call first.
  *
  * Execution: asynchronous on `stream` (a hipStream_t; NULL = the default
- * stream).  The call returns after the launch, without synchronising.
+ * stream).  The call returns after the launch, without synchronising.  It
+ * launches kernels only (no memset, no allocation once the stream's split-K
+ * workspace exists), so it can be captured into a HIP graph.
  *
  * Preconditions (checked on the host, before anything is enqueued):
  *   - 0 <= M, N <= 2^31 - 1; 16 <= K <= 2^23 and K % 16 == 0 (whole 16-byte
