@@ -408,3 +408,28 @@ def test_tensors_on_another_device_are_refused():
     torch.cuda.synchronize()
     nbad, worst, first = compare(out_bits(out), ref_mm(inp))
     assert nbad == 0
+
+
+def test_split_k_on_two_streams_at_once():
+    # calls on different streams use different library workspaces: split-K
+    # multiplies of different shapes, queued on two streams without any
+    # synchronisation between them, both match the oracle
+    inps = [wl.make_inputs(128, 1024, 4096, RW, "skinny", bias=True, key=61),
+            wl.make_inputs(64, 2048, 6144, PT, "skinny", bias=False, key=62)]
+    args = [[_to_dev(x) for x in (i.a, i.b, i.scale_a, i.scale_b, i.bias)] for i in inps]
+    for i in inps:
+        assert binding.select_splits(*i.shape, i.mode, i.bias is not None) > 1
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = [torch.empty(i.shape[0], i.shape[1], dtype=torch.bfloat16, device="cuda")
+            for i in inps]
+    for s in streams:
+        s.wait_stream(torch.cuda.current_stream())
+    for rep in range(3):
+        for k in (0, 1):
+            with torch.cuda.stream(streams[k]):
+                for _ in range(4):
+                    binding.fp8_scaled_mm(*args[k][:4], args[k][4], out=outs[k], mode=inps[k].mode)
+    torch.cuda.synchronize()
+    for k in (0, 1):
+        nbad, worst, first = compare(out_bits(outs[k]), ref_mm(inps[k]))
+        assert nbad == 0, (k, nbad, worst, first)
