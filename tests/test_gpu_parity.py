@@ -433,3 +433,27 @@ def test_split_k_on_two_streams_at_once():
     for k in (0, 1):
         nbad, worst, first = compare(out_bits(outs[k]), ref_mm(inps[k]))
         assert nbad == 0, (k, nbad, worst, first)
+
+
+@pytest.mark.parametrize("config,splits", [(-1, 0), (10, 1), (8, 1), (2, 1), (8, 3), (16, 2)])
+@pytest.mark.parametrize("mode", [PT, RW])
+def test_nan_codes_propagate(config, splits, mode):
+    # e4m3fn NaN codes (0x7F, 0xFF) in A and B: every output whose dot
+    # product meets one is NaN (the oracle's fp64 sum propagates it), every
+    # other output is unchanged; the comparison demands NaN where the
+    # reference is NaN
+    inp = wl.make_inputs(300, 520, 640, mode, "codes", bias=mode == RW, key=71 + mode)
+    a, b = inp.a.copy(), inp.b.copy()
+    a[5, 17] = 0x7F
+    a[211, 600] = 0xFF
+    b[33, 0] = 0x7F
+    b[519, 639] = 0xFF
+    inp = wl.Inputs(a, b, inp.scale_a, inp.scale_b, inp.bias, mode, "e4m3fn", "e4m3fn")
+    got = out_bits(run_gpu_plan(inp, config, splits))
+    ref = ref_mm(inp)
+    nbad, worst, first = compare(got, ref)
+    assert nbad == 0, (nbad, worst, first)
+    vals = bf16_bits_to_f64(got)
+    assert np.isnan(vals[5]).all() and np.isnan(vals[211]).all()
+    assert np.isnan(vals[:, 33]).all() and np.isnan(vals[:, 519]).all()
+    assert np.isfinite(np.delete(np.delete(vals, [5, 211], 0), [33, 519], 1)).all()
