@@ -1022,10 +1022,14 @@ fp8_gemm_kernel(Params p) {
 // 256 x 256 output tiles, K slices of 128 bytes, 8 waves in two groups of four
 // with one wave of each group on every SIMD (waves w and w+4 share SIMD w).
 // Group 1 runs one phase behind group 0, so on every SIMD one wave issues the
-// 16 MFMAs of a K slice from registers while the other reads its fragments of
-// that slice from LDS and issues global -> LDS loads; at the end of each phase a
-// workgroup barrier swaps the roles.  Wave (g, q) computes rows g*128 .. +128
-// and columns q*64 .. +64 of the tile with fp32 accumulators in registers.
+// 32 MFMAs (16 x 16 x 128) of a K slice from registers while the other reads
+// its fragments of that slice from LDS and issues global -> LDS loads; at the
+// end of each phase a workgroup barrier swaps the roles.  Wave (g, q) computes
+// rows g*128 .. +128 and columns q*64 .. +64 of the tile with fp32 accumulators
+// in registers.  The 16 x 16 x 128 form does the same work per wave as the
+// 32 x 32 x 64 one (same fragment bytes, same 128 accumulators per lane) but
+// draws less power per operation with random operands, so the power-limited
+// shader clock settles higher.
 //
 // Two LDS stage buffers, slice s in buffer s % 2, each holding the slice's A
 // rows 0-127 ("A-top", read only by group 0), A rows 128-255 ("A-bottom", read
@@ -1049,8 +1053,10 @@ constexpr int A_BYTES = BM * BK;                    // 32 KiB
 constexpr int HALF_A = A_BYTES / 2;                 // A-top / A-bottom, 16 KiB
 constexpr int STAGE_BYTES = (BM + BN) * BK;         // 64 KiB
 constexpr int MAIN_BYTES = 2 * STAGE_BYTES;
-constexpr int FM = 4, FN = 2;                       // 32 x 32 blocks per wave
-constexpr int KSTEPS = BK / Mfma<32>::KSTEP;        // 2 MFMA K steps per slice
+constexpr int MI = 16;                              // 16 x 16 x 128 MFMAs
+using acc_t = Mfma<MI>::acc_t;
+constexpr int FM = 128 / MI, FN = 64 / MI;          // MFMA blocks per wave
+constexpr int KSTEPS = BK / Mfma<MI>::KSTEP;        // MFMA K steps per slice
 constexpr int NOFF = 8;                             // load row groups per wave
 constexpr int EPI_BYTES = BM * 4 + BN * 4 + 1024;  // row scales, column scales, bias (1 KiB slot)
 // Output staging: group 0's waves use 4 KiB each after the parameters; group 1's
@@ -1102,31 +1108,32 @@ __device__ __forceinline__ void pp_load_a_half(uint8_t* smem, int buf, int q, in
         pp_dma(ra, st + (q + 4 * i) * 1024, L.off[i] + (BOTTOM ? L.bot : 0u), k0, inside);
 }
 
-// Fragments of one slice for wave (grp, q): A rows grp*128 + j*32 + l, B rows
-// q*64 + i*32 + l; lanes 32..63 take K bytes 32..63 of each 64-byte step.
+// Fragments of one slice for wave (grp, q): A rows grp*128 + j*MI + l, B rows
+// q*64 + i*MI + l with l = lane % MI; lane group lane / MI takes the 32 K bytes
+// 32 * (lane / MI) .. of each K step.
 __device__ __forceinline__ void pp_read(v8i (&fa)[pp::KSTEPS][pp::FM],
                                         v8i (&fb)[pp::KSTEPS][pp::FN], const uint8_t* st, int grp,
                                         int q, int lane) {
     // Addresses are recomputed here from an opaque copy of the lane id: kept
     // live across the loop they would cost registers the fragments need.
-    int l = lane % 32;
-    int lh = lane / 32;
+    int l = lane % pp::MI;
+    int lh = lane / pp::MI;
     asm volatile("" : "+v"(l), "+v"(lh));
 #pragma unroll
     for (int ks = 0; ks < pp::KSTEPS; ++ks) {
-        const int c0 = ks * 4 + lh * 2;
+        const int c0 = ks * (Mfma<pp::MI>::KSTEP / 16) + lh * 2;
 #pragma unroll
         for (int j = 0; j < pp::FM; ++j)
-            fa[ks][j] = read_frag<pp::CPR>(st, grp * 128 + j * 32, l, c0);
+            fa[ks][j] = read_frag<pp::CPR>(st, grp * 128 + j * pp::MI, l, c0);
 #pragma unroll
         for (int i = 0; i < pp::FN; ++i)
-            fb[ks][i] = read_frag<pp::CPR>(st + pp::A_BYTES, q * 64 + i * 32, l, c0);
+            fb[ks][i] = read_frag<pp::CPR>(st + pp::A_BYTES, q * 64 + i * pp::MI, l, c0);
     }
 }
 
-// The 16 MFMAs of one slice, from registers only.
+// The MFMAs of one slice (128 x 64 x 128 per wave), from registers only.
 template <int FMT>
-__device__ __forceinline__ void pp_compute(v16f (&acc)[pp::FN][pp::FM],
+__device__ __forceinline__ void pp_compute(pp::acc_t (&acc)[pp::FN][pp::FM],
                                            const v8i (&fa)[pp::KSTEPS][pp::FM],
                                            const v8i (&fb)[pp::KSTEPS][pp::FN]) {
 #pragma unroll
@@ -1135,7 +1142,7 @@ __device__ __forceinline__ void pp_compute(v16f (&acc)[pp::FN][pp::FM],
         for (int i = 0; i < pp::FN; ++i)
 #pragma unroll
             for (int j = 0; j < pp::FM; ++j)
-                acc[i][j] = Mfma<32>::template run<FMT>(fb[ks][i], fa[ks][j], acc[i][j]);
+                acc[i][j] = Mfma<pp::MI>::template run<FMT>(fb[ks][i], fa[ks][j], acc[i][j]);
 }
 
 // One work unit: output tile t and its K slices kb .. kb + n - 1 (the whole
@@ -1210,67 +1217,78 @@ __device__ __forceinline__ void pp_tile_start(uint8_t* smem, const Params& p, co
 }
 
 // Epilogue of wave (g, q) of the ping-pong kernel through a private 4 KiB LDS
-// area: each 32 x 64 block row of its outputs is written to LDS in the MFMA
-// layout (row l % 32, 4 columns per lane) and read back as 8 rows x 128 bytes
-// per instruction, so every global store writes 8 whole 128-byte lines
-// (instead of 32 pieces of 16 bytes).  LDS operations of one wave complete in
-// order, so no barrier is needed.  In the LDS area, 16-byte chunk c of row r
-// sits at c ^ ((r >> 1) & 7) (at most 2-way bank conflicts on the writes).
-// Falls back to store_tile where the block is not wholly inside the output or
-// 16-byte stores are not allowed.
+// area: each band of 32 x 64 outputs is written to LDS in the MFMA layout (a
+// lane holds runs of 4 consecutive columns of one row) and read back as 8 rows
+// x 128 bytes per instruction, so every global store writes 8 whole 128-byte
+// lines (instead of 32 pieces of 16 bytes).  LDS operations of one wave
+// complete in order, so no barrier is needed.  In the LDS area, 16-byte chunk c
+// of row r sits at c ^ ((r >> 1) & 7) (at most 2-way bank conflicts on the
+// writes).  Falls back to store_tile where the block is not wholly inside the
+// output or 16-byte stores are not allowed.
 template <bool RW, bool BIAS>
-__device__ __forceinline__ void pp_store_staged(const v16f (&acc)[pp::FN][pp::FM], const Params& p,
-                                                int row0, int col0, int mbase, int nbase,
-                                                const float* epi_sa, const float* epi_sb,
-                                                const uint16_t* epi_bias, float s_pt, int lane,
-                                                uint8_t* stg) {
-    constexpr int FM = pp::FM, FN = pp::FN;
+__device__ __forceinline__ void pp_store_staged(const pp::acc_t (&acc)[pp::FN][pp::FM],
+                                                const Params& p, int row0, int col0, int mbase,
+                                                int nbase, const float* epi_sa,
+                                                const float* epi_sb, const uint16_t* epi_bias,
+                                                float s_pt, int lane, uint8_t* stg) {
+    constexpr int MI = pp::MI, FM = pp::FM, FN = pp::FN;
+    constexpr int G = Mfma<MI>::NACC / 4;   // runs of 4 columns per block and lane
+    constexpr int JB = 32 / MI;             // MFMA row blocks per 32-row band
+    // Column, within the wave's 64, of run g of block i for this lane.
+    auto col = [&](int i, int g) {
+        return i * MI + (MI == 32 ? 8 * g + 4 * (lane / 32) : 4 * (lane / 16));
+    };
     float sa_r[FM];
-    v4f sb_r[FN][4];
-    uint2 b_r[FN][4];
-    const int h = lane / 32;
+    v4f sb_r[FN][G];
+    uint2 b_r[FN][G];
 #pragma unroll
-    for (int j = 0; j < FM; ++j) sa_r[j] = RW ? epi_sa[mbase + j * 32 + lane % 32] : s_pt;
+    for (int j = 0; j < FM; ++j) sa_r[j] = RW ? epi_sa[mbase + j * MI + lane % MI] : s_pt;
 #pragma unroll
     for (int i = 0; i < FN; ++i)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const int nl = nbase + i * 32 + 8 * g + 4 * h;
+        for (int g = 0; g < G; ++g) {
+            const int nl = nbase + col(i, g);
             if constexpr (RW) sb_r[i][g] = *reinterpret_cast<const v4f*>(epi_sb + nl);
             if constexpr (BIAS) b_r[i][g] = *reinterpret_cast<const uint2*>(epi_bias + nl);
         }
-    const int r = lane % 32;
 #pragma unroll
-    for (int j = 0; j < FM; ++j) {
+    for (int band = 0; band < FM / JB; ++band) {
 #pragma unroll
-        for (int i = 0; i < FN; ++i)
+        for (int jj = 0; jj < JB; ++jj) {
+            const int j = band * JB + jj;
+            const int r = jj * MI + lane % MI;
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                float y[4];
+            for (int i = 0; i < FN; ++i)
 #pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    const float sc = RW ? sa_r[j] * sb_r[i][g][c] : s_pt;
-                    const float v = acc[i][j][4 * g + c];
-                    if constexpr (BIAS) {
-                        const uint32_t bw = c < 2 ? b_r[i][g].x : b_r[i][g].y;
-                        const float bv = __uint_as_float(c % 2 == 0 ? bw << 16 : bw & 0xffff0000u);
-                        y[c] = __builtin_fmaf(v, sc, bv);
-                    } else {
-                        y[c] = v * sc;
+                for (int g = 0; g < G; ++g) {
+                    float y[4];
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        const float sc = RW ? sa_r[j] * sb_r[i][g][c] : s_pt;
+                        const float v = acc[i][j][4 * g + c];
+                        if constexpr (BIAS) {
+                            const uint32_t bw = c < 2 ? b_r[i][g].x : b_r[i][g].y;
+                            const float bv =
+                                __uint_as_float(c % 2 == 0 ? bw << 16 : bw & 0xffff0000u);
+                            y[c] = __builtin_fmaf(v, sc, bv);
+                        } else {
+                            y[c] = v * sc;
+                        }
                     }
+                    uint2 w;
+                    w.x = pack_bf16x2(y[0], y[1]);
+                    w.y = pack_bf16x2(y[2], y[3]);
+                    const int cl = col(i, g);
+                    const int cpos = (cl / 8) ^ ((r >> 1) & 7);
+                    *reinterpret_cast<uint2*>(stg + r * 128 + cpos * 16 + (cl % 8) * 2) = w;
                 }
-                uint2 w;
-                w.x = pack_bf16x2(y[0], y[1]);
-                w.y = pack_bf16x2(y[2], y[3]);
-                const int cpos = (i * 4 + g) ^ ((r >> 1) & 7);
-                *reinterpret_cast<uint2*>(stg + r * 128 + cpos * 16 + h * 8) = w;
-            }
+        }
 #pragma unroll
         for (int pass = 0; pass < 4; ++pass) {
             const int rr = pass * 8 + lane / 8;
             const int cc = lane % 8;
             const v4i v = *reinterpret_cast<const v4i*>(stg + rr * 128 + ((cc ^ ((rr >> 1) & 7)) * 16));
-            uint16_t* dst = p.out + (size_t)(row0 + mbase + j * 32 + rr) * p.N + col0 + nbase + cc * 8;
+            uint16_t* dst = p.out + (size_t)(row0 + mbase + band * 32 + rr) * p.N + col0 + nbase + cc * 8;
             *reinterpret_cast<v4i*>(dst) = v;
         }
     }
@@ -1278,18 +1296,18 @@ __device__ __forceinline__ void pp_store_staged(const v16f (&acc)[pp::FN][pp::FM
 
 // Returns true when it took the staged path, which issues exactly
 // kPpStagedStores global stores (the caller's vmcnt arithmetic relies on it).
-constexpr int kPpStagedStores = pp::FM * 4;
+constexpr int kPpStagedStores = (128 / 32) * 4;   // 4 bands of 4 passes
 
-__device__ __forceinline__ bool pp_store(const v16f (&acc)[pp::FN][pp::FM], const Params& p,
+__device__ __forceinline__ bool pp_store(const pp::acc_t (&acc)[pp::FN][pp::FM], const Params& p,
                                          int row0, int col0, int mbase, int nbase,
                                          const float* epi_sa, const float* epi_sb,
                                          const uint16_t* epi_bias, float s_pt, bool has_bias,
                                          int lane, uint8_t* stg) {
     asm volatile("" : "+v"(lane));
-    const bool full = p.vec16 && row0 + mbase + pp::FM * 32 <= p.M &&
-                      col0 + nbase + pp::FN * 32 <= p.N;   // wave-uniform
+    const bool full = p.vec16 && row0 + mbase + 128 <= p.M &&
+                      col0 + nbase + 64 <= p.N;   // wave-uniform
     if (!full) {
-        store_tile<32, pp::FM, pp::FN>(acc, p, row0, col0, mbase, nbase, epi_sa, epi_sb, epi_bias,
+        store_tile<pp::MI, pp::FM, pp::FN>(acc, p, row0, col0, mbase, nbase, epi_sa, epi_sb, epi_bias,
                                        s_pt, has_bias, lane);
         return false;
     }
@@ -1321,9 +1339,9 @@ __device__ __forceinline__ bool pp_store(const v16f (&acc)[pp::FN][pp::FM], cons
 // completed (vmcnt 0) before the arrival is counted.  The last wave leaves
 // the counter at zero for the next launch.  Each wave works alone: no
 // workgroup barrier is involved.
-__device__ __forceinline__ bool pp_split_fixup(v16f (&acc)[pp::FN][pp::FM], const Params& p,
+__device__ __forceinline__ bool pp_split_fixup(pp::acc_t (&acc)[pp::FN][pp::FM], const Params& p,
                                                int u, int t, int wave, int lane) {
-    constexpr int PER_WAVE = pp::FN * pp::FM * 16 * kWave;   // floats
+    constexpr int PER_WAVE = 128 * 64;   // floats: the wave's 128 x 64 outputs
     partial_publish<pp::FN, pp::FM>(acc, p.partials + ((size_t)u * pp::WAVES + wave) * PER_WAVE,
                                     kWave, lane, PER_WAVE * 4);
     wait_vmcnt<0>();
@@ -1336,7 +1354,7 @@ __device__ __forceinline__ bool pp_split_fixup(v16f (&acc)[pp::FN][pp::FM], cons
 #pragma unroll
     for (int i = 0; i < pp::FN; ++i)
 #pragma unroll
-        for (int j = 0; j < pp::FM; ++j) acc[i][j] = v16f{};
+        for (int j = 0; j < pp::FM; ++j) acc[i][j] = pp::acc_t{};
     for (int q = 0; q < p.splits; ++q)
         partial_accumulate<pp::FN, pp::FM>(
             acc, p.partials + ((size_t)(t * p.splits + q) * pp::WAVES + wave) * PER_WAVE, kWave, lane,
@@ -1397,11 +1415,11 @@ __global__ void __launch_bounds__(pp::THREADS) fp8_gemm_pp_kernel(Params p) {
     __builtin_amdgcn_sched_barrier(0);
 
     for (int u = wg; u < num_units; u += G, parity ^= 1) {
-        v16f acc[FN][FM];
+        acc_t acc[FN][FM];
 #pragma unroll
         for (int i = 0; i < FN; ++i)
 #pragma unroll
-            for (int j = 0; j < FM; ++j) acc[i][j] = v16f{};
+            for (int j = 0; j < FM; ++j) acc[i][j] = acc_t{};
         v8i fa[KSTEPS][FM], fb[KSTEPS][FN];
         float *epi_sa, *epi_sb;
         uint16_t* epi_bias;

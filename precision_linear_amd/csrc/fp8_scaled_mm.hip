@@ -60,7 +60,7 @@ struct ConfigInfo {
 // Ids are the positions in this table (the C ABI's config_id).
 const ConfigInfo kConfigs[kNumConfigs] = {
     FP8MM_GENERIC_CONFIGS(FP8MM_CFG_INFO)
-    ConfigInfo{"pp_bm256_bn256_bk128_w8_mfma32", pp::BM, pp::BN, pp::BK, true, pp::THREADS,
+    ConfigInfo{"pp_bm256_bn256_bk128_w8_mfma16", pp::BM, pp::BN, pp::BK, true, pp::THREADS,
                pp::LDS_BYTES, 1},
     FP8MM_GENERIC_CONFIGS_2(FP8MM_CFG_INFO)
 };
@@ -78,7 +78,7 @@ constexpr int kNarrow16x32 = 3;       // "bm16_bn32_bk512_w1x2_s6_mfma16"
 constexpr int kNarrow128x32 = 17;     // "bm128_bn32_bk256_w4x2_s3_mfma16"
 constexpr int kNarrow64x32 = 18;      // "bm64_bn32_bk256_w4x2_s4_mfma16"
 constexpr int kNarrow128x64 = 19;     // "bm128_bn64_bk256_w4x2_s3_mfma16"
-constexpr int kPingPongConfig = kPingPongId;   // "pp_bm256_bn256_bk128_w8_mfma32"
+constexpr int kPingPongConfig = kPingPongId;   // "pp_bm256_bn256_bk128_w8_mfma16"
 constexpr int kTwoPerCuConfig = 16;   // "bm128_bn128_bk128_w2x2_s2_mfma32", two workgroups per CU
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }

@@ -229,7 +229,7 @@ def test_quantize_e5m2_rejects_bad_arguments(L, kw, code):
 # The plans chosen for the benchmarked shapes, each picked from measured
 # sweeps on MI355X: a change to the selection heuristics shows up here.
 PLANS = {
-    (8192, 8192, 8192): ("pp_bm256_bn256_bk128_w8_mfma32", 1),
+    (8192, 8192, 8192): ("pp_bm256_bn256_bk128_w8_mfma16", 1),
     (16, 28672, 8192): ("bm16_bn112_bk256_w1x7_s4_mfma16", 1),
     (64, 28672, 8192): ("bm64_bn112_bk256_w1x7_s3_mfma16", 1),
     (128, 28672, 8192): ("bm128_bn128_bk128_w2x4_s4_mfma32", 1),
@@ -244,7 +244,7 @@ PLANS = {
     (512, 12288, 3072): ("bm128_bn128_bk128_w2x2_s2_mfma32", 1),
     (512, 3072, 12288): ("bm128_bn128_bk128_w2x2_s2_mfma32", 5),
     (1152, 3072, 12288): ("bm128_bn128_bk128_w2x2_s2_mfma32", 2),
-    (2304, 3072, 12288): ("pp_bm256_bn256_bk128_w8_mfma32", 2),
+    (2304, 3072, 12288): ("pp_bm256_bn256_bk128_w8_mfma16", 2),
     (8191, 1000, 4160): ("bm128_bn128_bk128_w2x2_s2_mfma32", 1),
 }
 

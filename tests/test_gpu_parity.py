@@ -309,7 +309,7 @@ def _cfg(name):
 @pytest.mark.parametrize("config", ["bm128_bn128_bk128_w2x2_s3_mfma32", "bm16_bn64_bk256_w1x4_s4_mfma16",
                                     "bm64_bn64_bk128_w4x1_s8_mfma16", "bm64_bn112_bk256_w1x7_s3_mfma16",
                                     "bm64_bn64_bk256_w1x4_s4_mfma16", "bm128_bn128_bk128_w2x4_s4_mfma32",
-                                    "pp_bm256_bn256_bk128_w8_mfma32", "bm128_bn32_bk256_w4x2_s3_mfma16",
+                                    "pp_bm256_bn256_bk128_w8_mfma16", "bm128_bn32_bk256_w4x2_s3_mfma16",
                                     "bm64_bn32_bk256_w4x2_s4_mfma16", "bm128_bn64_bk256_w4x2_s3_mfma16",
                                     "bm16_bn32_bk512_w1x2_s6_mfma16"])
 @pytest.mark.parametrize("splits", [2, 3, 4, 7])
@@ -331,7 +331,7 @@ def test_split_k_ping_pong_full_tiles(splits, mode):
     # whole 256 x 256 tiles (16-byte staged stores) plus a ragged edge tile,
     # K = 4160: 33 slices, so the units have 17 + 16 or 11 + 11 + 11 slices
     inp = wl.make_inputs(520, 768, 4160, mode, "codes", bias=mode == RW, key=40 + splits + mode)
-    pp = _cfg("pp_bm256_bn256_bk128_w8_mfma32")
+    pp = _cfg("pp_bm256_bn256_bk128_w8_mfma16")
     got = out_bits(run_gpu_plan(inp, pp, splits))
     nbad, worst, first = compare(got, ref_mm(inp))
     assert nbad == 0, (nbad, worst, first)
