@@ -8,19 +8,20 @@
 // pytorch PR #125204, Summary; the bias epilogue from PR #142045, Summary.
 //
 // Structure of one launch (all of it gfx950-specific):
-//   * Persistent grid: at most one workgroup per CU walks the output tiles in
-//     grouped order (GROUP_M tile rows per band, the L2-reuse order the gist
-//     cites from the Triton matmul tutorial), with workgroup ids renumbered so
-//     that the workgroups of one XCD take neighbouring tiles and share that
-//     XCD's L2.
+//   * Persistent grid: one workgroup per CU (two where the tile's LDS allows)
+//     walks the output tiles in grouped order (GROUP_M tile rows per band, the
+//     L2-reuse order the gist cites from the Triton matmul tutorial), with
+//     workgroup ids renumbered so that the workgroups of one XCD take
+//     neighbouring tiles and share that XCD's L2.
 //   * Staging: A and B K-slices go global -> LDS with 16-byte buffer loads that
 //     write LDS directly (no VGPR round trip).  Rows outside the matrix and the
 //     K tail read as zero: the buffer's record limit covers the rows, and K-tail
 //     chunks get an offset past that limit.  The 16-byte chunks of each LDS row
 //     are XOR-permuted by row so that the MFMA operand reads hit distinct banks.
 //     STAGES buffers rotate so the loads for later K slices run under the MFMAs.
-//   * Inner loop: v_mfma_f32_32x32x64_f8f6f4 (or 16x16x128) with e4m3 operands
-//     and fp32 accumulators held in registers for the whole K loop.
+//   * Inner loop: v_mfma_f32_16x16x128_f8f6f4 (ping-pong kernel, skinny and
+//     narrow tiles) or 32x32x64 (the other tiles) with e4m3 / e5m2 operands and
+//     fp32 accumulators held in registers for the whole K loop.
 //   * Epilogue: scale (fp32 sa*sb in both modes), optional bias, RNE to bf16,
 //     then the bf16 tile goes through LDS so that the stores to the output
 //     write whole runs of its rows (16, 4 or 2 bytes per lane, as wide as the
