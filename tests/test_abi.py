@@ -255,3 +255,40 @@ def test_plans_of_benchmarked_shapes(L, shape):
     M, N, K = shape
     cfg = L.fp8_scaled_mm_select_config(M, N, K, 1, 1)
     assert (names[cfg], L.fp8_scaled_mm_select_splits(M, N, K, 1, 1, -1)) == PLANS[shape]
+
+
+def _imported_modules(path):
+    import ast
+    tree = ast.parse(open(path).read(), filename=path)
+    for node in ast.walk(tree):
+        if isinstance(node, ast.Import):
+            yield from (a.name for a in node.names)
+        elif isinstance(node, ast.ImportFrom):
+            yield node.module or ""
+
+
+def test_product_package_never_imports_the_oracle():
+    """The oracle is test infrastructure: no module of the package (the path
+    every multiply takes) imports it, so no result can come from it."""
+    pkg = os.path.join(ROOT, "precision_linear_amd")
+    checked = 0
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith(".py"):
+                mods = list(_imported_modules(os.path.join(dirpath, f)))
+                assert not any(m == "oracle" or m.startswith("oracle.") for m in mods), f
+                checked += 1
+    assert checked >= 4
+    for f in os.listdir(os.path.join(pkg, "csrc")):
+        text = open(os.path.join(pkg, "csrc", f)).read()
+        assert "oracle" not in text, f
+
+
+def test_missing_library_is_an_error(monkeypatch):
+    """Without the HIP library the binding raises instead of computing anything."""
+    monkeypatch.setattr(binding, "_lib", None)
+    monkeypatch.setattr(binding, "library_path", os.path.join(ROOT, "no_such_dir", "lib.so"))
+    with pytest.raises(RuntimeError, match="no non-HIP fallback"):
+        binding.lib()
+    with pytest.raises(RuntimeError, match="missing"):
+        binding.select_config(64, 64, 64, "per_tensor")
