@@ -1042,9 +1042,11 @@ fp8_gemm_kernel(Params p) {
 //                         slice s+2             (last read in 2s)
 // and each wave waits for its own loads (vmcnt 0) at the end of its next
 // compute phase, before the barrier after which the data is first read.
-// Between tiles, group 0 issues the next tile's first slices and its
-// epilogue parameters right after its last compute phase, then writes its
-// outputs while group 1 finishes.
+// Between tiles, group 0 writes its outputs while group 1 runs its last
+// compute phase, group 1 then writes its outputs, and only after both have
+// issued their stores does group 0 issue the next tile's first slices and
+// epilogue parameters (stores issued behind loads that miss the caches would
+// wait for them in the CU's in-order memory queue).
 namespace pp {
 constexpr int BM = 256, BN = 256, BK = 128;
 constexpr int WAVES = 8;
@@ -1295,11 +1297,9 @@ __device__ __forceinline__ void pp_store_staged(const pp::acc_t (&acc)[pp::FN][p
     }
 }
 
-// Returns true when it took the staged path, which issues exactly
-// kPpStagedStores global stores (the caller's vmcnt arithmetic relies on it).
-constexpr int kPpStagedStores = (128 / 32) * 4;   // 4 bands of 4 passes
-
-__device__ __forceinline__ bool pp_store(const pp::acc_t (&acc)[pp::FN][pp::FM], const Params& p,
+// One wave's 128 x 64 outputs: staged through LDS where the block lies wholly
+// inside the output and rows allow 16-byte stores, else store_tile.
+__device__ __forceinline__ void pp_store(const pp::acc_t (&acc)[pp::FN][pp::FM], const Params& p,
                                          int row0, int col0, int mbase, int nbase,
                                          const float* epi_sa, const float* epi_sb,
                                          const uint16_t* epi_bias, float s_pt, bool has_bias,
@@ -1310,7 +1310,7 @@ __device__ __forceinline__ bool pp_store(const pp::acc_t (&acc)[pp::FN][pp::FM],
     if (!full) {
         store_tile<pp::MI, pp::FM, pp::FN>(acc, p, row0, col0, mbase, nbase, epi_sa, epi_sb, epi_bias,
                                        s_pt, has_bias, lane);
-        return false;
+        return;
     }
     if (p.rowwise) {
         if (has_bias)
@@ -1327,7 +1327,6 @@ __device__ __forceinline__ bool pp_store(const pp::acc_t (&acc)[pp::FN][pp::FM],
             pp_store_staged<false, false>(acc, p, row0, col0, mbase, nbase, epi_sa, epi_sb,
                                           epi_bias, s_pt, lane, stg);
     }
-    return true;
 }
 
 // Split-K for one wave of the ping-pong kernel.  The wave publishes its fp32
@@ -1440,16 +1439,23 @@ __global__ void __launch_bounds__(pp::THREADS) fp8_gemm_pp_kernel(Params p) {
                 barrier_lds();
                 __builtin_amdgcn_sched_barrier(0);
             }
-            // Between units: the next unit's parameters and first loads (every
-            // stage buffer is free: group 1 is in its last compute phase), then
-            // this unit's outputs (with split-K, only from the tile's last
-            // arriving unit).  Nothing waits for the next unit's loads before
-            // the outputs are written, and the final wait lets the output
-            // stores drain: on this architecture vector memory operations
-            // retire in issue order, so "at most kPpStagedStores outstanding"
-            // means every load issued before the stores has landed.
+            // Between units: this unit's outputs first (with split-K, only
+            // from the tile's last arriving unit), while group 1 runs its last
+            // compute phase; then, after the barrier that ends it, group 1
+            // writes its outputs.  Only once every wave's output stores are
+            // issued (the second barrier) do the next unit's parameters and
+            // first loads go out: vector memory operations leave a CU in issue
+            // order, so stores issued behind loads that miss the caches would
+            // wait for them, and group 0 would wait at the next unit's first
+            // barrier for group 1's stores.  Every stage buffer is free by then
+            // (group 1's staging area, A-bottom of buffer 1, is not loaded).
             const int un = u + G;
-            const PpTile T0 = T;
+            if (!split || pp_split_fixup(acc, p, u, T.t, wave, pp_lane()))
+                pp_store(acc, p, T.row0, T.col0, 0, q * 64, epi_sa, epi_sb, epi_bias, s_pt,
+                         has_bias, pp_lane(), smem + STG0 + q * STG_BYTES);
+            barrier_lds();   // pairs with group 1's last barrier of the tile
+            __builtin_amdgcn_s_barrier();   // group 1's output stores are issued
+            __builtin_amdgcn_sched_barrier(0);
             if (un < num_units) {
                 T = pp_tile(p, un, GROUP_M, xcd);
                 if (need_epi) {
@@ -1460,15 +1466,7 @@ __global__ void __launch_bounds__(pp::THREADS) fp8_gemm_pp_kernel(Params p) {
                 }
                 pp_tile_start(smem, p, T, L, q);
             }
-            bool staged = false;
-            if (!split || pp_split_fixup(acc, p, u, T0.t, wave, pp_lane()))
-                staged = pp_store(acc, p, T0.row0, T0.col0, 0, q * 64, epi_sa, epi_sb, epi_bias,
-                                  s_pt, has_bias, pp_lane(), smem + STG0 + q * STG_BYTES);
-            if (staged)
-                wait_vmcnt<kPpStagedStores>();
-            else
-                wait_vmcnt<0>();
-            barrier_lds();   // pairs with group 1's last barrier of the tile
+            wait_vmcnt<0>();
             __builtin_amdgcn_sched_barrier(0);
         } else {
             __builtin_amdgcn_s_barrier();   // one phase behind group 0
@@ -1490,8 +1488,10 @@ __global__ void __launch_bounds__(pp::THREADS) fp8_gemm_pp_kernel(Params p) {
                 __builtin_amdgcn_sched_barrier(0);
             }
             if (!split || pp_split_fixup(acc, p, u, T.t, wave, pp_lane()))
-                (void)pp_store(acc, p, T.row0, T.col0, 128, q * 64, epi_sa, epi_sb, epi_bias, s_pt,
-                               has_bias, pp_lane(), smem + STG1 + q * STG_BYTES);
+                pp_store(acc, p, T.row0, T.col0, 128, q * 64, epi_sa, epi_sb, epi_bias, s_pt,
+                         has_bias, pp_lane(), smem + STG1 + q * STG_BYTES);
+            __builtin_amdgcn_s_barrier();   // lets group 0 issue the next unit's loads
+            __builtin_amdgcn_sched_barrier(0);
             if (u + G < num_units) T = pp_tile(p, u + G, GROUP_M, xcd);
         }
     }
