@@ -261,7 +261,7 @@ def vendor_results(dev, reps=20):
             entry.update({"hipblaslt_us": round(tv * 1e6, 2), "ours_us": round(to * 1e6, 2),
                           "speedup": round(tv / to, 3),
                           "max_abs_diff_rel": float(f"{diff / scale:.3g}")})
-        except Exception as e:          # the library or this shape unavailable on the box
+        except Exception as e:          # hipBLASLt lacks this shape or mode here
             entry["error"] = f"{type(e).__name__}: {str(e)[:160]}"
         res.append(entry)
         del p
