@@ -208,15 +208,30 @@ def scaled_mm(a, b, scale_a, scale_b, bias=None, mode=PER_TENSOR, rows=None, col
 
     da = decode(a[rows], a_format)           # [m, K]
     db = decode(b[cols], b_format)           # [n, K]
+    # NaN codes (e4m3fn 0x7F / 0xFF) follow IEEE 754 arithmetic, written out
+    # here rather than left to the matrix-product library: a NaN operand makes
+    # its product NaN whatever the other factor (0 included), and a NaN term
+    # makes the sum NaN, so acc[m, n] is NaN exactly when row m of A or row n
+    # of B holds a NaN code.  The sums themselves are formed over the other
+    # values with the NaNs replaced by 0.
+    if (a_format != E4M3FN or b_format != E4M3FN) and not (
+            np.all(np.isfinite(da)) and np.all(np.isfinite(db))):
+        raise ValueError("e5m2 operands must be finite (no inf or NaN codes)")
+    nan_rows = np.isnan(da).any(axis=1)
+    nan_cols = np.isnan(db).any(axis=1)
+    if nan_rows.any() or nan_cols.any():
+        da = np.where(np.isnan(da), 0.0, da)
+        db = np.where(np.isnan(db), 0.0, db)
+    nan_mask = nan_rows[:, None] | nan_cols[None, :]
     if a_format == E4M3FN and b_format == E4M3FN:
         acc = da @ db.T
     else:
         if K > 32768:
             raise ValueError("the integer accumulation is only argued for K <= 32768")
-        if not (np.all(np.isfinite(da)) and np.all(np.isfinite(db))):
-            raise ValueError("e5m2 operands must be finite (no inf or NaN codes)")
         acc = _exact_integer_acc(da, db, UNIT_EXP[a_format], UNIT_EXP[b_format])
     mag = np.abs(da) @ np.abs(db).T
+    if nan_mask.any():
+        acc = np.where(nan_mask, np.nan, acc)
 
     sa = np.asarray(scale_a, dtype=np.float32).astype(np.float64).reshape(-1)
     sb = np.asarray(scale_b, dtype=np.float32).astype(np.float64).reshape(-1)

@@ -453,6 +453,34 @@ def test_nan_code_propagates():
     assert np.all(r["bits"][1] == oracle.f64_to_bf16_rne(np.array([16.0]))[0])
 
 
+def test_nan_times_zero_is_nan():
+    # IEEE 754: NaN * 0 is NaN, and a NaN term makes the sum NaN.  The NaN
+    # codes here meet only zeros (B's column 3 is zero in every row, A's row 1
+    # is zero except a NaN; B's row 2 holds a NaN where A is zero), so a sum
+    # that skipped zero products would lose them.
+    a = np.full((3, 16), 0x38, np.uint8)
+    a[0, 3] = 0x7F
+    a[1, :] = 0x00
+    a[1, 9] = 0xFF
+    a[2, 5] = 0x00
+    b = np.full((3, 16), 0x40, np.uint8)
+    b[:, 3] = 0x00
+    b[:, 9] = 0x00
+    b[2, 5] = 0x7F
+    r = oracle.scaled_mm(a, b, np.ones(1, np.float32), np.ones(1, np.float32))
+    bits = r["bits"]
+    assert np.all(bits[0] == 0x7FC0) and np.all(bits[1] == 0x7FC0)
+    assert np.all(bits[:, 2] == 0x7FC0)
+    # row 2 x columns 0, 1: A[2] = 1.0 except a 0 at k=5, B = 2.0 except zeros
+    # at k = 3, 9: 13 products of 2
+    assert np.all(bits[2, :2] == oracle.f64_to_bf16_rne(np.array([26.0]))[0])
+    # the same with a bias and row-wise scales: NaN stays NaN
+    r = oracle.scaled_mm(a, b, np.full(3, 0.5, np.float32), np.full(3, 2.0, np.float32),
+                         np.full(3, 0x3F80, np.uint16), RW)
+    assert np.all(r["bits"][0] == 0x7FC0) and np.all(r["bits"][:, 2] == 0x7FC0)
+    assert np.all(r["bits"][2, :2] == oracle.f64_to_bf16_rne(np.array([27.0]))[0])
+
+
 # --------------------------------------------------- the pins catch mutants ---
 
 def _mutants():
