@@ -1465,8 +1465,13 @@ __global__ void __launch_bounds__(pp::THREADS) fp8_gemm_pp_kernel(Params p) {
                     pp_params_dma(p, T, q, pp_lane(), has_bias, sa, sb, bias);
                 }
                 pp_tile_start(smem, p, T, L, q);
+                // The next unit's first reads take rows of A-top and B that
+                // all four waves of this group loaded: every wave's loads must
+                // have landed (own wait, then the barrier) before any reads.
+                // Group 1 joins this barrier at the end of its unit.
+                wait_vmcnt<0>();
+                barrier_lds();
             }
-            wait_vmcnt<0>();
             __builtin_amdgcn_sched_barrier(0);
         } else {
             __builtin_amdgcn_s_barrier();   // one phase behind group 0
@@ -1492,7 +1497,11 @@ __global__ void __launch_bounds__(pp::THREADS) fp8_gemm_pp_kernel(Params p) {
                          has_bias, pp_lane(), smem + STG1 + q * STG_BYTES);
             __builtin_amdgcn_s_barrier();   // lets group 0 issue the next unit's loads
             __builtin_amdgcn_sched_barrier(0);
-            if (u + G < num_units) T = pp_tile(p, u + G, GROUP_M, xcd);
+            if (u + G < num_units) {
+                T = pp_tile(p, u + G, GROUP_M, xcd);
+                __builtin_amdgcn_s_barrier();   // group 0's first slices have landed
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
     }
 }

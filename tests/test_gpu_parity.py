@@ -1,9 +1,13 @@
 """GPU parity: the HIP library against the CPU oracle, element by element,
 on seeded inputs, through the C ABI (via the thin ctypes binding).
 
-Small and ragged shapes are compared in full; the full-size workloads are
-compared on sampled rows and columns that the oracle computes one by one.
+Small and ragged shapes, and every e4m3fn workload up to M = N = K = 8192,
+are compared in full; the largest shape (16384 x 16384 x 8192) and the e5m2
+workloads, whose exact integer oracle is slow, on rows and columns that hit
+every output tile of the launch.
 """
+import re
+
 import numpy as np
 import pytest
 import torch
@@ -61,13 +65,41 @@ def check_full(inp, config=-1):
     return got, ref
 
 
-def check_sampled(inp, out, n_rows=24, n_cols=24, seed=0):
-    """Compare whole sampled rows and whole sampled columns (every tile of the
-    grid is hit by both), including the first and last of each."""
+def tile_dims(inp, config=-1):
+    """(BM, BN) of the tile configuration the call uses (the automatic choice
+    for config < 0), read from its name."""
     M, N, K = inp.shape
-    rng = np.random.Generator(np.random.PCG64(seed))
-    rows = np.unique(np.concatenate([[0, M - 1], rng.integers(0, M, n_rows)]))
-    cols = np.unique(np.concatenate([[0, N - 1], rng.integers(0, N, n_cols)]))
+    cfg = config if config >= 0 else binding.select_config(M, N, K, inp.mode, inp.bias is not None)
+    name = binding.config_names()[cfg]
+    return int(re.search(r"bm(\d+)", name).group(1)), int(re.search(r"bn(\d+)", name).group(1))
+
+
+def covering_indices(n, band, rot):
+    """One index inside every band of `band` consecutive indices (the last band
+    may be short), at an offset that rotates from band to band, plus 0 and n-1.
+    With band = the tile's height (width), every tile row (column) of the grid
+    contains a chosen index, and the offsets reach different waves and lanes
+    of the tiles."""
+    idx = [0, n - 1]
+    for b in range((n + band - 1) // band):
+        lo = b * band
+        width = min(band, n - lo)
+        idx.append(lo + (b * 37 + rot) % width)
+    return np.unique(np.asarray(idx, dtype=np.int64))
+
+
+def check_sampled(inp, out, config=-1, band_scale=1, rot=0):
+    """Compare whole rows and whole columns chosen by covering_indices: one row
+    in every tile row and one column in every tile column of the launch's tile
+    grid, so every output tile is checked along a full row and a full column.
+    band_scale > 1 samples every band_scale-th tile row/column band instead
+    (only for the slow e5m2 oracle)."""
+    M, N, K = inp.shape
+    bm, bn = tile_dims(inp, config)
+    rows = covering_indices(M, bm * band_scale, rot)
+    cols = covering_indices(N, bn * band_scale, rot + 11)
+    print(f"[parity] sampled {len(rows)} rows (band {bm * band_scale}), {len(cols)} cols "
+          f"(band {bn * band_scale})", flush=True)
     rows_t = torch.from_numpy(rows).to(out.device)
     cols_t = torch.from_numpy(cols).to(out.device)
     g_rows = out_bits(out.index_select(0, rows_t))
@@ -280,15 +312,16 @@ def test_workload(name):
     out = run_gpu(inp)
     M, N, K = inp.shape
     e4m3 = inp.a_format == inp.b_format == "e4m3fn"
-    if M * N * K <= (2048 ** 3 if e4m3 else 1024 ** 3):
+    if e4m3 or M * N * K <= 1024 ** 3:
+        # every output element, up to the M = N = K = 8192 headline shape
         ref = ref_mm(inp)
         nbad, worst, first = compare(out_bits(out), ref)
+        print(f"[parity] full compare: worst error {worst:.3f} of the bound", flush=True)
         assert nbad == 0, (nbad, worst, first)
-    elif e4m3:
-        check_sampled(inp, out)
     else:
-        # the oracle's exact integer sums are slow: fewer sampled rows/columns
-        check_sampled(inp, out, n_rows=3, n_cols=3)
+        # e5m2: the oracle's exact integer sums are slow; one row in every
+        # tile row and one column in every tile column
+        check_sampled(inp, out, rot=len(name))
 
 
 @pytest.mark.slow
@@ -297,7 +330,38 @@ def test_workload_largest(name):
     inp = wl.make_workload(name)
     print(f"[parity] workload {name} shape={inp.shape}", flush=True)
     out = run_gpu(inp)
-    check_sampled(inp, out, n_rows=8, n_cols=8)
+    check_sampled(inp, out, rot=len(name))
+
+
+# ------------------------------------ ping-pong kernel: several tiles per CU ---
+
+@pytest.mark.parametrize("shape", [(4352, 4096, 512), (8192, 8192, 128), (8192, 8192, 256),
+                                   (4400, 4104, 384), (6144, 6144, 2176)])
+@pytest.mark.parametrize("mode,bias", [(PT, False), (RW, True), (PT, True)])
+def test_ping_pong_several_tiles_per_workgroup(shape, mode, bias):
+    # More 256 x 256 tiles than workgroups (272, 1024, 1024, 306, 576 tiles on
+    # 256 CUs): workgroups change tiles, so the tile-change path (outputs of
+    # one tile, then the next tile's first slices and epilogue parameters,
+    # alternating parameter areas) runs; units of 1, 2, 3, 4 and 17 slices;
+    # ragged edge tiles in (4400, 4104, 384).  Compared in full.
+    M, N, K = shape
+    pp = _cfg("pp_bm256_bn256_bk128_w8_mfma16")
+    inp = wl.make_inputs(M, N, K, mode, "codes", bias=bias, key=M + N + K + 3 * mode + bias)
+    print(f"[parity] ping-pong shape={shape} mode={mode} bias={bias}", flush=True)
+    got = out_bits(run_gpu_plan(inp, pp, 1))
+    nbad, worst, first = compare(got, ref_mm(inp))
+    assert nbad == 0, (nbad, worst, first)
+
+
+@pytest.mark.parametrize("mode", [PT, RW])
+def test_ping_pong_several_units_per_workgroup_split(mode):
+    # split-K units: 272 tiles x 2 splits = 544 units on 256 workgroups
+    M, N, K = 4352, 4096, 10240
+    pp = _cfg("pp_bm256_bn256_bk128_w8_mfma16")
+    inp = wl.make_inputs(M, N, K, mode, "codes", bias=mode == RW, key=90 + mode)
+    got = out_bits(run_gpu_plan(inp, pp, 2))
+    nbad, worst, first = compare(got, ref_mm(inp))
+    assert nbad == 0, (nbad, worst, first)
 
 
 # ---------------------------------------------------------------- split-K ---

@@ -218,3 +218,33 @@ def test_outputs_on_another_device_are_refused():
     q, s = binding.fp8_quantize(x, RW)
     torch.cuda.synchronize()
     assert q.is_cuda and s.is_cuda
+
+
+# ------------------------------------------------- the large-input code paths ---
+
+def _workload_bits(rows, cols, key):
+    from precision_linear_amd import workloads as wl
+    return wl.bf16_matrix_bits(rows, cols, key=key)
+
+
+@pytest.mark.parametrize("rows,cols,fmt", [(8192, 8192, "e4m3fn"), (8192, 8192, "e5m2"),
+                                           (8192, 4096, "e4m3fn"), (4099, 8192, "e4m3fn")])
+def test_per_tensor_large_bitexact(rows, cols, fmt):
+    # The benchmarked per-tensor size and the sizes around it: the amax and
+    # quantisation passes run their unrolled grid-stride loops (every
+    # workgroup takes several strides), and the scale comes from the maxima of
+    # the whole grid of workgroups (2048 on 256 CUs).  The matrix's amax is
+    # planted in the last elements, which the last stride of the last
+    # workgroups reads.
+    bits = _workload_bits(rows, cols, key=rows + cols + len(fmt))
+    bits[-1, -1] = bf16_bits([-9.5])[0]
+    check(bits, PT, fmt)
+
+
+@pytest.mark.parametrize("rows,cols,fmt", [(40000, 256, "e4m3fn"), (40000, 256, "e5m2"),
+                                           (33000, 4112, "e4m3fn")])
+def test_rowwise_more_rows_than_workgroups_bitexact(rows, cols, fmt):
+    # More rows than the row-wise grid (128 workgroups per CU): workgroups
+    # walk several rows with the next row prefetched into registers.
+    bits = _workload_bits(rows, cols, key=rows * 3 + cols + len(fmt))
+    check(bits, RW, fmt)
