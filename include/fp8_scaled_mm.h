@@ -31,23 +31,19 @@
  * call returns; it may be called from several host threads.
  *
  * Workspace: when the output has too few tiles to occupy the GPU, the K
- * reduction is split over several workgroups whose fp32 partial tiles meet in
- * a workspace (the split-K of the gist "matmul_fp8.py", autotune parameter
- * SPLIT_K, done with a deterministic in-order sum instead of atomics).  The
- * plain entry points then use a workspace owned by the library, one per
- * (device, stream), allocated and zero-filled by the first such call and
- * grown (after synchronising that stream) when a larger one is needed; it is
- * freed only at process exit.  fp8_scaled_mm_with_plan accepts a caller
- * workspace instead and then allocates nothing.  Calls on different streams
- * never share a workspace.  The library's own workspace is allocated and
- * zero-filled (hipMalloc, hipMemset, a device synchronisation) during the
- * first split call on a stream: code that captures that call into a HIP graph
- * passes a workspace of its own, or makes one uncaptured call first.
+ * reduction can be split over several workgroups whose fp32 partial tiles
+ * meet in a workspace (the split-K of the gist "matmul_fp8.py", autotune
+ * parameter SPLIT_K, done with a deterministic in-order sum instead of
+ * atomics).  The library never allocates one: fp8_scaled_mm and
+ * fp8_scaled_mm_with_config never split K (they pick tiles that fill the GPU
+ * without it), and fp8_scaled_mm_with_plan / fp8_scaled_mm_typed split K
+ * only with a caller workspace.
  *
  * Execution: asynchronous on `stream` (a hipStream_t; NULL = the default
- * stream).  The call returns after the launch, without synchronising.  It
- * launches kernels only (no memset, no allocation once the stream's split-K
- * workspace exists), so it can be captured into a HIP graph.
+ * stream).  Every entry point only enqueues kernels: no allocation, no
+ * memset, no host synchronisation, so a call can be captured into a HIP
+ * graph, the first call on a stream included.  The first call on a device
+ * reads the device's properties once (CU count, architecture).
  *
  * Preconditions (checked on the host, before anything is enqueued):
  *   - 0 <= M, N <= 2^31 - 1; 16 <= K <= 2^23 and K % 16 == 0 (whole 16-byte
@@ -59,7 +55,8 @@
  *     aligned.  out must not overlap any input.
  * Errors: the return value is FP8MM_OK (0) or one of the FP8MM_ERR_* codes;
  * on a validation error nothing is enqueued and `out` is untouched.  A
- * launch failure reported by the runtime gives FP8MM_ERR_LAUNCH.
+ * device that is not a gfx950 gives FP8MM_ERR_DEVICE; a launch failure
+ * reported by the runtime gives FP8MM_ERR_LAUNCH.
  */
 #ifndef FP8_SCALED_MM_H
 #define FP8_SCALED_MM_H
@@ -113,14 +110,15 @@ int fp8_scaled_mm_with_config(const void* A, const void* B, const float* scale_a
 
 /* The most general form: explicit tile configuration (config_id < 0: chosen
  * from the shape), split-K factor (splits == 0: chosen; 1: no split; at most
- * 64, clamped to the number of K slices), and workspace.  With a non-NULL
- * `workspace` (256-byte aligned, at least fp8_scaled_mm_workspace_size()
- * bytes, zero-filled before its first use: its first 256 KiB are arrival
- * counters, which every call leaves at zero again; the partial tiles after
- * them need no initial value) the library allocates nothing; with NULL it uses its own (see the
- * workspace note above).  A caller workspace must not be used by two calls
- * that can run at the same time.  Results do not depend on which workgroup
- * finishes first: partial tiles are summed in split order. */
+ * 64, clamped to the number of K slices), and workspace.  K is split only
+ * with a non-NULL `workspace`: 256-byte aligned, at least
+ * fp8_scaled_mm_workspace_size() bytes, zero-filled before its first use (its
+ * first 256 KiB are arrival counters, which every call leaves at zero again;
+ * the partial tiles after them need no initial value).  The caller owns it.
+ * With a NULL workspace the automatic plan does not split, and an explicit
+ * splits > 1 returns FP8MM_ERR_WORKSPACE.  A workspace must not be used by
+ * two calls that can run at the same time.  Results do not depend on which
+ * workgroup finishes first: partial tiles are summed in split order. */
 int fp8_scaled_mm_with_plan(const void* A, const void* B, const float* scale_a,
                             const float* scale_b, const void* bias_or_null, void* out,
                             int64_t M, int64_t N, int64_t K, int scaling_mode,
@@ -142,13 +140,13 @@ int fp8_scaled_mm_typed(const void* A, int a_format, const void* B, int b_format
                         int64_t workspace_bytes);
 
 /* Workspace bytes the plan (config_id, splits; negative/zero = automatic)
- * needs for this problem; 0 when it does not split K, -1 for a bad mode.
- * Host logic only. */
+ * needs for this problem when the call has a workspace; 0 when it does not
+ * split K, -1 for a bad mode.  Host logic only. */
 int64_t fp8_scaled_mm_workspace_size(int64_t M, int64_t N, int64_t K, int scaling_mode,
                                      int has_bias, int config_id, int splits);
 
-/* The split-K factor the automatic plan uses (host logic only; -1 for an
- * invalid problem). */
+/* The split-K factor the automatic plan uses when the call has a workspace
+ * (host logic only; -1 for an invalid problem).  Without a workspace it is 1. */
 int fp8_scaled_mm_select_splits(int64_t M, int64_t N, int64_t K, int scaling_mode, int has_bias,
                                 int config_id);
 
@@ -158,16 +156,21 @@ int fp8_scaled_mm_num_configs(void);
 /* Static, NUL-terminated description of a configuration ("" if unknown). */
 const char* fp8_scaled_mm_config_name(int config_id);
 
-/* The configuration fp8_scaled_mm would use for this problem (pure host
- * logic: no device access).  Returns -1 for an invalid problem. */
-int fp8_scaled_mm_select_config(int64_t M, int64_t N, int64_t K, int scaling_mode, int has_bias);
+/* The configuration the automatic plan uses for this problem: without a
+ * workspace (with_workspace == 0: fp8_scaled_mm, or a NULL workspace) or with
+ * one (fp8_scaled_mm_with_plan with a workspace).  Pure
+ * host logic: no device access.  Returns -1 for an invalid problem. */
+int fp8_scaled_mm_select_config(int64_t M, int64_t N, int64_t K, int scaling_mode, int has_bias,
+                                int with_workspace);
 
 /* Grid size (workgroups) a launch of `config_id` without split-K uses on a
  * device with `num_cus` compute units for an M x N output (host logic only). */
 int64_t fp8_scaled_mm_grid_size(int config_id, int64_t M, int64_t N, int num_cus);
 
-/* Static, NUL-terminated text for a status code. */
+/* Static, NUL-terminated text for a status code (fp8mm_status_string is the
+ * same function under the short name). */
 const char* fp8_scaled_mm_status_string(int status);
+const char* fp8mm_status_string(int status);
 
 #ifdef __cplusplus
 }

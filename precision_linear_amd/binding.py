@@ -34,7 +34,7 @@ EXPORTS = ("fp8_scaled_mm", "fp8_scaled_mm_with_config", "fp8_scaled_mm_with_pla
            "fp8_scaled_mm_typed",
            "fp8_scaled_mm_workspace_size", "fp8_scaled_mm_select_splits",
            "fp8_scaled_mm_num_configs", "fp8_scaled_mm_config_name", "fp8_scaled_mm_select_config",
-           "fp8_scaled_mm_grid_size", "fp8_scaled_mm_status_string",
+           "fp8_scaled_mm_grid_size", "fp8_scaled_mm_status_string", "fp8mm_status_string",
            "fp8_quantize_e4m3", "fp8_quantize_e5m2", "fp8_quantize_status_string")
 
 # status codes from include/fp8_quantize.h
@@ -78,12 +78,14 @@ def lib() -> ctypes.CDLL:
         L.fp8_scaled_mm_num_configs.restype = i32
         L.fp8_scaled_mm_config_name.argtypes = [i32]
         L.fp8_scaled_mm_config_name.restype = ctypes.c_char_p
-        L.fp8_scaled_mm_select_config.argtypes = [i64, i64, i64, i32, i32]
+        L.fp8_scaled_mm_select_config.argtypes = [i64, i64, i64, i32, i32, i32]
         L.fp8_scaled_mm_select_config.restype = i32
         L.fp8_scaled_mm_grid_size.argtypes = [i32, i64, i64, i32]
         L.fp8_scaled_mm_grid_size.restype = i64
         L.fp8_scaled_mm_status_string.argtypes = [i32]
         L.fp8_scaled_mm_status_string.restype = ctypes.c_char_p
+        L.fp8mm_status_string.argtypes = [i32]
+        L.fp8mm_status_string.restype = ctypes.c_char_p
         L.fp8_quantize_e4m3.argtypes = [vp, vp, vp, i64, i64, i32, vp]
         L.fp8_quantize_e4m3.restype = i32
         L.fp8_quantize_e5m2.argtypes = [vp, vp, vp, i64, i64, i32, vp]
@@ -103,8 +105,12 @@ def config_names() -> list:
     return [L.fp8_scaled_mm_config_name(i).decode() for i in range(L.fp8_scaled_mm_num_configs())]
 
 
-def select_config(M, N, K, mode, has_bias=False) -> int:
-    return int(lib().fp8_scaled_mm_select_config(M, N, K, _MODES[mode], int(bool(has_bias))))
+def select_config(M, N, K, mode, has_bias=False, with_workspace=True) -> int:
+    """The automatic configuration; with_workspace=True is the plan this
+    module's fp8_scaled_mm runs (it supplies a workspace whenever the plan
+    splits K), False the one of the C entry point fp8_scaled_mm."""
+    return int(lib().fp8_scaled_mm_select_config(M, N, K, _MODES[mode], int(bool(has_bias)),
+                                                 int(bool(with_workspace))))
 
 
 def select_splits(M, N, K, mode, has_bias=False, config=-1) -> int:
@@ -115,6 +121,26 @@ def select_splits(M, N, K, mode, has_bias=False, config=-1) -> int:
 def workspace_size(M, N, K, mode, has_bias=False, config=-1, splits=0) -> int:
     return int(lib().fp8_scaled_mm_workspace_size(M, N, K, _MODES[mode], int(bool(has_bias)),
                                                   int(config), int(splits)))
+
+
+# Split-K workspaces handed to the library, per (device, stream): zero-filled
+# torch allocations (the library allocates nothing itself).  Calls on one
+# stream are ordered, so they can share one; a larger one replaces it for
+# later calls, but none is ever freed, because a captured HIP graph may still
+# hold its address.
+_workspaces: dict = {}
+
+
+def _workspace(device: torch.device, stream: int, nbytes: int) -> torch.Tensor:
+    key = (device.index, stream)
+    have = _workspaces.get(key)
+    if have and have[-1].numel() >= nbytes:
+        return have[-1]
+    size = max(nbytes, 2 * have[-1].numel() if have else 0)
+    size = (size + (1 << 20) - 1) >> 20 << 20
+    ws = torch.zeros(size, dtype=torch.uint8, device=device)   # a fill kernel on this stream
+    _workspaces.setdefault(key, []).append(ws)
+    return ws
 
 
 _TORCH_FORMATS = {torch.float8_e4m3fn: E4M3FN, torch.float8_e5m2: E5M2}
@@ -153,8 +179,9 @@ def fp8_scaled_mm(a: torch.Tensor, b: torch.Tensor, scale_a: torch.Tensor, scale
     view (stride (1, K)), which is the same memory.  Each operand is e4m3fn or
     e5m2: taken from its torch dtype, or from a_format / b_format for uint8
     codes (default e4m3fn).  `config` (-1: automatic) and `splits` (0:
-    automatic) select the plan; `workspace` (a GPU byte tensor, zero-filled
-    before first use) replaces the library-owned split-K workspace."""
+    automatic) select the plan.  When the plan splits K, its workspace is
+    `workspace` (a GPU byte tensor, zero-filled before first use) or, if that
+    is None, one this module keeps per stream (allocated by torch)."""
     if mode not in _MODES:
         raise ValueError(f"mode must be 'per_tensor' or 'rowwise', got {mode!r}")
     m = _MODES[mode]
@@ -190,12 +217,19 @@ def fp8_scaled_mm(a: torch.Tensor, b: torch.Tensor, scale_a: torch.Tensor, scale
         out = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
     elif out.dtype != torch.bfloat16 or tuple(out.shape) != (M, N) or not out.is_contiguous():
         raise ValueError("out must be a contiguous bf16 M x N tensor")
+    stream = torch.cuda.current_stream(a.device).cuda_stream
     ws_ptr, ws_bytes = None, 0
     if workspace is not None:
         if not workspace.is_cuda or not workspace.is_contiguous():
             raise ValueError("workspace must be a contiguous GPU tensor")
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
-    stream = torch.cuda.current_stream(a.device).cuda_stream
+    elif splits != 1:
+        need = int(lib().fp8_scaled_mm_workspace_size(M, N, K, m, int(bias is not None),
+                                                      int(config), int(splits)))
+        if need > 0:
+            with torch.cuda.device(a.device):
+                ws = _workspace(a.device, stream, need)
+            ws_ptr, ws_bytes = ws.data_ptr(), ws.numel()
     with torch.cuda.device(a.device):
         st = lib().fp8_scaled_mm_typed(
             a.data_ptr(), fa, b.data_ptr(), fb, scale_a.data_ptr(), scale_b.data_ptr(),

@@ -74,38 +74,30 @@ struct LaunchPair {
 constexpr int kFormats = 4;
 
 // The generic kernel's tile configurations, in config-id order:
-// X(name, BM, BN, BK, WAVES_M, WAVES_N, STAGES, MFMA size, GROUP_M).  Ids 0..9
-// are the first list, id 10 is the ping-pong kernel, ids 11.. the second list.
+// X(name, BM, BN, BK, WAVES_M, WAVES_N, STAGES, MFMA size, GROUP_M); the
+// ping-pong kernel follows them (id kPingPongId).
+//   * few rows (M <= 16, 64, 128) and many columns: tiles as tall as M, 112
+//     or 64 wide, or 128 x 128, streaming B from HBM;
+//   * few rows and few columns (a column shard of a skinny problem): narrow
+//     tiles, split over K (the last unit of a tile reads every partial, so
+//     smaller tiles make that fix-up cheaper) or, without a workspace, enough
+//     of them to fill the CUs;
+//   * 128 x 128 on 8 waves (mid-size grids) and on 4 waves with two
+//     workgroups per CU (one's output stores overlap the other's loads).
 #define FP8MM_GENERIC_CONFIGS(X)                                                   \
-    X("bm128_bn128_bk128_w2x2_s3_mfma32", 128, 128, 128, 2, 2, 3, 32, 8)           \
+    X("bm16_bn32_bk512_w1x2_s6_mfma16", 16, 32, 512, 1, 2, 6, 16, 8)               \
     X("bm16_bn64_bk256_w1x4_s4_mfma16", 16, 64, 256, 1, 4, 4, 16, 8)               \
     X("bm16_bn112_bk256_w1x7_s4_mfma16", 16, 112, 256, 1, 7, 4, 16, 8)             \
-    X("bm16_bn32_bk512_w1x2_s6_mfma16", 16, 32, 512, 1, 2, 6, 16, 8)               \
-    X("bm64_bn64_bk128_w4x1_s8_mfma16", 64, 64, 128, 4, 1, 8, 16, 8)               \
-    X("bm64_bn112_bk256_w1x7_s3_mfma16", 64, 112, 256, 1, 7, 3, 16, 8)             \
-    X("bm64_bn64_bk256_w1x4_s4_mfma16", 64, 64, 256, 1, 4, 4, 16, 8)               \
-    X("bm128_bn128_bk128_w2x2_s4_mfma32", 128, 128, 128, 2, 2, 4, 32, 8)           \
-    X("bm128_bn128_bk128_w2x4_s4_mfma32", 128, 128, 128, 2, 4, 4, 32, 8)           \
-    X("bm256_bn256_bk128_w2x4_s2_mfma32", 256, 256, 128, 2, 4, 2, 32, 8)
-// Wide tiles for skinny problems (few rows, many columns): less of each
-// workgroup's load traffic goes to the A rows every tile re-reads.  Then
-// narrow tiles for few rows and few columns (a column shard of a skinny
-// problem), split over K: the last unit of a tile reads every partial, so
-// smaller tiles make that fix-up cheaper.
-#define FP8MM_GENERIC_CONFIGS_2(X)                                                 \
-    X("bm16_bn128_bk256_w1x4_s4_mfma16", 16, 128, 256, 1, 4, 4, 16, 8)             \
-    X("bm64_bn256_bk128_w1x8_s3_mfma16", 64, 256, 128, 1, 8, 3, 16, 8)             \
-    X("bm64_bn224_bk128_w1x7_s3_mfma16", 64, 224, 128, 1, 7, 3, 16, 8)             \
-    X("bm128_bn256_bk128_w2x4_s3_mfma32", 128, 256, 128, 2, 4, 3, 32, 8)           \
-    X("bm128_bn224_bk128_w1x7_s3_mfma32", 128, 224, 128, 1, 7, 3, 32, 8)           \
-    X("bm128_bn128_bk128_w2x2_s2_mfma32", 128, 128, 128, 2, 2, 2, 32, 8)           \
-    X("bm128_bn32_bk256_w4x2_s3_mfma16", 128, 32, 256, 4, 2, 3, 16, 8)             \
     X("bm64_bn32_bk256_w4x2_s4_mfma16", 64, 32, 256, 4, 2, 4, 16, 8)               \
-    X("bm128_bn64_bk256_w4x2_s3_mfma16", 128, 64, 256, 4, 2, 3, 16, 8)
+    X("bm64_bn64_bk256_w1x4_s4_mfma16", 64, 64, 256, 1, 4, 4, 16, 8)               \
+    X("bm64_bn112_bk256_w1x7_s3_mfma16", 64, 112, 256, 1, 7, 3, 16, 8)             \
+    X("bm128_bn32_bk256_w4x2_s3_mfma16", 128, 32, 256, 4, 2, 3, 16, 8)             \
+    X("bm128_bn64_bk256_w4x2_s3_mfma16", 128, 64, 256, 4, 2, 3, 16, 8)             \
+    X("bm128_bn128_bk128_w2x4_s4_mfma32", 128, 128, 128, 2, 4, 4, 32, 8)           \
+    X("bm128_bn128_bk128_w2x2_s2_mfma32", 128, 128, 128, 2, 2, 2, 32, 8)
 constexpr int kNumGenericConfigs = 10;
 constexpr int kPingPongId = kNumGenericConfigs;
-constexpr int kNumGenericConfigs2 = 9;
-constexpr int kNumConfigs = kNumGenericConfigs + 1 + kNumGenericConfigs2;
+constexpr int kNumConfigs = kNumGenericConfigs + 1;
 
 // One table per format pair, defined in fp8_gemm_f<k>.hip.  Not const: a
 // const namespace-scope variable would also be emitted for the device, where
@@ -1536,6 +1528,5 @@ void launch_cfg(const Params& p, dim3 grid, hipStream_t stream) {
     namespace fp8mm {                                                             \
     LaunchPair NAME[kNumConfigs] = {                                              \
         FP8MM_GENERIC_CONFIGS(FP8MM_PAIR_F(FMT))                                  \
-        LaunchPair{&launch_pp<8, FMT>, nullptr},                                  \
-        FP8MM_GENERIC_CONFIGS_2(FP8MM_PAIR_F(FMT))};                              \
+        LaunchPair{&launch_pp<8, FMT>, nullptr}};                                 \
     }

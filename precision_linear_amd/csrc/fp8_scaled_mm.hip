@@ -31,9 +31,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include <map>
+#include <string.h>
+
 #include <mutex>
-#include <utility>
 
 #include "../../include/fp8_scaled_mm.h"
 #include "fp8_gemm_kernels.h"
@@ -62,31 +62,30 @@ const ConfigInfo kConfigs[kNumConfigs] = {
     FP8MM_GENERIC_CONFIGS(FP8MM_CFG_INFO)
     ConfigInfo{"pp_bm256_bn256_bk128_w8_mfma16", pp::BM, pp::BN, pp::BK, true, pp::THREADS,
                pp::LDS_BYTES, 1},
-    FP8MM_GENERIC_CONFIGS_2(FP8MM_CFG_INFO)
 };
 #undef FP8MM_CFG_INFO
 
 // Launch wrappers by operand formats, then configuration.
 LaunchPair* const kLaunch[kFormats] = {kLaunchF0, kLaunchF1, kLaunchF2, kLaunchF3};
-constexpr int kMidConfig = 8;         // "bm128_bn128_bk128_w2x4_s4_mfma32"
+constexpr int kNarrow16x32 = 0;       // "bm16_bn32_bk512_w1x2_s6_mfma16"
 constexpr int kSkinny16x64 = 1;       // "bm16_bn64_bk256_w1x4_s4_mfma16"
 constexpr int kSkinny16x112 = 2;      // "bm16_bn112_bk256_w1x7_s4_mfma16"
+constexpr int kNarrow64x32 = 3;       // "bm64_bn32_bk256_w4x2_s4_mfma16"
+constexpr int kSkinny64x64 = 4;       // "bm64_bn64_bk256_w1x4_s4_mfma16"
 constexpr int kSkinny64x112 = 5;      // "bm64_bn112_bk256_w1x7_s3_mfma16"
-constexpr int kSkinny64x64 = 6;       // "bm64_bn64_bk256_w1x4_s4_mfma16"
-constexpr int kSkinny128x128 = 8;     // "bm128_bn128_bk128_w2x4_s4_mfma32"
-constexpr int kNarrow16x32 = 3;       // "bm16_bn32_bk512_w1x2_s6_mfma16"
-constexpr int kNarrow128x32 = 17;     // "bm128_bn32_bk256_w4x2_s3_mfma16"
-constexpr int kNarrow64x32 = 18;      // "bm64_bn32_bk256_w4x2_s4_mfma16"
-constexpr int kNarrow128x64 = 19;     // "bm128_bn64_bk256_w4x2_s3_mfma16"
+constexpr int kNarrow128x32 = 6;      // "bm128_bn32_bk256_w4x2_s3_mfma16"
+constexpr int kNarrow128x64 = 7;      // "bm128_bn64_bk256_w4x2_s3_mfma16"
+constexpr int kMidConfig = 8;         // "bm128_bn128_bk128_w2x4_s4_mfma32"
+constexpr int kSkinny128x128 = kMidConfig;
+constexpr int kTwoPerCuConfig = 9;    // "bm128_bn128_bk128_w2x2_s2_mfma32", two workgroups per CU
 constexpr int kPingPongConfig = kPingPongId;   // "pp_bm256_bn256_bk128_w8_mfma16"
-constexpr int kTwoPerCuConfig = 16;   // "bm128_bn128_bk128_w2x2_s2_mfma32", two workgroups per CU
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 int choose_splits(int cfg, int64_t M, int64_t N, int64_t K);
 
-int choose_config(int64_t M, int64_t N, int64_t K, int mode, int has_bias) {
-    (void)mode; (void)has_bias;
+// The tile configuration for a call that may split K.
+int choose_config_split(int64_t M, int64_t N, int64_t K) {
     // Skinny problems (M <= 128) are HBM-bound on B: tiles as tall as M and
     // 112 columns wide when that gives about one tile per CU (N = 28672 is
     // 256 x 112), else narrower tiles whose K reduction is split until the
@@ -132,17 +131,59 @@ int choose_config(int64_t M, int64_t N, int64_t K, int mode, int has_bias) {
     return kMidConfig;
 }
 
-int device_cus(int dev) {
-    // Per-device compute-unit count, read once.
-    static int cache[64] = {0};
-    if (dev < 0 || dev >= 64) return 0;
-    if (cache[dev] == 0) {
-        int cus = 0;
-        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-            return 0;
-        __atomic_store_n(&cache[dev], cus, __ATOMIC_RELAXED);
+// The tile configuration for a call that cannot split K, where the plan
+// above would: the tallest tile (of at most M rows) whose grid has at least
+// 200 tiles, else the smallest tile; for larger M, 128 x 128 tiles two per
+// CU or on 8 waves, or 128 x 64.  From a sweep of every configuration
+// without split-K on MI355X: M=128, K=28672, N=1024: 16 x 32 tiles (256 of
+// them) 40 us against 73 us with 128 x 32; M=64, K=8192, N=3584: 16 x 64
+// tiles 18 us; 512 x 3072 x 12288: 128 x 64 tiles 44 us against 76 us with
+// 128 x 128 two per CU.
+int choose_config_nosplit(int64_t M, int64_t N, int64_t K) {
+    (void)K;
+    auto tiles = [&](int cfg) { return cdiv(M, kConfigs[cfg].bm) * cdiv(N, kConfigs[cfg].bn); };
+    if (M <= 128) {
+        const int order[] = {kNarrow128x32, kNarrow64x32, kSkinny16x64, kNarrow16x32};
+        for (int cfg : order)
+            if (kConfigs[cfg].bm <= (M <= 16 ? 16 : M <= 64 ? 64 : 128) && tiles(cfg) >= 200)
+                return cfg;
+        return kNarrow16x32;
     }
-    return __atomic_load_n(&cache[dev], __ATOMIC_RELAXED);
+    const int64_t tiles128 = cdiv(M, 128) * cdiv(N, 128);
+    if (tiles128 >= 384) return kTwoPerCuConfig;
+    if (tiles128 >= 160) return kMidConfig;
+    return tiles(kNarrow128x64) > tiles128 ? kNarrow128x64 : kMidConfig;
+}
+
+// The automatic tile configuration.  can_split: the call has a workspace for
+// split-K partials; without one, K is never split, and where the plan with a
+// workspace would split, narrower tiles take its place.
+int choose_config(int64_t M, int64_t N, int64_t K, int mode, int has_bias, bool can_split) {
+    (void)mode; (void)has_bias;
+    const int cfg = choose_config_split(M, N, K);
+    if (can_split || choose_splits(cfg, M, N, K) <= 1) return cfg;
+    return choose_config_nosplit(M, N, K);
+}
+
+// Per-device facts, read once per device: the compute-unit count and whether
+// the device is a gfx950 (the kernels are built for it only).  0 = not read
+// yet; a lost race only reads them twice.
+constexpr int kMaxDevices = 64;
+int g_cus[kMaxDevices];
+int g_arch_ok[kMaxDevices];   // 1: gfx950, 2: another architecture
+
+int device_cus(int dev) {
+    if (dev < 0 || dev >= kMaxDevices) return 0;
+    if (__atomic_load_n(&g_arch_ok[dev], __ATOMIC_ACQUIRE) == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return 0;
+        const bool gfx950 = strncmp(prop.gcnArchName, "gfx950", 6) == 0 &&
+                            (prop.gcnArchName[6] == 0 || prop.gcnArchName[6] == ':');
+        __atomic_store_n(&g_cus[dev], prop.multiProcessorCount, __ATOMIC_RELAXED);
+        __atomic_store_n(&g_arch_ok[dev], gfx950 ? 1 : 2, __ATOMIC_RELEASE);
+    }
+    if (__atomic_load_n(&g_arch_ok[dev], __ATOMIC_ACQUIRE) != 1) return 0;
+    return __atomic_load_n(&g_cus[dev], __ATOMIC_RELAXED);
 }
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
@@ -223,82 +264,13 @@ int64_t workspace_bytes(int cfg, int64_t M, int64_t N, int splits) {
     return kCounterBytes + tiles * splits * (int64_t)c.bm * c.bn * 4;
 }
 
-// Library-owned split-K workspaces, one per (device, stream): calls on one
-// stream are ordered, so a stream's workspace is never used by two launches at
-// once.  Created on the first split call (zero-filled), grown when needed,
-// kept until the process ends.
-struct OwnedWorkspace {
-    void* ptr = nullptr;
-    int64_t bytes = 0;
-};
-std::mutex g_ws_mutex;
-std::map<std::pair<int, hipStream_t>, OwnedWorkspace> g_ws;
+// Where a call's split-K workspace comes from.
+enum class WsSource { kNone, kCaller };
 
-int owned_workspace(int dev, hipStream_t stream, int64_t bytes, void** out) {
-    std::lock_guard<std::mutex> lock(g_ws_mutex);
-    OwnedWorkspace& w = g_ws[std::make_pair(dev, stream)];
-    if (w.bytes < bytes) {
-        if (w.ptr) {
-            if (hipStreamSynchronize(stream) != hipSuccess) return FP8MM_ERR_LAUNCH;
-            (void)hipFree(w.ptr);
-            w.ptr = nullptr;
-            w.bytes = 0;
-        }
-        void* p = nullptr;
-        if (hipMalloc(&p, (size_t)bytes) != hipSuccess) return FP8MM_ERR_DEVICE;
-        // Counters must start at zero; every launch leaves them at zero.
-        if (hipMemset(p, 0, (size_t)bytes) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
-            (void)hipFree(p);
-            return FP8MM_ERR_DEVICE;
-        }
-        w.ptr = p;
-        w.bytes = bytes;
-    }
-    *out = w.ptr;
-    return FP8MM_OK;
-}
-
-}  // namespace
-
-extern "C" {
-
-int fp8_scaled_mm_num_configs(void) { return kNumConfigs; }
-
-const char* fp8_scaled_mm_config_name(int id) {
-    return (id >= 0 && id < kNumConfigs) ? kConfigs[id].name : "";
-}
-
-int fp8_scaled_mm_select_config(int64_t M, int64_t N, int64_t K, int mode, int has_bias) {
-    if (mode != FP8MM_PER_TENSOR && mode != FP8MM_ROWWISE) return -1;
-    if (M < 0 || N < 0 || K < 16 || K % 16 != 0) return -1;
-    return choose_config(M, N, K, mode, has_bias);
-}
-
-int64_t fp8_scaled_mm_grid_size(int id, int64_t M, int64_t N, int num_cus) {
-    if (id < 0 || id >= kNumConfigs || M <= 0 || N <= 0 || num_cus <= 0) return 0;
-    return grid_for(id, M, N, 1, num_cus);
-}
-
-const char* fp8_scaled_mm_status_string(int s) {
-    switch (s) {
-        case FP8MM_OK: return "ok";
-        case FP8MM_ERR_NULL: return "a required pointer is NULL";
-        case FP8MM_ERR_SHAPE: return "M, N or K out of range (need 0<=M,N<2^31, 16<=K<=2^23, K%16==0)";
-        case FP8MM_ERR_ALIGN: return "misaligned pointer (A,B: 16 B; scales: 4 B; bias,out: 2 B)";
-        case FP8MM_ERR_MODE: return "unknown scaling mode";
-        case FP8MM_ERR_DEVICE: return "no usable gfx950 device";
-        case FP8MM_ERR_LAUNCH: return "kernel launch failed";
-        case FP8MM_ERR_CONFIG: return "unknown tile configuration or split count";
-        case FP8MM_ERR_WORKSPACE: return "workspace smaller than fp8_scaled_mm_workspace_size()";
-        case FP8MM_ERR_FORMAT: return "unknown operand format (FP8MM_E4M3FN or FP8MM_E5M2)";
-        default: return "unknown status";
-    }
-}
-
-int fp8_scaled_mm_typed(const void* A, int a_format, const void* B, int b_format,
-                        const float* scale_a, const float* scale_b, const void* bias, void* out,
-                        int64_t M, int64_t N, int64_t K, int mode, struct ihipStream_t* stream,
-                        int config_id, int splits, void* workspace, int64_t workspace_size) {
+int run_mm(const void* A, int a_format, const void* B, int b_format, const float* scale_a,
+           const float* scale_b, const void* bias, void* out, int64_t M, int64_t N, int64_t K,
+           int mode, struct ihipStream_t* stream, int config_id, int splits, void* workspace,
+           int64_t workspace_size, WsSource src) {
     if ((a_format != FP8MM_E4M3FN && a_format != FP8MM_E5M2) ||
         (b_format != FP8MM_E4M3FN && b_format != FP8MM_E5M2))
         return FP8MM_ERR_FORMAT;
@@ -308,15 +280,22 @@ int fp8_scaled_mm_typed(const void* A, int a_format, const void* B, int b_format
     if (config_id >= kNumConfigs) return FP8MM_ERR_CONFIG;
     if (splits < 0 || splits > 64) return FP8MM_ERR_CONFIG;
     if (M == 0 || N == 0) return FP8MM_OK;
-    const int cfg = config_id >= 0 ? config_id : choose_config(M, N, K, mode, bias != nullptr);
+    // K is split only where the partial tiles have somewhere to go: without a
+    // workspace the automatic plan does not split, and an explicit split
+    // count that still splits after clamping to the K slices is refused.
+    const bool can_split = src != WsSource::kNone;
+    const int cfg = config_id >= 0 ? config_id : choose_config(M, N, K, mode, bias != nullptr, can_split);
     const ConfigInfo& c = kConfigs[cfg];
     const int64_t k_iters = cdiv(K, c.bk);
-    const int sp = plan_splits(cfg, M, N, K, splits);
+    int sp = plan_splits(cfg, M, N, K, can_split || splits > 1 ? splits : 1);
+    if (!can_split && sp > 1) return FP8MM_ERR_WORKSPACE;
     const int64_t tiles = cdiv(M, c.bm) * cdiv(N, c.bn);
     if (tiles * sp > INT32_MAX) return FP8MM_ERR_SHAPE;
     const int64_t ws_need = workspace_bytes(cfg, M, N, sp);
-    if (workspace && workspace_size < ws_need) return FP8MM_ERR_WORKSPACE;
-    if (workspace && ((uintptr_t)workspace & 255)) return FP8MM_ERR_ALIGN;
+    if (src == WsSource::kCaller) {
+        if (workspace_size < ws_need) return FP8MM_ERR_WORKSPACE;
+        if ((uintptr_t)workspace & 255) return FP8MM_ERR_ALIGN;
+    }
 
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess) return FP8MM_ERR_DEVICE;
@@ -324,11 +303,8 @@ int fp8_scaled_mm_typed(const void* A, int a_format, const void* B, int b_format
     if (cus <= 0) return FP8MM_ERR_DEVICE;
     const hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
 
-    void* ws = workspace;
-    if (ws_need > 0 && !ws) {
-        st = owned_workspace(dev, hs, ws_need, &ws);
-        if (st != FP8MM_OK) return st;
-    }
+    void* ws = src == WsSource::kCaller ? workspace : nullptr;
+    (void)hipGetLastError();  // clear a stale error from earlier, unrelated calls
 
     Params p;
     p.A = static_cast<const uint8_t*>(A);
@@ -358,12 +334,61 @@ int fp8_scaled_mm_typed(const void* A, int a_format, const void* B, int b_format
     }
 
     const dim3 grid((unsigned)grid_for(cfg, M, N, sp, cus));
-    (void)hipGetLastError();  // clear a stale error from earlier, unrelated calls
     const LaunchPair& l = kLaunch[fmt][cfg];
     if (p.tiles_m == 1 && l.stream) l.stream(p, grid, hs);
     else l.plain(p, grid, hs);
     if (hipGetLastError() != hipSuccess) return FP8MM_ERR_LAUNCH;
     return FP8MM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fp8_scaled_mm_num_configs(void) { return kNumConfigs; }
+
+const char* fp8_scaled_mm_config_name(int id) {
+    return (id >= 0 && id < kNumConfigs) ? kConfigs[id].name : "";
+}
+
+int fp8_scaled_mm_select_config(int64_t M, int64_t N, int64_t K, int mode, int has_bias,
+                                int with_workspace) {
+    if (mode != FP8MM_PER_TENSOR && mode != FP8MM_ROWWISE) return -1;
+    if (M < 0 || N < 0 || K < 16 || K % 16 != 0) return -1;
+    return choose_config(M, N, K, mode, has_bias, with_workspace != 0);
+}
+
+int64_t fp8_scaled_mm_grid_size(int id, int64_t M, int64_t N, int num_cus) {
+    if (id < 0 || id >= kNumConfigs || M <= 0 || N <= 0 || num_cus <= 0) return 0;
+    return grid_for(id, M, N, 1, num_cus);
+}
+
+const char* fp8_scaled_mm_status_string(int s) {
+    switch (s) {
+        case FP8MM_OK: return "ok";
+        case FP8MM_ERR_NULL: return "a required pointer is NULL";
+        case FP8MM_ERR_SHAPE: return "M, N or K out of range (need 0<=M,N<2^31, 16<=K<=2^23, K%16==0)";
+        case FP8MM_ERR_ALIGN: return "misaligned pointer (A,B: 16 B; scales: 4 B; bias,out: 2 B; workspace: 256 B)";
+        case FP8MM_ERR_MODE: return "unknown scaling mode";
+        case FP8MM_ERR_DEVICE: return "no usable gfx950 device";
+        case FP8MM_ERR_LAUNCH: return "kernel launch failed";
+        case FP8MM_ERR_CONFIG: return "unknown tile configuration or split count";
+        case FP8MM_ERR_WORKSPACE:
+            return "split-K needs a workspace of at least fp8_scaled_mm_workspace_size() bytes";
+        case FP8MM_ERR_FORMAT: return "unknown operand format (FP8MM_E4M3FN or FP8MM_E5M2)";
+        default: return "unknown status";
+    }
+}
+
+const char* fp8mm_status_string(int s) { return fp8_scaled_mm_status_string(s); }
+
+int fp8_scaled_mm_typed(const void* A, int a_format, const void* B, int b_format,
+                        const float* scale_a, const float* scale_b, const void* bias, void* out,
+                        int64_t M, int64_t N, int64_t K, int mode, struct ihipStream_t* stream,
+                        int config_id, int splits, void* workspace, int64_t workspace_size) {
+    return run_mm(A, a_format, B, b_format, scale_a, scale_b, bias, out, M, N, K, mode, stream,
+                  config_id, splits, workspace, workspace_size,
+                  workspace ? WsSource::kCaller : WsSource::kNone);
 }
 
 int fp8_scaled_mm_with_plan(const void* A, const void* B, const float* scale_a,
@@ -393,7 +418,7 @@ int fp8_scaled_mm_select_splits(int64_t M, int64_t N, int64_t K, int mode, int h
                                 int config_id) {
     if (mode != FP8MM_PER_TENSOR && mode != FP8MM_ROWWISE) return -1;
     if (M <= 0 || N <= 0 || K < 16 || K % 16 != 0 || config_id >= kNumConfigs) return -1;
-    const int cfg = config_id >= 0 ? config_id : choose_config(M, N, K, mode, has_bias);
+    const int cfg = config_id >= 0 ? config_id : choose_config(M, N, K, mode, has_bias, true);
     return plan_splits(cfg, M, N, K, 0);
 }
 
@@ -401,7 +426,8 @@ int64_t fp8_scaled_mm_workspace_size(int64_t M, int64_t N, int64_t K, int mode, 
                                      int config_id, int splits) {
     if (mode != FP8MM_PER_TENSOR && mode != FP8MM_ROWWISE) return -1;
     if (M <= 0 || N <= 0 || K < 16 || K % 16 != 0 || config_id >= kNumConfigs) return 0;
-    const int cfg = config_id >= 0 ? config_id : choose_config(M, N, K, mode, has_bias);
+    if (splits < 0 || splits > 64) return 0;
+    const int cfg = config_id >= 0 ? config_id : choose_config(M, N, K, mode, has_bias, true);
     return workspace_bytes(cfg, M, N, plan_splits(cfg, M, N, K, splits));
 }
 

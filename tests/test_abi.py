@@ -26,7 +26,7 @@ def _declared_functions():
     for h in HEADERS:
         text = open(h).read()
         text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-        names |= set(re.findall(r"\b(fp8_\w+)\s*\(", text))
+        names |= set(re.findall(r"\b(fp8(?:mm)?_\w+)\s*\(", text))
     return sorted(names)
 
 
@@ -41,7 +41,9 @@ def test_exports_every_declared_function(L):
 def test_status_strings(L):
     for s in range(10):
         assert binding.status_string(s) != "unknown status"
+        assert L.fp8mm_status_string(s) == L.fp8_scaled_mm_status_string(s)
     assert binding.status_string(99) == "unknown status"
+    assert L.fp8mm_status_string(99) == b"unknown status"
 
 
 def test_configs_listed(L):
@@ -97,10 +99,11 @@ def test_select_config_host_logic(L):
     for shape in [(8192, 8192, 8192), (2048, 2048, 2048), (256, 256, 256), (16, 28672, 8192),
                   (64, 8192, 28672), (128, 28672, 8192), (4095, 4097, 96), (1, 1, 16)]:
         for mode in (0, 1):
-            c = L.fp8_scaled_mm_select_config(*shape, mode, 1)
-            assert 0 <= c < n
-    assert L.fp8_scaled_mm_select_config(16, 16, 16, 3, 0) == -1
-    assert L.fp8_scaled_mm_select_config(16, 16, 24, 0, 0) == -1
+            for ws in (0, 1):
+                c = L.fp8_scaled_mm_select_config(*shape, mode, 1, ws)
+                assert 0 <= c < n
+    assert L.fp8_scaled_mm_select_config(16, 16, 16, 3, 0, 0) == -1
+    assert L.fp8_scaled_mm_select_config(16, 16, 24, 0, 0, 1) == -1
 
 
 def test_grid_size_is_persistent(L):
@@ -126,7 +129,7 @@ def test_workspace_and_split_host_logic(L):
     assert L.fp8_scaled_mm_select_splits(8192, 8192, 8192, 0, 0, -1) == 1
     assert L.fp8_scaled_mm_workspace_size(8192, 8192, 8192, 0, 0, -1, 0) == 0
     # a few tiles with a long K split, and the workspace covers counters + partials
-    cfg = binding.config_names().index("bm128_bn128_bk128_w2x2_s3_mfma32")
+    cfg = binding.config_names().index("bm128_bn128_bk128_w2x2_s2_mfma32")
     s = L.fp8_scaled_mm_select_splits(128, 8192, 28672, 1, 1, cfg)
     assert s > 1
     ws = L.fp8_scaled_mm_workspace_size(128, 8192, 28672, 1, 1, cfg, s)
@@ -141,13 +144,17 @@ def test_workspace_and_split_host_logic(L):
 def test_plan_validation(L):
     P = 0x10000
     f = L.fp8_scaled_mm_with_plan
-    cfg = binding.config_names().index("bm128_bn128_bk128_w2x2_s3_mfma32")
+    cfg = binding.config_names().index("bm128_bn128_bk128_w2x2_s2_mfma32")
     assert f(P, P, P, P, None, P, 128, 128, 4096, 0, None, cfg, 65, None, 0) == binding.ERR_CONFIG
     assert f(P, P, P, P, None, P, 128, 128, 4096, 0, None, cfg, -1, None, 0) == binding.ERR_CONFIG
     # caller workspace too small for a 4-way split
     assert f(P, P, P, P, None, P, 128, 128, 4096, 0, None, cfg, 4, P, 1024) == binding.ERR_WORKSPACE
     need = L.fp8_scaled_mm_workspace_size(128, 128, 4096, 0, 0, cfg, 4)
     assert f(P, P, P, P, None, P, 128, 128, 4096, 0, None, cfg, 4, P + 128, need) == binding.ERR_ALIGN
+    # splitting K needs a caller workspace: the library allocates none
+    assert f(P, P, P, P, None, P, 128, 128, 4096, 0, None, cfg, 4, None, 0) == binding.ERR_WORKSPACE
+    assert L.fp8_scaled_mm_typed(P, 0, P, 0, P, P, None, P, 128, 128, 4096, 0, None, cfg, 2,
+                                 None, 0) == binding.ERR_WORKSPACE
 
 
 # ---- quantiser ---------------------------------------------------------------
@@ -251,10 +258,23 @@ PLANS = {
 
 @pytest.mark.parametrize("shape", list(PLANS), ids=[f"{m}x{n}x{k}" for m, n, k in PLANS])
 def test_plans_of_benchmarked_shapes(L, shape):
+    # with a workspace (the binding supplies one when the plan splits K)
     names = binding.config_names()
     M, N, K = shape
-    cfg = L.fp8_scaled_mm_select_config(M, N, K, 1, 1)
+    cfg = L.fp8_scaled_mm_select_config(M, N, K, 1, 1, 1)
     assert (names[cfg], L.fp8_scaled_mm_select_splits(M, N, K, 1, 1, -1)) == PLANS[shape]
+
+
+@pytest.mark.parametrize("shape", list(PLANS), ids=[f"{m}x{n}x{k}" for m, n, k in PLANS])
+def test_plans_without_workspace(L, shape):
+    # fp8_scaled_mm has no workspace, so it never splits K: its configuration
+    # differs from the plan with a workspace only where that plan splits
+    M, N, K = shape
+    with_ws = L.fp8_scaled_mm_select_config(M, N, K, 1, 1, 1)
+    without = L.fp8_scaled_mm_select_config(M, N, K, 1, 1, 0)
+    if PLANS[shape][1] == 1:
+        assert without == with_ws
+    assert 0 <= without < L.fp8_scaled_mm_num_configs()
 
 
 def _imported_modules(path):

@@ -1,7 +1,6 @@
 """The library's calls captured into a HIP graph (through torch.cuda.CUDAGraph)
 replay to the same bits as the eager calls: they launch kernels only (no host
-synchronisation, no allocation once a stream's split-K workspace exists, no
-memset)."""
+synchronisation, no allocation, no memset)."""
 import numpy as np
 import pytest
 import torch
@@ -39,7 +38,7 @@ def test_graph_replays_match_eager():
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
-        calls()                      # eager, on the capture stream (creates its workspace)
+        calls()                      # eager, on the capture stream (the binding's workspace)
     torch.cuda.synchronize()
     eager = [t.clone() for t in (out_g, out_s, q_rw, s_rw, q_pt, s_pt)]
 

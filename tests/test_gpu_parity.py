@@ -370,8 +370,8 @@ def _cfg(name):
     return binding.config_names().index(name)
 
 
-@pytest.mark.parametrize("config", ["bm128_bn128_bk128_w2x2_s3_mfma32", "bm16_bn64_bk256_w1x4_s4_mfma16",
-                                    "bm64_bn64_bk128_w4x1_s8_mfma16", "bm64_bn112_bk256_w1x7_s3_mfma16",
+@pytest.mark.parametrize("config", ["bm128_bn128_bk128_w2x2_s2_mfma32", "bm16_bn64_bk256_w1x4_s4_mfma16",
+                                    "bm16_bn112_bk256_w1x7_s4_mfma16", "bm64_bn112_bk256_w1x7_s3_mfma16",
                                     "bm64_bn64_bk256_w1x4_s4_mfma16", "bm128_bn128_bk128_w2x4_s4_mfma32",
                                     "pp_bm256_bn256_bk128_w8_mfma16", "bm128_bn32_bk256_w4x2_s3_mfma16",
                                     "bm64_bn32_bk256_w4x2_s4_mfma16", "bm128_bn64_bk256_w4x2_s3_mfma16",
@@ -419,14 +419,14 @@ def run_gpu_plan(inp, config, splits, workspace=None, out=None):
 
 def test_split_k_more_splits_than_slices():
     inp = wl.make_inputs(64, 96, 256, PT, "codes", key=3)
-    got = out_bits(run_gpu_plan(inp, _cfg("bm128_bn128_bk128_w2x2_s3_mfma32"), 16))
+    got = out_bits(run_gpu_plan(inp, _cfg("bm128_bn128_bk128_w2x2_s2_mfma32"), 16))
     ref = oracle.scaled_mm(inp.a, inp.b, inp.scale_a, inp.scale_b, None, PT)
     assert compare(got, ref)[0] == 0
 
 
 def test_split_k_deterministic_and_workspace_equivalent():
     inp = wl.make_inputs(128, 512, 8192, RW, "normal", bias=True, key=11)
-    cfg = _cfg("bm128_bn128_bk128_w2x2_s3_mfma32")
+    cfg = _cfg("bm128_bn128_bk128_w2x2_s2_mfma32")
     r1 = out_bits(run_gpu_plan(inp, cfg, 8))
     r2 = out_bits(run_gpu_plan(inp, cfg, 8))
     need = binding.workspace_size(128, 512, 8192, RW, True, cfg, 8)
@@ -440,7 +440,7 @@ def test_split_k_deterministic_and_workspace_equivalent():
 
 
 def test_split_k_changing_plans_on_one_stream():
-    cfg = _cfg("bm128_bn128_bk128_w2x2_s3_mfma32")
+    cfg = _cfg("bm128_bn128_bk128_w2x2_s2_mfma32")
     # the 1-tile plan leaves non-zero partials right after the counters of a
     # small plan; the 72-tile plan that follows must still find zero counters
     for i, (shape, splits) in enumerate([((256, 384, 2048), 4), ((128, 256, 4096), 2),
@@ -499,7 +499,11 @@ def test_split_k_on_two_streams_at_once():
         assert nbad == 0, (k, nbad, worst, first)
 
 
-@pytest.mark.parametrize("config,splits", [(-1, 0), (10, 1), (8, 1), (2, 1), (8, 3), (16, 2)])
+@pytest.mark.parametrize("config,splits", [(-1, 0), ("pp_bm256_bn256_bk128_w8_mfma16", 1),
+                                           ("bm128_bn128_bk128_w2x4_s4_mfma32", 1),
+                                           ("bm16_bn112_bk256_w1x7_s4_mfma16", 1),
+                                           ("bm128_bn128_bk128_w2x4_s4_mfma32", 3),
+                                           ("bm128_bn128_bk128_w2x2_s2_mfma32", 2)])
 @pytest.mark.parametrize("mode", [PT, RW])
 def test_nan_codes_propagate(config, splits, mode):
     # e4m3fn NaN codes (0x7F, 0xFF) in A and B: every output whose dot
@@ -513,7 +517,7 @@ def test_nan_codes_propagate(config, splits, mode):
     b[33, 0] = 0x7F
     b[519, 639] = 0xFF
     inp = wl.Inputs(a, b, inp.scale_a, inp.scale_b, inp.bias, mode, "e4m3fn", "e4m3fn")
-    got = out_bits(run_gpu_plan(inp, config, splits))
+    got = out_bits(run_gpu_plan(inp, config if config == -1 else _cfg(config), splits))
     ref = ref_mm(inp)
     nbad, worst, first = compare(got, ref)
     assert nbad == 0, (nbad, worst, first)
