@@ -1053,7 +1053,7 @@ using acc_t = Mfma<MI>::acc_t;
 constexpr int FM = 128 / MI, FN = 64 / MI;          // MFMA blocks per wave
 constexpr int KSTEPS = BK / Mfma<MI>::KSTEP;        // MFMA K steps per slice
 constexpr int NOFF = 8;                             // load row groups per wave
-constexpr int EPI_BYTES = BM * 4 + BN * 4 + 1024;  // row scales, column scales, bias (1 KiB slot)
+constexpr int EPI_BYTES = BM * 4 + BN * 4 + BN * 2; // row scales, column scales, bias
 // Output staging: group 0's waves use 4 KiB each after the parameters; group 1's
 // waves use the A-bottom part of stage buffer 1, which is idle while they write
 // their outputs (the next tile's first loads fill buffer 0 and buffer 1's A-top).
@@ -1183,21 +1183,33 @@ __device__ __forceinline__ PpTile pp_tile(const Params& p, int u, int group_m, i
 }
 
 // A unit's epilogue parameters (256 row scales, 256 column scales, 256 bias
-// values) go global -> LDS as three wave-wide 16-byte loads (waves 0, 1, 2 of
-// group 0), like the operand slices: no register holds them and nothing waits
-// for them until the vmcnt waits that cover the slices.  Entries past the
-// last row or column read as zero or as whatever follows in LDS; the
-// epilogue never uses them.  The bias slot is 1 KiB so a full wave fits.
-__device__ __forceinline__ void pp_params_dma(const Params& p, const PpTile& T, int q, int lane,
-                                              bool has_bias, float* epi_sa, float* epi_sb,
-                                              uint16_t* epi_bias) {
-    const uint32_t off = (uint32_t)lane * 16;
-    if (q == 0 && p.rowwise)
-        dma16(make_rsrc(p.scale_a + T.row0, (uint32_t)min(pp::BM, p.M - T.row0) * 4), epi_sa, off, 0);
-    if (q == 1 && p.rowwise)
-        dma16(make_rsrc(p.scale_b + T.col0, (uint32_t)min(pp::BN, p.N - T.col0) * 4), epi_sb, off, 0);
-    if (q == 2 && has_bias)
-        dma16(make_rsrc(p.bias + T.col0, (uint32_t)min(pp::BN, p.N - T.col0) * 2), epi_bias, off, 0);
+// values), one of each per thread of group 0 (tid 0..255): loaded into
+// registers with the unit's first slices and written to the LDS parameter
+// area once those loads have been waited for.  Entries past the last row or
+// column are 0 (the epilogue never uses them).  Element loads, not 16-byte
+// LDS-direct ones: the bias is only 2-byte aligned, and a 16-byte load whose
+// record limit ends inside a dword reads that whole dword as zero (with an
+// odd number of columns left, the last bias value would be lost).
+struct PpParams {
+    float sa, sb;
+    uint16_t bias;
+};
+
+__device__ __forceinline__ PpParams pp_params_load(const Params& p, const PpTile& T, int t,
+                                                   bool has_bias) {
+    PpParams v;
+    const bool row_ok = T.row0 + t < p.M, col_ok = T.col0 + t < p.N;
+    v.sa = (p.rowwise && row_ok) ? p.scale_a[T.row0 + t] : 0.f;
+    v.sb = (p.rowwise && col_ok) ? p.scale_b[T.col0 + t] : 0.f;
+    v.bias = (has_bias && col_ok) ? p.bias[T.col0 + t] : (uint16_t)0;
+    return v;
+}
+
+__device__ __forceinline__ void pp_params_store(const PpParams& v, int t, float* epi_sa,
+                                                float* epi_sb, uint16_t* epi_bias) {
+    epi_sa[t] = v.sa;
+    epi_sb[t] = v.sb;
+    epi_bias[t] = v.bias;
 }
 
 // A unit's first loads, all from group 0 (wave q): its first K slice whole
@@ -1396,12 +1408,16 @@ __global__ void __launch_bounds__(pp::THREADS) fp8_gemm_pp_kernel(Params p) {
     int parity = 0;
     PpTile T = pp_tile(p, wg, GROUP_M, xcd);
     if (grp == 0) {
-        float *sa, *sb;
-        uint16_t* bias;
-        epi_area(0, sa, sb, bias);
-        if (need_epi) pp_params_dma(p, T, q, pp_lane(), has_bias, sa, sb, bias);
+        PpParams pv;
+        if (need_epi) pv = pp_params_load(p, T, tid, has_bias);
         pp_tile_start(smem, p, T, L, q);
         wait_vmcnt<0>();
+        if (need_epi) {
+            float *sa, *sb;
+            uint16_t* bias;
+            epi_area(0, sa, sb, bias);
+            pp_params_store(pv, tid, sa, sb, bias);
+        }
     }
     barrier_lds();
     __builtin_amdgcn_sched_barrier(0);
@@ -1450,18 +1466,20 @@ __global__ void __launch_bounds__(pp::THREADS) fp8_gemm_pp_kernel(Params p) {
             __builtin_amdgcn_sched_barrier(0);
             if (un < num_units) {
                 T = pp_tile(p, un, GROUP_M, xcd);
-                if (need_epi) {
-                    float *sa, *sb;
-                    uint16_t* bias;
-                    epi_area(parity ^ 1, sa, sb, bias);
-                    pp_params_dma(p, T, q, pp_lane(), has_bias, sa, sb, bias);
-                }
+                PpParams pv;
+                if (need_epi) pv = pp_params_load(p, T, tid, has_bias);
                 pp_tile_start(smem, p, T, L, q);
                 // The next unit's first reads take rows of A-top and B that
                 // all four waves of this group loaded: every wave's loads must
                 // have landed (own wait, then the barrier) before any reads.
                 // Group 1 joins this barrier at the end of its unit.
                 wait_vmcnt<0>();
+                if (need_epi) {
+                    float *sa, *sb;
+                    uint16_t* bias;
+                    epi_area(parity ^ 1, sa, sb, bias);
+                    pp_params_store(pv, tid, sa, sb, bias);
+                }
                 barrier_lds();
             }
             __builtin_amdgcn_sched_barrier(0);

@@ -525,3 +525,28 @@ def test_nan_codes_propagate(config, splits, mode):
     assert np.isnan(vals[5]).all() and np.isnan(vals[211]).all()
     assert np.isnan(vals[:, 33]).all() and np.isnan(vals[:, 519]).all()
     assert np.isfinite(np.delete(np.delete(vals, [5, 211], 0), [33, 519], 1)).all()
+
+
+@pytest.mark.parametrize("config", _configs(), ids=_config_ids())
+@pytest.mark.parametrize("N", [375, 257, 519, 8])
+@pytest.mark.parametrize("mode", [PT, RW])
+def test_zero_a_gives_the_bias_in_every_column(config, N, mode):
+    # A = 0: every output is exactly bf16(bias[n]) (the fp32 accumulator is 0,
+    # so fma(0, s, bias) = bias).  Odd and even numbers of columns in the last
+    # column tile, and a bias that is only 2-byte aligned: no bias value may
+    # be lost or shifted.  (A 16-byte LDS-direct load of the bias whose record
+    # limit ended inside a dword once read the last bias value as 0.)
+    M, K = 300, 128
+    inp = wl.make_inputs(M, N, K, mode, "codes", bias=True, key=N + 7 * mode + 13 * config)
+    a = torch.zeros((M, K), dtype=torch.uint8, device=DEV)
+    b, sa, sb = _to_dev(inp.b), _to_dev(inp.scale_a), _to_dev(inp.scale_b)
+    buf = torch.empty(N + 1, dtype=torch.bfloat16, device=DEV)
+    bias = buf[1:]                                          # 2-byte aligned, not 4
+    bias.copy_(_to_dev(inp.bias))
+    assert bias.data_ptr() % 4 == 2
+    out = binding.fp8_scaled_mm(a, b, sa, sb, bias, mode=mode, config=config)
+    torch.cuda.synchronize()
+    got = out_bits(out)
+    want = np.broadcast_to(inp.bias, (M, N))
+    bad = np.argwhere(got != want)
+    assert bad.size == 0, f"{len(bad)} outputs differ from the bias, first at {tuple(bad[0])}"
