@@ -84,7 +84,8 @@ enum fp8mm_status {
     FP8MM_ERR_LAUNCH = 6,  /* the kernel launch failed */
     FP8MM_ERR_CONFIG = 7,  /* unknown tile configuration id or split count */
     FP8MM_ERR_WORKSPACE = 8, /* caller workspace smaller than required */
-    FP8MM_ERR_FORMAT = 9     /* unknown operand format */
+    FP8MM_ERR_FORMAT = 9,    /* unknown operand format */
+    FP8MM_ERR_SCRATCH = 10   /* fp8_scaled_mm_noalloc: plan larger than its scratch */
 };
 
 /* Operand formats (OCP 8-bit floating point).  The gist "matmul_fp8.py",
@@ -138,6 +139,26 @@ int fp8_scaled_mm_typed(const void* A, int a_format, const void* B, int b_format
                         void* out, int64_t M, int64_t N, int64_t K, int scaling_mode,
                         struct ihipStream_t* stream, int config_id, int splits, void* workspace,
                         int64_t workspace_bytes);
+
+/* For callers that cannot allocate (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation): fp8_scaled_mm_with_plan
+ * (config_id < 0 / splits == 0: automatic, as there) whose split-K counters
+ * and partial tiles live in a 64 MiB static device array of the library
+ * instead of a caller workspace.  Each GPU the library runs on holds its own
+ * copy from module load until the process ends; the call allocates nothing
+ * and only enqueues kernels (a small kernel that zeroes the counters its plan
+ * uses, then the multiply).  The array's device address is looked up once
+ * per device, on the first call there.  The automatic plan splits only as
+ * far as its partial tiles fit in the array; an explicit split count whose
+ * plan does not fit returns FP8MM_ERR_SCRATCH with nothing enqueued.  Every
+ * call on a GPU shares that GPU's array: calls that can overlap on one GPU
+ * (different streams, or several host threads) race and may give wrong
+ * results; calls on one stream are ordered and safe.  Operand formats are
+ * e4m3fn; the rest of the contract is fp8_scaled_mm_with_plan's. */
+int fp8_scaled_mm_noalloc(const void* A, const void* B, const float* scale_a,
+                          const float* scale_b, const void* bias_or_null, void* out, int64_t M,
+                          int64_t N, int64_t K, int scaling_mode, struct ihipStream_t* stream,
+                          int config_id, int splits);
 
 /* Workspace bytes the plan (config_id, splits; negative/zero = automatic)
  * needs for this problem when the call has a workspace; 0 when it does not

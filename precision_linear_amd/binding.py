@@ -27,11 +27,12 @@ _FORMATS = {"e4m3fn": E4M3FN, "e5m2": E5M2, E4M3FN: E4M3FN, E5M2: E5M2}
 
 # status codes from include/fp8_scaled_mm.h
 (OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_MODE, ERR_DEVICE, ERR_LAUNCH, ERR_CONFIG, ERR_WORKSPACE,
- ERR_FORMAT) = range(10)
-_ARG_ERRORS = {ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_MODE, ERR_CONFIG, ERR_WORKSPACE, ERR_FORMAT}
+ ERR_FORMAT, ERR_SCRATCH) = range(11)
+_ARG_ERRORS = {ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_MODE, ERR_CONFIG, ERR_WORKSPACE, ERR_FORMAT,
+               ERR_SCRATCH}
 
 EXPORTS = ("fp8_scaled_mm", "fp8_scaled_mm_with_config", "fp8_scaled_mm_with_plan",
-           "fp8_scaled_mm_typed",
+           "fp8_scaled_mm_typed", "fp8_scaled_mm_noalloc",
            "fp8_scaled_mm_workspace_size", "fp8_scaled_mm_select_splits",
            "fp8_scaled_mm_num_configs", "fp8_scaled_mm_config_name", "fp8_scaled_mm_select_config",
            "fp8_scaled_mm_grid_size", "fp8_scaled_mm_status_string", "fp8mm_status_string",
@@ -70,6 +71,8 @@ def lib() -> ctypes.CDLL:
         L.fp8_scaled_mm_typed.argtypes = [vp, i32, vp, i32, vp, vp, vp, vp, i64, i64, i64, i32, vp,
                                           i32, i32, vp, i64]
         L.fp8_scaled_mm_typed.restype = i32
+        L.fp8_scaled_mm_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, vp, i32, i32]
+        L.fp8_scaled_mm_noalloc.restype = i32
         L.fp8_scaled_mm_workspace_size.argtypes = [i64, i64, i64, i32, i32, i32, i32]
         L.fp8_scaled_mm_workspace_size.restype = i64
         L.fp8_scaled_mm_select_splits.argtypes = [i64, i64, i64, i32, i32, i32]

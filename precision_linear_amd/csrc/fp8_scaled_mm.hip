@@ -264,8 +264,39 @@ int64_t workspace_bytes(int cfg, int64_t M, int64_t N, int splits) {
     return kCounterBytes + tiles * splits * (int64_t)c.bm * c.bn * 4;
 }
 
+// Device scratch for fp8_scaled_mm_noalloc: its split-K counters and partial
+// tiles, for callers that cannot allocate.  Each GPU the library runs on
+// holds one copy from module load until the process ends; every call on that
+// GPU shares it.  In host code `scratch` names a host-side stand-in, not the
+// device memory: kernels and copies get the device address that
+// hipGetSymbolAddress returns, resolved once per device.
+constexpr int64_t kScratchBytes = int64_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices];
+
+// The device address of `scratch` on device `dev` (the current device), or
+// null if the runtime cannot give it.
+void* scratch_on(int dev) {
+    if (dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+        g_scratch_ptr[dev] = ptr;
+    }
+    return g_scratch_ptr[dev];
+}
+
+// Zeroes n arrival counters (a kernel, not a memset, so that it can be
+// captured into a graph like the multiply that follows it).
+__global__ void __launch_bounds__(256) clear_counters_kernel(unsigned* c, int n) {
+    for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) c[i] = 0u;
+}
+
 // Where a call's split-K workspace comes from.
-enum class WsSource { kNone, kCaller };
+enum class WsSource { kNone, kCaller, kScratch };
 
 int run_mm(const void* A, int a_format, const void* B, int b_format, const float* scale_a,
            const float* scale_b, const void* bias, void* out, int64_t M, int64_t N, int64_t K,
@@ -289,6 +320,11 @@ int run_mm(const void* A, int a_format, const void* B, int b_format, const float
     const int64_t k_iters = cdiv(K, c.bk);
     int sp = plan_splits(cfg, M, N, K, can_split || splits > 1 ? splits : 1);
     if (!can_split && sp > 1) return FP8MM_ERR_WORKSPACE;
+    if (src == WsSource::kScratch && workspace_bytes(cfg, M, N, sp) > kScratchBytes) {
+        if (splits > 1) return FP8MM_ERR_SCRATCH;       // asked for a plan that does not fit
+        while (sp > 1 && workspace_bytes(cfg, M, N, sp) > kScratchBytes)
+            sp = plan_splits(cfg, M, N, K, sp - 1);
+    }
     const int64_t tiles = cdiv(M, c.bm) * cdiv(N, c.bn);
     if (tiles * sp > INT32_MAX) return FP8MM_ERR_SHAPE;
     const int64_t ws_need = workspace_bytes(cfg, M, N, sp);
@@ -305,6 +341,16 @@ int run_mm(const void* A, int a_format, const void* B, int b_format, const float
 
     void* ws = src == WsSource::kCaller ? workspace : nullptr;
     (void)hipGetLastError();  // clear a stale error from earlier, unrelated calls
+    if (src == WsSource::kScratch && sp > 1) {
+        ws = scratch_on(dev);
+        if (!ws) return FP8MM_ERR_DEVICE;
+        // The scratch keeps whatever the last call on this GPU left in it:
+        // the counters this plan uses start from zero.
+        const int n = (int)(tiles * counters_per_tile(cfg));
+        const int blocks = (n + 255) / 256 < 256 ? (n + 255) / 256 : 256;
+        hipLaunchKernelGGL(clear_counters_kernel, dim3(blocks), dim3(256), 0, hs,
+                           static_cast<unsigned*>(ws), n);
+    }
 
     Params p;
     p.A = static_cast<const uint8_t*>(A);
@@ -376,6 +422,9 @@ const char* fp8_scaled_mm_status_string(int s) {
         case FP8MM_ERR_WORKSPACE:
             return "split-K needs a workspace of at least fp8_scaled_mm_workspace_size() bytes";
         case FP8MM_ERR_FORMAT: return "unknown operand format (FP8MM_E4M3FN or FP8MM_E5M2)";
+        case FP8MM_ERR_SCRATCH:
+            return "the requested split-K plan needs more than the 64 MiB device scratch of "
+                   "fp8_scaled_mm_noalloc";
         default: return "unknown status";
     }
 }
@@ -412,6 +461,14 @@ int fp8_scaled_mm(const void* A, const void* B, const float* scale_a, const floa
                   struct ihipStream_t* stream) {
     return fp8_scaled_mm_with_plan(A, B, scale_a, scale_b, bias, out, M, N, K, mode, stream, -1, 0,
                                    nullptr, 0);
+}
+
+int fp8_scaled_mm_noalloc(const void* A, const void* B, const float* scale_a,
+                          const float* scale_b, const void* bias, void* out, int64_t M, int64_t N,
+                          int64_t K, int mode, struct ihipStream_t* stream, int config_id,
+                          int splits) {
+    return run_mm(A, FP8MM_E4M3FN, B, FP8MM_E4M3FN, scale_a, scale_b, bias, out, M, N, K, mode,
+                  stream, config_id, splits, nullptr, 0, WsSource::kScratch);
 }
 
 int fp8_scaled_mm_select_splits(int64_t M, int64_t N, int64_t K, int mode, int has_bias,

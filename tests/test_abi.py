@@ -39,7 +39,7 @@ def test_exports_every_declared_function(L):
 
 
 def test_status_strings(L):
-    for s in range(10):
+    for s in range(11):
         assert binding.status_string(s) != "unknown status"
         assert L.fp8mm_status_string(s) == L.fp8_scaled_mm_status_string(s)
     assert binding.status_string(99) == "unknown status"

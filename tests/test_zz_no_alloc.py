@@ -1,0 +1,91 @@
+"""fp8_scaled_mm_noalloc -- the entry point for callers that cannot allocate
+-- against fp8_scaled_mm_with_plan (the same tile configuration and split
+count, with a caller workspace), through the C ABI: two calls in a row on the
+same GPU (so the second finds the scratch as the first left it), the second
+with a smaller problem; both bit-identical to the workspace form and within
+the oracle's tolerance."""
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+from precision_linear_amd import binding
+from precision_linear_amd import workloads as wl
+from parity import compare
+from test_gpu_parity import _to_dev, out_bits, ref_mm
+
+pytestmark = pytest.mark.gpu
+PT, RW = wl.PER_TENSOR, wl.ROWWISE
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _args(inp):
+    return [_to_dev(x) for x in (inp.a, inp.b, inp.scale_a, inp.scale_b, inp.bias)]
+
+
+def _noalloc(L, args, out, inp, config, splits):
+    a, b, sa, sb, bias = args
+    M, N, K = inp.shape
+    return L.fp8_scaled_mm_noalloc(_ptr(a), _ptr(b), _ptr(sa), _ptr(sb), _ptr(bias), _ptr(out),
+                                   M, N, K, inp.mode,
+                                   ctypes.c_void_p(torch.cuda.current_stream().cuda_stream),
+                                   config, splits)
+
+
+def _with_plan(L, args, out, inp, config, splits):
+    a, b, sa, sb, bias = args
+    M, N, K = inp.shape
+    need = L.fp8_scaled_mm_workspace_size(M, N, K, inp.mode, int(bias is not None), config, splits)
+    ws = torch.zeros(max(need, 256), dtype=torch.uint8, device="cuda")
+    st = L.fp8_scaled_mm_with_plan(_ptr(a), _ptr(b), _ptr(sa), _ptr(sb), _ptr(bias), _ptr(out),
+                                   M, N, K, inp.mode,
+                                   ctypes.c_void_p(torch.cuda.current_stream().cuda_stream),
+                                   config, splits, _ptr(ws), ws.numel())
+    return st, ws
+
+
+CASES = [
+    # (first, second): the second call is smaller than the first
+    (((128, 8192, 28672, RW, True, "skinny"), -1, 0), ((64, 2048, 8192, RW, True, "skinny"), -1, 0)),
+    (((520, 768, 4160, PT, False, "codes"), "pp_bm256_bn256_bk128_w8_mfma16", 3),
+     ((300, 260, 1040, RW, True, "codes"), "pp_bm256_bn256_bk128_w8_mfma16", 2)),
+    (((150, 230, 1040, RW, True, "codes"), "bm128_bn32_bk256_w4x2_s3_mfma16", 4),
+     ((16, 200, 1040, PT, False, "codes"), "bm16_bn32_bk512_w1x2_s6_mfma16", 2)),
+]
+
+
+@pytest.mark.parametrize("case", range(len(CASES)))
+def test_noalloc_matches_the_workspace_form(case):
+    L = binding.lib()
+    names = binding.config_names()
+    for k, ((M, N, K, mode, bias, recipe), config, splits) in enumerate(CASES[case]):
+        cfg = names.index(config) if isinstance(config, str) else config
+        inp = wl.make_inputs(M, N, K, mode, recipe, bias=bias, key=500 + 10 * case + k)
+        print(f"[noalloc] case {case} call {k}: shape={inp.shape} mode={mode} bias={bias} "
+              f"config={cfg} splits={splits}", flush=True)
+        args = _args(inp)
+        out_n = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+        out_w = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+        assert _noalloc(L, args, out_n, inp, cfg, splits) == binding.OK
+        st, ws = _with_plan(L, args, out_w, inp, cfg, splits)
+        assert st == binding.OK
+        torch.cuda.synchronize()
+        if splits == 0:
+            assert binding.select_splits(M, N, K, mode, bias, cfg) > 1   # the plan does split
+        assert torch.equal(out_n.view(torch.int16), out_w.view(torch.int16))
+        nbad, worst, first = compare(out_bits(out_n), ref_mm(inp))
+        assert nbad == 0, (nbad, worst, first)
+
+
+def test_noalloc_plan_beyond_the_scratch_is_refused():
+    # 1024 tiles of 256 x 256, 3 splits: 768 MiB of partial tiles > 64 MiB
+    L = binding.lib()
+    P = 0x10000
+    pp = binding.config_names().index("pp_bm256_bn256_bk128_w8_mfma16")
+    st = L.fp8_scaled_mm_noalloc(P, P, P, P, None, P, 8192, 8192, 8192, 0, None, pp, 3)
+    assert st == binding.ERR_SCRATCH
+    assert "scratch" in binding.status_string(st)
