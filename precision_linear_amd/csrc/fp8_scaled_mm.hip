@@ -369,7 +369,6 @@ int run_mm(const void* A, int a_format, const void* B, int b_format, const float
     p.rowwise = mode == FP8MM_ROWWISE;
     p.vec_store = (N % 4 == 0) && aligned(out, 8);
     p.vec16 = (N % 8 == 0) && aligned(out, 16);
-    p.vec4 = (N % 2 == 0) && aligned(out, 4);
     p.splits = sp;
     p.k_chunk = (int)cdiv(k_iters, sp);
     p.counters = nullptr;
