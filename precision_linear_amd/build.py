@@ -4,6 +4,8 @@ quantiser -- and their C ABI) for gfx950.
 hipcc cross-compiles without a GPU.  The library is written next to this
 file so that it travels with the source tree.
 """
+from __future__ import annotations
+
 import os
 import shutil
 import subprocess
@@ -37,23 +39,39 @@ def _run(cmd, verbose):
         sys.stderr.write(res.stderr)
 
 
-def build(verbose: bool = False) -> str:
+# Host-only sanitizer instrumentation (AddressSanitizer + UndefinedBehavior-
+# Sanitizer) for the translation units whose host code is the C ABI's logic
+# (argument validation, plan and workspace arithmetic); device code is built
+# as usual.  Every -fsanitize flag is scoped to the host compilation.
+SANITIZE_HOST = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                 "-Xarch_host", "-fno-sanitize-recover=undefined",
+                 "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-g"]
+HOST_LOGIC_SRCS = {"fp8_scaled_mm.hip", "fp8_quantize.hip"}
+
+
+def build(verbose: bool = False, sanitize: bool = False, out: str | None = None) -> str:
     """Compile every source to an object (in parallel), then link the
-    shared library; always rebuilds."""
+    shared library; always rebuilds.  sanitize=True builds the host logic
+    with ASan/UBSan (a test build, loaded with the sanitizer runtime
+    preloaded) into `out` instead of the package's library."""
     from concurrent.futures import ThreadPoolExecutor
+    target = out or LIB
     objdir = tempfile.mkdtemp(prefix="fp8mm_build_")
     try:
         objs = [os.path.join(objdir, os.path.basename(src) + ".o") for src in SRCS]
-        jobs = [[HIPCC, *FLAGS, "-c", src, "-o", obj] for src, obj in zip(SRCS, objs)]
+        jobs = []
+        for src, obj in zip(SRCS, objs):
+            extra = SANITIZE_HOST if sanitize and os.path.basename(src) in HOST_LOGIC_SRCS else []
+            jobs.append([HIPCC, *FLAGS, *extra, "-c", src, "-o", obj])
         workers = max(1, min(len(jobs), os.cpu_count() or 1))
         with ThreadPoolExecutor(max_workers=workers) as ex:
             list(ex.map(lambda c: _run(c, verbose), jobs))
-        tmp = LIB + ".tmp"
+        tmp = target + ".tmp"
         _run([HIPCC, "--offload-arch=gfx950", "-shared", *objs, "-o", tmp], verbose)
-        shutil.move(tmp, LIB)
+        shutil.move(tmp, target)
     finally:
         shutil.rmtree(objdir, ignore_errors=True)
-    return LIB
+    return target
 
 
 if __name__ == "__main__":
