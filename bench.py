@@ -20,8 +20,9 @@ The JSON line also carries
                 timed on its own, reported as p50 with p20 / p80) for both
                 headline modes, once with a 1 GiB buffer read before every
                 run (the 256 MB MALL holds nothing of the operands) and once
-                with the operands left in the caches; plus the shader clock
-                observed under the headline load;
+                with the operands left in the caches (the shader clock under
+                this load comes from a counter run: GRBM_GUI_ACTIVE per XCD over
+                the launch time, in the kernel-trace summary under profiles/);
   cpu_baseline  the CPU oracle timed on this host's cores on one whole step
                 (both 8192^3 multiplies, every output element);
   parity        each timed workload's GPU output against that oracle run,
@@ -40,7 +41,6 @@ import hashlib
 import json
 import os
 import sys
-import threading
 import time
 
 import numpy as np
@@ -189,70 +189,6 @@ def gist_protocol(problem, flush):
     r = quantiles(ts)
     r["tflops_p50"] = round(problem.w.flops / (r["p50_us"] * 1e-6) / 1e12, 1)
     return r
-
-
-def observe_clock(problems, ms=250.0):
-    """The shader (GFX) clock while the headline multiplies run back to back:
-    a side thread reads the GPU's metrics every few ms while about `ms` of
-    launches drain."""
-    import torch
-    try:
-        import amdsmi
-        amdsmi.amdsmi_init()
-        h = amdsmi.amdsmi_get_processor_handles()[0]
-    except Exception as e:
-        return {"error": f"amdsmi unavailable: {type(e).__name__}"}
-
-    def read():
-        try:
-            m = amdsmi.amdsmi_get_gpu_metrics_info(h)
-            for k in ("current_gfxclks", "current_gfxclk", "average_gfxclk_frequency"):
-                v = m.get(k)
-                if isinstance(v, (list, tuple)):
-                    v = [x for x in v if isinstance(x, (int, float)) and 0 < x < 10000]
-                    if v:
-                        return float(np.mean(v)), k
-                elif isinstance(v, (int, float)) and 0 < v < 10000:
-                    return float(v), k
-        except Exception:
-            pass
-        try:
-            c = amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.SYS)
-            return float(c["clk"]), "clock_info SYS"
-        except Exception:
-            return None, None
-
-    per_launch_ms = 0.36
-    n = max(8, int(ms / per_launch_ms / len(problems)))
-    samples, source = [], [None]
-    stop = threading.Event()
-
-    def poll():
-        while not stop.is_set():
-            v, k = read()
-            if v is not None:
-                samples.append(v)
-                source[0] = k
-            time.sleep(0.003)
-
-    for _ in range(n):
-        for p in problems:
-            p.launch()
-    th = threading.Thread(target=poll)
-    th.start()
-    torch.cuda.synchronize()
-    stop.set()
-    th.join()
-    try:
-        amdsmi.amdsmi_shut_down()
-    except Exception:
-        pass
-    if not samples:
-        return {"error": "no clock samples"}
-    # the first samples can predate the metrics' refresh: drop the first 10%
-    s = samples[len(samples) // 10:] or samples
-    return {"gfx_mhz_mean": round(float(np.mean(s)), 1), "gfx_mhz_min": round(float(np.min(s)), 1),
-            "gfx_mhz_max": round(float(np.max(s)), 1), "samples": len(s), "source": source[0]}
 
 
 def skinny_results(dev, reps=20, keep=None):
@@ -652,7 +588,6 @@ def main():
         "runs": "1 untimed + 8 warm-up + 32 timed, one HIP event pair each",
         "flushed": {p.name: gist_protocol(p, flush) for p in probs},
         "resident": {p.name: gist_protocol(p, None) for p in probs},
-        "clock": observe_clock(probs),
     }
     del flush
     torch.cuda.empty_cache()
