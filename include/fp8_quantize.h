@@ -26,8 +26,10 @@
  * Pointers are DEVICE pointers on the current HIP device; the caller owns them
  * and the library keeps none after the call.  The library allocates nothing.
  * Execution is asynchronous on `stream` (a hipStream_t; NULL = default).  The
- * per-tensor mode uses scale[0] as its running maximum while the call's
- * kernels run.
+ * per-tensor mode of fp8_quantize_e4m3 / _e5m2 reads x twice (a maximum pass,
+ * then the conversion); while its kernels run, the first 4 bytes per
+ * workgroup of q hold the workgroups' partial maxima, which the conversion
+ * then overwrites.  The _ws entry points below read x once.
  *
  * Preconditions (checked on the host before anything is enqueued):
  *   0 <= rows, cols <= 2^31, cols % 16 == 0; x and q 16-byte aligned, scale
@@ -58,7 +60,8 @@ enum fp8q_status {
     FP8Q_ERR_ALIGN = 3,  /* a pointer is not aligned as required */
     FP8Q_ERR_MODE = 4,   /* unknown scaling_mode */
     FP8Q_ERR_DEVICE = 5, /* no usable HIP device */
-    FP8Q_ERR_LAUNCH = 6  /* a kernel launch failed */
+    FP8Q_ERR_LAUNCH = 6, /* a kernel launch failed */
+    FP8Q_ERR_WORKSPACE = 7 /* workspace smaller than fp8_quantize_workspace_size() */
 };
 
 /* Quantise x into (q, scale) as described above. */
@@ -72,6 +75,46 @@ int fp8_quantize_e4m3(const void* x, void* q, float* scale, int64_t rows, int64_
  * what fp8_scaled_mm_typed takes with FP8MM_E5M2. */
 int fp8_quantize_e5m2(const void* x, void* q, float* scale, int64_t rows, int64_t cols,
                       int scaling_mode, struct ihipStream_t* stream);
+
+/* Bytes of workspace the _ws entry points need for these arguments: 67840
+ * for a per-tensor call with elements, else 0 (row-wise mode and empty matrices
+ * use none). */
+int64_t fp8_quantize_workspace_size(int64_t rows, int64_t cols, int scaling_mode);
+
+/* The same operation as fp8_quantize_e4m3 / fp8_quantize_e5m2 (same results,
+ * bit for bit), with a caller workspace that lets the per-tensor mode read x
+ * once: one workgroup per CU holds its share of x in registers and LDS while
+ * the maximum is formed across the grid, then converts it.
+ *
+ *   workspace        device memory, 4-byte aligned, at least
+ *                    fp8_quantize_workspace_size() bytes, ZERO-FILLED before
+ *                    its first use.  Every call sets its counters and flags
+ *                    back to zero once the stream has run it, so one buffer
+ *                    serves all calls ordered on one stream; calls that may
+ *                    run at the same time need separate buffers.  NULL: the two-pass path
+ *                    of fp8_quantize_e4m3 (no workspace is used).
+ *   workspace_bytes  its size in bytes.
+ *
+ * The grid-wide wait of the one-pass kernel is bounded: if other work holds
+ * CUs so that the kernel's workgroups cannot all run at once, a workgroup that
+ * has waited 1 ms (see fp8_quantize_set_wait_limit_us) leaves its share to the
+ * last workgroup to reach the wait, which re-reads and converts it.  Only the
+ * time changes.
+ * Errors: as fp8_quantize_e4m3, plus FP8Q_ERR_WORKSPACE (workspace non-NULL
+ * and smaller than needed) and FP8Q_ERR_ALIGN (workspace not 4-byte aligned);
+ * nothing is enqueued then.  Row-wise calls ignore the workspace. */
+int fp8_quantize_e4m3_ws(const void* x, void* q, float* scale, int64_t rows, int64_t cols,
+                         int scaling_mode, void* workspace, int64_t workspace_bytes,
+                         struct ihipStream_t* stream);
+int fp8_quantize_e5m2_ws(const void* x, void* q, float* scale, int64_t rows, int64_t cols,
+                         int scaling_mode, void* workspace, int64_t workspace_bytes,
+                         struct ihipStream_t* stream);
+
+/* Test hook: the one-pass kernel's wait limit, in microseconds, for calls
+ * enqueued after this one (process-wide, not thread-safe).  0 makes every
+ * workgroup but the last to arrive leave its share to that one; a negative
+ * value restores the default of 1000.  Returns the previous limit. */
+int64_t fp8_quantize_set_wait_limit_us(int64_t us);
 
 /* Static, NUL-terminated text for a status code. */
 const char* fp8_quantize_status_string(int status);

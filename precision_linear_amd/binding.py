@@ -36,11 +36,14 @@ EXPORTS = ("fp8_scaled_mm", "fp8_scaled_mm_with_config", "fp8_scaled_mm_with_pla
            "fp8_scaled_mm_workspace_size", "fp8_scaled_mm_select_splits",
            "fp8_scaled_mm_num_configs", "fp8_scaled_mm_config_name", "fp8_scaled_mm_select_config",
            "fp8_scaled_mm_grid_size", "fp8_scaled_mm_status_string", "fp8mm_status_string",
-           "fp8_quantize_e4m3", "fp8_quantize_e5m2", "fp8_quantize_status_string")
+           "fp8_quantize_e4m3", "fp8_quantize_e5m2", "fp8_quantize_e4m3_ws", "fp8_quantize_e5m2_ws",
+           "fp8_quantize_workspace_size", "fp8_quantize_set_wait_limit_us",
+           "fp8_quantize_status_string")
 
 # status codes from include/fp8_quantize.h
-Q_OK, Q_ERR_NULL, Q_ERR_SHAPE, Q_ERR_ALIGN, Q_ERR_MODE, Q_ERR_DEVICE, Q_ERR_LAUNCH = range(7)
-_Q_ARG_ERRORS = {Q_ERR_NULL, Q_ERR_SHAPE, Q_ERR_ALIGN, Q_ERR_MODE}
+(Q_OK, Q_ERR_NULL, Q_ERR_SHAPE, Q_ERR_ALIGN, Q_ERR_MODE, Q_ERR_DEVICE, Q_ERR_LAUNCH,
+ Q_ERR_WORKSPACE) = range(8)
+_Q_ARG_ERRORS = {Q_ERR_NULL, Q_ERR_SHAPE, Q_ERR_ALIGN, Q_ERR_MODE, Q_ERR_WORKSPACE}
 
 
 class Fp8MMError(RuntimeError):
@@ -93,6 +96,13 @@ def lib() -> ctypes.CDLL:
         L.fp8_quantize_e4m3.restype = i32
         L.fp8_quantize_e5m2.argtypes = [vp, vp, vp, i64, i64, i32, vp]
         L.fp8_quantize_e5m2.restype = i32
+        for name in ("fp8_quantize_e4m3_ws", "fp8_quantize_e5m2_ws"):
+            getattr(L, name).argtypes = [vp, vp, vp, i64, i64, i32, vp, i64, vp]
+            getattr(L, name).restype = i32
+        L.fp8_quantize_workspace_size.argtypes = [i64, i64, i32]
+        L.fp8_quantize_workspace_size.restype = i64
+        L.fp8_quantize_set_wait_limit_us.argtypes = [i64]
+        L.fp8_quantize_set_wait_limit_us.restype = i64
         L.fp8_quantize_status_string.argtypes = [i32]
         L.fp8_quantize_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -134,8 +144,8 @@ def workspace_size(M, N, K, mode, has_bias=False, config=-1, splits=0) -> int:
 _workspaces: dict = {}
 
 
-def _workspace(device: torch.device, stream: int, nbytes: int) -> torch.Tensor:
-    key = (device.index, stream)
+def _workspace(device: torch.device, stream: int, nbytes: int, kind: str = "mm") -> torch.Tensor:
+    key = (device.index, stream, kind)
     have = _workspaces.get(key)
     if have and have[-1].numel() >= nbytes:
         return have[-1]
@@ -246,17 +256,19 @@ def fp8_scaled_mm(a: torch.Tensor, b: torch.Tensor, scale_a: torch.Tensor, scale
 
 
 def fp8_quantize(x: torch.Tensor, mode="rowwise", q: torch.Tensor | None = None,
-                 scale: torch.Tensor | None = None, fmt="e4m3fn"):
+                 scale: torch.Tensor | None = None, fmt="e4m3fn", workspace=True):
     """(q, scale) = dynamic float8 quantisation of a rows x cols bf16 GPU matrix:
     scale = amax/qmax (one value, or one per row), q = RNE(clamp(x/scale, +-qmax))
     as uint8 codes, with qmax = 448 (fmt 'e4m3fn') or 57344 ('e5m2').  `q` and
-    `scale` may be passed to reuse buffers."""
+    `scale` may be passed to reuse buffers.  workspace=True gives the per-tensor
+    mode a per-stream workspace (its one-pass path); False runs the two-pass
+    path, which needs none."""
     if mode not in _MODES:
         raise ValueError(f"mode must be 'per_tensor' or 'rowwise', got {mode!r}")
     if fmt not in _FORMATS:
         raise ValueError(f"fmt must be 'e4m3fn' or 'e5m2', got {fmt!r}")
     f = _FORMATS[fmt]
-    fn_name = "fp8_quantize_e4m3" if f == E4M3FN else "fp8_quantize_e5m2"
+    fn_name = "fp8_quantize_e4m3_ws" if f == E4M3FN else "fp8_quantize_e5m2_ws"
     m = _MODES[mode]
     if x.dtype != torch.bfloat16 or x.dim() != 2 or not x.is_contiguous() or not x.is_cuda:
         raise ValueError("x must be a contiguous 2-D bf16 GPU tensor")
@@ -274,9 +286,12 @@ def fp8_quantize(x: torch.Tensor, mode="rowwise", q: torch.Tensor | None = None,
         raise ValueError(f"scale must be a contiguous float32 tensor of {n_scale} elements")
     stream = torch.cuda.current_stream(x.device).cuda_stream
     with torch.cuda.device(x.device):
+        need = int(lib().fp8_quantize_workspace_size(rows, cols, m)) if workspace else 0
+        ws = _workspace(x.device, stream, need, "quantize") if need > 0 else None
         st = getattr(lib(), fn_name)(x.data_ptr() if x.numel() else None,
                                      q.data_ptr() if q.numel() else None, scale.data_ptr(),
-                                     rows, cols, m, stream)
+                                     rows, cols, m, ws.data_ptr() if ws is not None else None,
+                                     need, stream)
     if st != Q_OK:
         msg = f"{fn_name}: {lib().fp8_quantize_status_string(st).decode()} (status {st})"
         if st in _Q_ARG_ERRORS:

@@ -11,20 +11,25 @@
 // A row (or matrix) whose amax is 0 gets scale 0 and codes 0 (the division
 // would be 0/0).
 //
-// HBM-bound: every element is read once (twice for the per-tensor mode, whose
-// second pass usually hits the 256 MB MALL) and written once.
+// HBM-bound: every element is read once and written once (read twice by the
+// per-tensor mode's two-pass path; the MALL keeps little of the first read for
+// the second: re-reading 128 MiB right after reading it is 11% faster than
+// reading it cold).
 //   * Row-wise: one workgroup per row (grid-stride over rows beyond 128 per
 //     CU).  A row of up to 8 x 4096 elements stays in registers between the
 //     amax and the quantisation (16 bf16 = 32 bytes per thread and chunk,
 //     loaded as two 16-byte vectors); longer rows are read a second time
 //     (from L2).
-//   * Per-tensor: a grid-stride amax pass whose workgroups each write their
+//   * Per-tensor, two passes (no workspace, or a matrix below the one-pass
+//     threshold): a grid-stride amax pass whose workgroups each write their
 //     maximum to a slot of their own, one workgroup that reduces the slots
 //     and writes the scale, and a quantisation pass.  The slots are the first
 //     4 * (workgroups) bytes of q, which the quantisation pass then
 //     overwrites (every workgroup covers at least 4096 elements, so they fit):
 //     the library allocates nothing.  (An atomic maximum on one word instead
 //     serialised about 9 ns per workgroup at the end of the pass.)
+//   * Per-tensor, one pass (with a caller workspace): see
+//     quant_tensor_onepass_kernel.
 //   * x / scale must be the correctly rounded fp32 quotient (the fp8 rounding
 //     that follows turns a one-ulp difference at a tie into another code).
 //     The IEEE division sequence is a dozen VALU instructions per element,
@@ -339,6 +344,289 @@ quant_tensor_kernel(const uint16_t* __restrict__ x, uint8_t* __restrict__ q, int
     }
 }
 
+// ---------------------------------------------------------------------------
+// Per-tensor mode in one pass over x (with a caller workspace).
+//
+// One workgroup of 1024 threads per CU.  Pass 1 reads the whole matrix in
+// grid-stride steps of 1024 groups per workgroup (32 KiB of x); the first
+// kHoldRegs steps stay in registers and the next kHoldLds in LDS (8192 x 8192
+// on 256 CUs is 16 steps, 15 of them held), later ones are only reduced.
+// Each workgroup publishes its maximum and counts itself in; the last to
+// arrive reduces the maxima and hands the scale to every workgroup through a
+// word of its own (one 128-byte line each, so no line is polled by more than
+// one workgroup, nor by anyone while the count is raised); each waits for its
+// word, then converts what it holds, re-reading only the steps it did not
+// hold.  x is read once, not twice.
+//
+// The wait needs every workgroup of the grid to reach pass 1's end while the
+// others wait, i.e. all of them resident at once.  One per CU with the CU
+// count as the grid is that, but not when other kernels hold CUs (another
+// stream, another process).  So the wait is bounded: a workgroup that has
+// waited 1 ms of the constant-rate wall clock (or the limit set by
+// fp8_quantize_set_wait_limit_us) tries to claim its word with a
+// compare-and-swap (0 -> kGaveUp); if that succeeds it leaves, freeing its
+// CU for the workgroups not yet started, and its share is left to the last
+// to arrive, whose exchange of that word returns kGaveUp: after its own pass 2
+// it converts every share so left (re-reading x).  If the claim fails, the
+// scale has just arrived and the workgroup goes on.  Each word thus has one
+// owner at every moment, and the result never depends on which path a share
+// took.
+//
+// Workspace (32-bit words; zero-filled before its first use, and every call
+// sets them back to zero: the last to arrive resets the counter, the maxima
+// and the words of shares left to it, every other workgroup its own word once
+// read):
+//   [0] arrivals   [kWsPartial + b] ~(workgroup b's maximum's bits), 0 until stored
+//   [kWsGo + 32 b] ~(the scale's bits) for workgroup b, 0 until it is known,
+//                  kGaveUp once b has left its share (a scale's bits are never
+//                  all ones, nor kGaveUp's complement: the maximum skips NaN)
+constexpr int kOneThreads = 1024;
+constexpr int kOneWaves = kOneThreads / 64;
+constexpr int kHoldRegs = 11;                    // steps held in registers (88 VGPRs)
+constexpr int kHoldLds = 4;                      // steps held in LDS (128 KiB)
+constexpr int kOneMaxGrid = 512;
+constexpr int kWsPartial = 64;
+constexpr int kWsGo = kWsPartial + kOneMaxGrid;
+constexpr int kGoStride = 32;                    // words: one 128-byte line per workgroup
+constexpr int64_t kOneWorkspaceBytes = 4 * (kWsGo + kGoStride * kOneMaxGrid);
+constexpr uint32_t kGaveUp = 0x00400001u;        // ~ of a NaN pattern
+// The grid-wide wait costs a few memory round trips plus the spread of the
+// workgroups' pass-1 end times (MI355X: 6-8 us); below about 6 steps per
+// workgroup (25M elements on 256 CUs) reading x twice is faster: 4096 x 4096
+// one pass 23.4 us, two passes 20.2 us; 8192 x 4096 31.9 us against 34.7 us.
+constexpr int64_t kOnePassMinSteps = 6;
+constexpr int64_t kWaitUsDefault = 1000;
+constexpr uint32_t kMaxPolls = 1u << 20;
+constexpr uint32_t kBufferWord3 = 0x00020000u;   // raw buffer, 32-bit data format
+
+int64_t g_wait_us = kWaitUsDefault;
+
+// Workspace words are read and written with device-scope atomics (coherent
+// across the XCDs' L2s), relaxed.  No fence is needed: the only data that
+// passes between workgroups is in those words themselves, and each word says
+// by its own value whether it has been written (a maximum and a scale word
+// are nonzero once stored), so a reader waits for the value, not for an
+// ordering.  (An acquire at this scope would also invalidate the XCD's L2:
+// one per workgroup cost 2.5 us per 8192 x 8192 call.)
+__device__ __forceinline__ uint32_t ws_load(const uint32_t* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void ws_store(uint32_t* p, uint32_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// 16 bytes per lane from x into LDS: lane l's bytes at byte offset voff land
+// at lds + 16 l (lds is wave-uniform, in M0).  Inline asm: the compiler does
+// not track these loads, so their consumer waits with an explicit vmcnt(0).
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, const void* lds, uint32_t voff) {
+    const uint32_t m0 = (uint32_t)(uintptr_t)lds;
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                 :
+                 : "v"(voff), "s"(rsrc), "{m0}"(m0)
+                 : "memory");
+}
+
+// Maximum over a workgroup of W waves (all lanes return it).
+template <int W>
+__device__ __forceinline__ float block_max_w(float m, float* red) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+    __syncthreads();
+    if (threadIdx.x % 64 == 0) red[threadIdx.x / 64] = m;
+    __syncthreads();
+    m = red[0];
+#pragma unroll
+    for (int w = 1; w < W; ++w) m = fmaxf(m, red[w]);
+    return m;
+}
+
+template <int FMT>
+__global__ void __launch_bounds__(kOneThreads)
+quant_tensor_onepass_kernel(const uint16_t* __restrict__ x, uint8_t* __restrict__ q, float* __restrict__ scale,
+                            int64_t groups, uint32_t* ws, int64_t wait_ticks) {
+    __shared__ __attribute__((aligned(1024))) uint4 held[kHoldLds][2][kOneThreads];
+    __shared__ float red[kOneWaves];
+    __shared__ uint32_t left[kOneMaxGrid];   // the last to arrive: shares left to it
+    __shared__ float s_scale;
+    __shared__ int s_last, s_gave, s_any_left;
+    const int tid = threadIdx.x;
+    const int64_t T = (int64_t)gridDim.x * kOneThreads;
+    const int64_t g0 = blockIdx.x * (int64_t)kOneThreads + tid;
+    const int64_t steps = (groups + T - 1) / T;
+    // The held steps in 32-bit byte offsets from x and q (at most
+    // (kHoldRegs + kHoldLds) * 2^19 groups of 32 bytes: under 2^31), with
+    // step s present when s * T < groups - g0.
+    const uint32_t t32 = (uint32_t)T;
+    const int64_t rem = groups - g0;
+    const uint32_t lim = rem <= 0 ? 0u : rem >= 0x7fffffff ? 0x7fffffffu : (uint32_t)rem;
+    const uint32_t off0 = (uint32_t)g0 * 32u;
+    const char* xc = reinterpret_cast<const char*>(x);
+    char* qc = reinterpret_cast<char*>(q);
+    auto held_store = [&](uint32_t s, const uint4& c) {
+        *reinterpret_cast<uint4*>(qc + (off0 / 2u + s * t32 * 16u)) = c;
+    };
+    uint32_t* go = ws + kWsGo + kGoStride * blockIdx.x;
+
+    // Pass 1: issue every held step's loads (registers, then LDS), then the
+    // rest; reduce once they are in.
+    uint4 v[kHoldRegs][2];
+#pragma unroll
+    for (uint32_t s = 0; s < kHoldRegs; ++s) {
+        if (s * t32 < lim) {
+            const uint4* p = reinterpret_cast<const uint4*>(xc + (off0 + s * t32 * 32u));
+            v[s][0] = p[0];
+            v[s][1] = p[1];
+        }
+    }
+    {
+        const int64_t xbytes = groups * 32;
+        const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<char*>(xc), (short)0, (int)(xbytes < 0xffffffffll ? xbytes : 0xffffffffll),
+            (int)kBufferWord3);
+        const int wave = tid / 64;
+#pragma unroll
+        for (uint32_t s = 0; s < kHoldLds; ++s) {
+            if ((kHoldRegs + s) * t32 < lim) {
+                const uint32_t o = off0 + (kHoldRegs + s) * t32 * 32u;
+                dma16(rx, &held[s][0][wave * 64], o);
+                dma16(rx, &held[s][1][wave * 64], o + 16u);
+            }
+        }
+    }
+    float m = 0.f;
+    for (int64_t s = kHoldRegs + kHoldLds; s < steps; ++s) {
+        const int64_t g = s * T + g0;
+        if (g < groups) {
+            uint4 w[2];
+            load16(x + g * kGroup, w);
+            m = fmaxf(m, absmax16(w));
+        }
+    }
+#pragma unroll
+    for (uint32_t s = 0; s < kHoldRegs; ++s)
+        if (s * t32 < lim) m = fmaxf(m, absmax16(v[s]));
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the LDS loads (each lane reads its own)
+#pragma unroll
+    for (uint32_t s = 0; s < kHoldLds; ++s) {
+        if ((kHoldRegs + s) * t32 < lim) {
+            const uint4 w[2] = {held[s][0][tid], held[s][1][tid]};
+            m = fmaxf(m, absmax16(w));
+        }
+    }
+    m = block_max_w<kOneWaves>(m, red);
+
+    // Count in.  The maximum goes out as ~bits (never 0: the maximum is not
+    // NaN) without waiting for it to land; the last to arrive waits for every
+    // word to be nonzero, makes the scale, and hands it out.
+    if (tid == 0) {
+        ws_store(ws + kWsPartial + blockIdx.x, ~__float_as_uint(m));
+        s_last = __hip_atomic_fetch_add(ws, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                 gridDim.x - 1;
+    }
+    __syncthreads();
+    const bool last = s_last != 0;
+    uint32_t was = 0u;   // the last to arrive: what workgroup tid's word held
+    if (last) {
+        float a = 0.f;
+        int missing = 0;
+        if (tid < (int)gridDim.x) {
+            // Every count is in, so every maximum has been stored; one still
+            // in flight lands within a memory round trip.  (Bounded all the
+            // same: should one never land, the scale is NaN and every code
+            // NaN, rather than a wrong scale.)
+            uint32_t* pw = ws + kWsPartial + tid;
+            uint32_t w = ws_load(pw);
+            for (uint32_t polls = 0; w == 0u && polls < kMaxPolls; ++polls) {
+                __builtin_amdgcn_s_sleep(1);
+                w = ws_load(pw);
+            }
+            missing = w == 0u;
+            a = __uint_as_float(~w);
+            ws_store(pw, 0u);
+        }
+        float sc = block_max_w<kOneWaves>(a, red) / Fp8Fmt<FMT>::kMax;
+        if (__syncthreads_or(missing)) sc = __uint_as_float(0x7fc00000u);
+        if (tid < (int)gridDim.x && tid != (int)blockIdx.x)   // (its own word stays 0)
+            was = __hip_atomic_exchange(ws + kWsGo + kGoStride * tid, ~__float_as_uint(sc),
+                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (tid == 0) {
+            ws_store(ws, 0u);   // every count is in
+            s_scale = sc;
+            s_gave = 0;
+        }
+    } else if (tid == 0) {
+        // Wait for this workgroup's word (bounded by the clock and, should it
+        // not advance, by the number of polls, each about 500 cycles apart).
+        int gave_up = 0;
+        const uint64_t t0 = wall_clock64();
+        uint32_t w = ws_load(go);
+        for (uint32_t polls = 0; w == 0u; ++polls) {
+            if ((int64_t)(wall_clock64() - t0) >= wait_ticks || polls >= kMaxPolls) {
+                w = __hip_atomic_exchange(go, kGaveUp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (w == 0u) {
+                    gave_up = 1;          // claimed: the share is left to the last to arrive
+                } else {
+                    ws_store(go, 0u);     // the scale came first: undo the claim
+                }
+                break;
+            }
+            __builtin_amdgcn_s_sleep(8);
+            w = ws_load(go);
+        }
+        if (!gave_up) ws_store(go, 0u);
+        s_scale = __uint_as_float(~w);
+        s_gave = gave_up;
+    }
+    __syncthreads();
+    if (s_gave) return;
+    const float sc = s_scale;
+    if (blockIdx.x == 0 && tid == 0) scale[0] = sc;
+
+    // Pass 2: convert what is held, re-read the rest (the first re-read step
+    // is loaded before the LDS-held steps are converted, once the registers
+    // of the others are free).
+    const Div d = make_div(sc);
+#pragma unroll
+    for (uint32_t k = 0; k < kHoldRegs; ++k)
+        if (k * t32 < lim) held_store(k, quant16<FMT>(v[k], d));
+    int64_t s = kHoldRegs + kHoldLds;
+    uint4 nx[2];
+    if (s < steps && s * T + g0 < groups) load16(x + (s * T + g0) * kGroup, nx);
+#pragma unroll
+    for (uint32_t k = 0; k < kHoldLds; ++k) {
+        if ((kHoldRegs + k) * t32 < lim) {
+            const uint4 w[2] = {held[k][0][tid], held[k][1][tid]};
+            held_store(kHoldRegs + k, quant16<FMT>(w, d));
+        }
+    }
+    for (; s < steps; ++s) {
+        const int64_t g = s * T + g0;
+        if (g < groups) {
+            const uint4 w[2] = {nx[0], nx[1]};
+            const int64_t gn = g + T;
+            if (gn < groups) load16(x + gn * kGroup, nx);
+            *reinterpret_cast<uint4*>(q + g * kGroup) = quant16<FMT>(w, d);
+        }
+    }
+    if (!last) return;
+
+    // The last to arrive: convert the shares left to it, and set their words
+    // back to zero.
+    if (tid < (int)gridDim.x) left[tid] = was == kGaveUp;
+    if (__syncthreads_or(was == kGaveUp)) {
+        for (uint32_t b = 0; b < gridDim.x; ++b) {
+            if (!left[b]) continue;
+            if (b == 0 && tid == 0) scale[0] = sc;
+            for (int64_t g = b * (int64_t)kOneThreads + tid; g < groups; g += T) {
+                uint4 w[2];
+                load16(x + g * kGroup, w);
+                *reinterpret_cast<uint4*>(q + g * kGroup) = quant16<FMT>(w, d);
+            }
+        }
+        if (tid < (int)gridDim.x && was == kGaveUp) ws_store(ws + kWsGo + kGoStride * tid, 0u);
+    }
+}
+
 bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
 int device_cus_q() {
@@ -349,9 +637,18 @@ int device_cus_q() {
     return cus;
 }
 
+// Ticks of the device's wall clock in `us` microseconds (0 if unknown).
+int64_t wait_ticks(int64_t us) {
+    int dev = -1, khz = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess) return 0;
+    return us * (int64_t)khz / 1000;
+}
+
 template <int FMT>
 int quantize_impl(const void* x, void* q, float* scale, int64_t rows, int64_t cols,
-                  int scaling_mode, struct ihipStream_t* stream) {
+                  int scaling_mode, void* workspace, int64_t workspace_bytes,
+                  struct ihipStream_t* stream) {
     if (scaling_mode != FP8Q_PER_TENSOR && scaling_mode != FP8Q_ROWWISE) return FP8Q_ERR_MODE;
     if (rows < 0 || cols < 0 || cols % kGroup != 0 || cols > (int64_t(1) << 31) ||
         rows > (int64_t(1) << 31))
@@ -361,6 +658,9 @@ int quantize_impl(const void* x, void* q, float* scale, int64_t rows, int64_t co
     if ((n_scales > 0 && !scale) || (!empty && (!x || !q))) return FP8Q_ERR_NULL;
     if ((uintptr_t)scale & 3) return FP8Q_ERR_ALIGN;
     if (!empty && (!aligned16(x) || !aligned16(q))) return FP8Q_ERR_ALIGN;
+    if (workspace && ((uintptr_t)workspace & 3)) return FP8Q_ERR_ALIGN;
+    const bool onepass = workspace && !empty && scaling_mode == FP8Q_PER_TENSOR;
+    if (onepass && workspace_bytes < kOneWorkspaceBytes) return FP8Q_ERR_WORKSPACE;
     if (n_scales == 0) return FP8Q_OK;   // row-wise without rows: nothing to write
     const int cus = device_cus_q();
     if (cus <= 0) return FP8Q_ERR_DEVICE;
@@ -396,6 +696,16 @@ int quantize_impl(const void* x, void* q, float* scale, int64_t rows, int64_t co
         else
             hipLaunchKernelGGL((quant_rowwise_kernel<0, FMT>), dim3(grid), dim3(kThreads), 0, hs, xb, qb,
                                scale, rows, cols);
+    } else if (onepass && rows * cols / kGroup >= kOnePassMinSteps * (int64_t)(cus < kOneMaxGrid ? cus : kOneMaxGrid) *
+                                                   kOneThreads) {
+        const int64_t groups = rows * cols / kGroup;
+        const int64_t want = (groups + kOneThreads - 1) / kOneThreads;
+        const int64_t cap = cus < kOneMaxGrid ? cus : kOneMaxGrid;
+        const unsigned grid = (unsigned)(want < cap ? want : cap);
+        const int64_t ticks = wait_ticks(g_wait_us);
+        uint32_t* ws = static_cast<uint32_t*>(workspace);
+        hipLaunchKernelGGL(quant_tensor_onepass_kernel<FMT>, dim3(grid), dim3(kOneThreads), 0, hs, xb, qb,
+                           scale, groups, ws, ticks);
     } else {
         const int64_t groups = rows * cols / kGroup;
         const int64_t want = (groups + kThreads - 1) / kThreads;
@@ -421,12 +731,35 @@ extern "C" {
 
 int fp8_quantize_e4m3(const void* x, void* q, float* scale, int64_t rows, int64_t cols,
                       int scaling_mode, struct ihipStream_t* stream) {
-    return quantize_impl<0>(x, q, scale, rows, cols, scaling_mode, stream);
+    return quantize_impl<0>(x, q, scale, rows, cols, scaling_mode, nullptr, 0, stream);
 }
 
 int fp8_quantize_e5m2(const void* x, void* q, float* scale, int64_t rows, int64_t cols,
                       int scaling_mode, struct ihipStream_t* stream) {
-    return quantize_impl<1>(x, q, scale, rows, cols, scaling_mode, stream);
+    return quantize_impl<1>(x, q, scale, rows, cols, scaling_mode, nullptr, 0, stream);
+}
+
+int64_t fp8_quantize_workspace_size(int64_t rows, int64_t cols, int scaling_mode) {
+    if (scaling_mode != FP8Q_PER_TENSOR || rows <= 0 || cols <= 0) return 0;
+    return kOneWorkspaceBytes;
+}
+
+int fp8_quantize_e4m3_ws(const void* x, void* q, float* scale, int64_t rows, int64_t cols,
+                         int scaling_mode, void* workspace, int64_t workspace_bytes,
+                         struct ihipStream_t* stream) {
+    return quantize_impl<0>(x, q, scale, rows, cols, scaling_mode, workspace, workspace_bytes, stream);
+}
+
+int fp8_quantize_e5m2_ws(const void* x, void* q, float* scale, int64_t rows, int64_t cols,
+                         int scaling_mode, void* workspace, int64_t workspace_bytes,
+                         struct ihipStream_t* stream) {
+    return quantize_impl<1>(x, q, scale, rows, cols, scaling_mode, workspace, workspace_bytes, stream);
+}
+
+int64_t fp8_quantize_set_wait_limit_us(int64_t us) {
+    const int64_t before = g_wait_us;
+    g_wait_us = us < 0 ? kWaitUsDefault : us;
+    return before;
 }
 
 const char* fp8_quantize_status_string(int s) {
@@ -438,6 +771,7 @@ const char* fp8_quantize_status_string(int s) {
         case FP8Q_ERR_MODE: return "unknown scaling mode";
         case FP8Q_ERR_DEVICE: return "no usable HIP device";
         case FP8Q_ERR_LAUNCH: return "kernel launch failed";
+        case FP8Q_ERR_WORKSPACE: return "workspace smaller than fp8_quantize_workspace_size()";
         default: return "unknown status";
     }
 }

@@ -183,8 +183,8 @@ def test_quantize_empty_rowwise_needs_no_device(L):
 
 
 def test_quantize_status_strings(L):
-    for s in range(7):
-        assert L.fp8_quantize_status_string(s)
+    for s in range(8):
+        assert L.fp8_quantize_status_string(s) != b"unknown status"
     assert L.fp8_quantize_status_string(42) == b"unknown status"
 
 
@@ -231,6 +231,33 @@ def test_quantize_e5m2_rejects_bad_arguments(L, kw, code):
     args.update(kw)
     assert L.fp8_quantize_e5m2(args["x"], args["q"], args["scale"], args["rows"], args["cols"],
                                args["mode"], None) == code
+
+
+def test_quantize_workspace_size(L):
+    # per-tensor calls with elements take the one-pass kernel's workspace;
+    # row-wise and empty calls take none
+    assert L.fp8_quantize_workspace_size(8192, 8192, binding.PER_TENSOR) == 67840
+    assert L.fp8_quantize_workspace_size(1, 16, binding.PER_TENSOR) == 67840
+    assert L.fp8_quantize_workspace_size(8192, 8192, binding.ROWWISE) == 0
+    assert L.fp8_quantize_workspace_size(0, 64, binding.PER_TENSOR) == 0
+    assert L.fp8_quantize_workspace_size(64, 0, binding.PER_TENSOR) == 0
+
+
+@pytest.mark.parametrize("fn", ["fp8_quantize_e4m3_ws", "fp8_quantize_e5m2_ws"])
+def test_quantize_ws_rejects_bad_workspaces(L, fn):
+    f = getattr(L, fn)
+    need = L.fp8_quantize_workspace_size(64, 64, binding.PER_TENSOR)
+    assert f(P, P, P, 64, 64, binding.PER_TENSOR, P, need - 4, None) == binding.Q_ERR_WORKSPACE
+    assert f(P, P, P, 64, 64, binding.PER_TENSOR, P + 2, need, None) == binding.Q_ERR_ALIGN
+    # the shared argument checks come first, as in fp8_quantize_e4m3
+    assert f(P, P, P, 64, 24, binding.PER_TENSOR, P, need, None) == binding.Q_ERR_SHAPE
+    assert f(P, P, P, 64, 64, 2, P, need, None) == binding.Q_ERR_MODE
+
+
+def test_quantize_wait_limit_hook_returns_the_previous_limit(L):
+    assert L.fp8_quantize_set_wait_limit_us(5) == 1000
+    assert L.fp8_quantize_set_wait_limit_us(-1) == 5
+    assert L.fp8_quantize_set_wait_limit_us(-1) == 1000
 
 
 # The plans chosen for the benchmarked shapes, each picked from measured

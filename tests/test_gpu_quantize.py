@@ -21,16 +21,16 @@ def bf16_bits(x):
     return torch.from_numpy(np.asarray(x, np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
 
 
-def run(bits, mode, fmt="e4m3fn"):
+def run(bits, mode, fmt="e4m3fn", workspace=True):
     x = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(DEV)
-    print(f"[quantize] shape={bits.shape} mode={mode} fmt={fmt}", flush=True)
-    q, s = binding.fp8_quantize(x, mode, fmt=fmt)
+    print(f"[quantize] shape={bits.shape} mode={mode} fmt={fmt} workspace={workspace}", flush=True)
+    q, s = binding.fp8_quantize(x, mode, fmt=fmt, workspace=workspace)
     torch.cuda.synchronize()
     return q.cpu().numpy(), s.cpu().numpy()
 
 
-def check(bits, mode, fmt="e4m3fn"):
-    q, s = run(bits, mode, fmt)
+def check(bits, mode, fmt="e4m3fn", workspace=True):
+    q, s = run(bits, mode, fmt, workspace)
     rq, rs = oracle.quantize(bits, mode, OFMT[fmt])
     assert np.array_equal(s.view(np.uint32), rs.view(np.uint32)), "scales differ"
     bad = np.argwhere(q != rq)
@@ -49,12 +49,19 @@ def _normal(rows, cols, seed, spread=True):
 
 # cols: one 4096-element chunk, a ragged second chunk, the register-resident
 # 7-8 chunks (28672) and a row too long for registers (40960)
+# mode and path: per-tensor with a workspace (these shapes are below the
+# one-pass kernel's size threshold, so this checks that the selection falls
+# back to the two-pass kernels) and without one; row-wise uses no workspace.
+# The one-pass kernel itself is checked at the sizes that take it, below.
+PATHS = [(PT, True), (PT, False), (RW, True)]
+
+
 @pytest.mark.parametrize("fmt", FMTS)
-@pytest.mark.parametrize("mode", [PT, RW])
+@pytest.mark.parametrize("mode,workspace", PATHS)
 @pytest.mark.parametrize("rows,cols", [(1, 16), (3, 48), (37, 4096), (19, 4112), (8, 16384),
                                        (5, 28672), (3, 40960), (300, 272)])
-def test_random_matrices_bitexact(rows, cols, mode, fmt):
-    check(_normal(rows, cols, rows * 7 + cols), mode, fmt)
+def test_random_matrices_bitexact(rows, cols, mode, workspace, fmt):
+    check(_normal(rows, cols, rows * 7 + cols), mode, fmt, workspace)
 
 
 @pytest.mark.parametrize("fmt", FMTS)
@@ -227,18 +234,105 @@ def _workload_bits(rows, cols, key):
     return wl.bf16_matrix_bits(rows, cols, key=key)
 
 
+@pytest.mark.parametrize("workspace", [True, False], ids=["onepass", "twopass"])
 @pytest.mark.parametrize("rows,cols,fmt", [(8192, 8192, "e4m3fn"), (8192, 8192, "e5m2"),
-                                           (8192, 4096, "e4m3fn"), (4099, 8192, "e4m3fn")])
-def test_per_tensor_large_bitexact(rows, cols, fmt):
-    # The benchmarked per-tensor size and the sizes around it: the amax and
-    # quantisation passes run their unrolled grid-stride loops (every
-    # workgroup takes several strides), and the scale comes from the maxima of
-    # the whole grid of workgroups (2048 on 256 CUs).  The matrix's amax is
-    # planted in the last elements, which the last stride of the last
-    # workgroups reads.
+                                           (8192, 4096, "e4m3fn"), (4099, 8192, "e4m3fn"),
+                                           (6000, 8192, "e5m2")])
+def test_per_tensor_large_bitexact(rows, cols, fmt, workspace):
+    # The benchmarked per-tensor size and the sizes around it.  Two passes:
+    # the amax and quantisation passes run their unrolled grid-stride loops
+    # (every workgroup takes several strides), and the scale comes from the
+    # maxima of the whole grid of workgroups (2048 on 256 CUs).  One pass, with
+    # 256 workgroups of 1024 groups per step: 8192 x 4096 and 4099 x 8192 are
+    # 8 steps (all held in registers), 6000 x 8192 12 (registers, then part
+    # of the first LDS step), 8192 x 8192 16 (registers, LDS, and one step
+    # read again in the conversion).  The matrix's amax is planted in the
+    # last elements, which the last stride of the last workgroups reads.
     bits = _workload_bits(rows, cols, key=rows + cols + len(fmt))
     bits[-1, -1] = bf16_bits([-9.5])[0]
-    check(bits, PT, fmt)
+    check(bits, PT, fmt, workspace)
+
+
+def _quantize_ws():
+    stream = torch.cuda.current_stream(torch.device(DEV)).cuda_stream
+    return binding._workspaces[(torch.device(DEV).index, stream, "quantize")][-1]
+
+
+@pytest.mark.parametrize("rows,cols,fmt", [(8192, 4096, "e5m2"), (4099, 8192, "e4m3fn"),
+                                           (8192, 8192, "e4m3fn")])
+def test_per_tensor_onepass_shares_left_to_the_last_arrival(rows, cols, fmt):
+    # A wait limit of 0: every workgroup of the one-pass kernel but the last
+    # to arrive gives up at once and leaves its share to that one, which
+    # re-reads it; the codes must not change, and the workspace must be back
+    # at zero after the call.
+    bits = _workload_bits(rows, cols, key=rows * 5 + cols + len(fmt))
+    before = binding.lib().fp8_quantize_set_wait_limit_us(0)
+    try:
+        check(bits, PT, fmt, True)
+    finally:
+        binding.lib().fp8_quantize_set_wait_limit_us(before)
+    assert not _quantize_ws().view(torch.int32).cpu().numpy().any()
+
+
+def test_per_tensor_onepass_workspace_is_left_at_zero():
+    bits = _workload_bits(8192, 8192, key=77)
+    for _ in range(2):
+        check(bits, PT, "e4m3fn", True)
+        assert not _quantize_ws().view(torch.int32).cpu().numpy().any()
+
+
+def test_per_tensor_onepass_on_two_streams_at_once():
+    # Two calls that may run at the same time, each on its own stream (and so
+    # with its own workspace): when they compete for CUs, workgroups that
+    # cannot all be resident fall back to the second kernel; the results
+    # stay exact.
+    xs = [_workload_bits(8192, 8192, key=k) for k in (91, 92)]
+    refs = [oracle.quantize(b, PT, oracle.E4M3FN) for b in xs]
+    ts = [torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).to(DEV) for b in xs]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    torch.cuda.synchronize()
+    print("[quantize] two streams, 8192x8192 per-tensor each", flush=True)
+    outs = []
+    for _ in range(3):
+        for t, st in zip(ts, streams):
+            with torch.cuda.stream(st):
+                outs.append(binding.fp8_quantize(t, PT))
+    torch.cuda.synchronize()
+    for i, (q, sc) in enumerate(outs):
+        rq, rs = refs[i % 2]
+        assert np.array_equal(sc.cpu().numpy().view(np.uint32), rs.view(np.uint32))
+        assert np.array_equal(q.cpu().numpy(), rq), f"call {i}"
+
+
+def test_per_tensor_onepass_in_a_graph():
+    # Captured once, replayed several times with eager work between the
+    # replays: every replay equals the eager result (the workspace's counters
+    # are reset by a kernel, never by a memset node).
+    bits = _workload_bits(4099, 8192, key=5)
+    x = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(DEV)
+    print("[quantize] graph capture of the per-tensor one-pass path", flush=True)
+    q0, s0 = binding.fp8_quantize(x, PT)
+    torch.cuda.synchronize()
+    ref_q, ref_s = q0.cpu().numpy(), s0.cpu().numpy()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        q, sc = binding.fp8_quantize(x, PT)          # the workspace of stream s exists before capture
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            binding.fp8_quantize(x, PT, q=q, scale=sc)
+    torch.cuda.synchronize()
+    for i in range(3):
+        q.zero_()
+        sc.fill_(-1.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(sc.cpu().numpy(), ref_s), f"replay {i}"
+        assert np.array_equal(q.cpu().numpy(), ref_q), f"replay {i}"
+        _ = binding.fp8_quantize(x, PT)              # eager work between replays
+        torch.cuda.synchronize()
 
 
 @pytest.mark.parametrize("rows,cols,fmt", [(40000, 256, "e4m3fn"), (40000, 256, "e5m2"),
