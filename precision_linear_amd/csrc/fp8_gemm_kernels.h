@@ -113,6 +113,7 @@ namespace {
 using namespace fp8mm;
 
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef v4i v4i_a2 __attribute__((aligned(2)));   // 16 bytes at any even LDS address
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
@@ -276,7 +277,8 @@ struct Cfg {
     // overlap the other's loads), else one.
     static constexpr int OCCUPANCY = LDS_BYTES * 2 <= 160 * 1024 ? 2 : 1;
     static_assert(STAGES >= 2, "at least double buffering");
-    static_assert(BN % 8 == 0 && BM * BN * 2 <= MAIN_BYTES, "the output tile fits the stage buffers");
+    static_assert(BN % 8 == 0 && BM * (BN * 2 + 16) <= MAIN_BYTES,
+                  "the output tile (with its padded rows) fits the stage buffers");
     static_assert(LOADS * (STAGES - 1) <= 63, "vmcnt counts up to 63");
 };
 
@@ -634,9 +636,12 @@ __device__ __forceinline__ void store_tile(const typename Mfma<MI>::acc_t (&acc)
 // them into a row-major copy of the whole BM x BN tile in LDS.  Row r of that
 // copy has STG_CHUNKS 16-byte chunks; chunk c sits at position (c + r) mod
 // STG_CHUNKS, so the lanes of one MFMA block, which hold one column run each
-// of consecutive rows, write to different banks.  Rows and columns outside
-// the output are converted too (from zero accumulators) and never stored.
-template <class C, bool RW, bool BIAS>
+// of consecutive rows, write to different banks.  PAD instead: rows are
+// STG_CHUNKS + 1 chunks apart and not rotated (the odd number of chunks per
+// row spreads consecutive rows over the banks), so that any 16 bytes of a
+// row, at any even offset, are contiguous.  Rows and columns outside the
+// output are converted too (from zero accumulators) and never stored.
+template <class C, bool RW, bool BIAS, bool PAD>
 __device__ __forceinline__ void stage_tile_impl(
     const typename Mfma<C::MI_>::acc_t (&acc)[C::FN][C::FM], uint8_t* stg, int mbase, int nbase,
     const float* epi_sa, const float* epi_sb, const uint16_t* epi_bias, float s_pt, int lane) {
@@ -677,8 +682,11 @@ __device__ __forceinline__ void stage_tile_impl(
                 uint2 w;
                 w.x = pack_bf16x2(y[0], y[1]);
                 w.y = pack_bf16x2(y[2], y[3]);
-                *reinterpret_cast<uint2*>(stg + ml * (NCH * 16) + (((byte >> 4) + ml) % NCH) * 16 +
-                                          (byte & 15)) = w;
+                if constexpr (PAD)
+                    *reinterpret_cast<uint2*>(stg + ml * ((NCH + 1) * 16) + byte) = w;
+                else
+                    *reinterpret_cast<uint2*>(stg + ml * (NCH * 16) + (((byte >> 4) + ml) % NCH) * 16 +
+                                              (byte & 15)) = w;
             }
         }
 }
@@ -709,17 +717,18 @@ __device__ __forceinline__ void store_staged(const uint8_t* stg, const Params& p
 }
 
 // The same for rows whose start is not 16-byte aligned (odd N, or an output
-// only 2- or 4-byte aligned).  Row r of the tile is a head of h < 8 values up
-// to the first 16-byte boundary of its output row, a body of 16-byte pieces
-// and a tail of fewer than 8 values.  Two passes, each with consecutive lanes
-// on consecutive work items and no loop inside a lane: the body pieces (a
-// piece starts 2h bytes into a staged 16-byte chunk and is assembled from two
-// neighbouring chunks, with a 2-byte funnel shift when 2h is not a multiple
-// of 4), then one value per lane for the heads and tails.
+// only 2- or 4-byte aligned), from the padded copy.  Row r of the tile is a
+// head of h < 8 values up to the first 16-byte boundary of its output row, a
+// body of 16-byte pieces and a tail of fewer than 8 values.  Two passes, each
+// with consecutive lanes on consecutive work items and no loop inside a lane:
+// the body pieces (each one 16-byte LDS read at the piece's even offset, 2h
+// bytes into a staged chunk: gfx950's LDS reads unaligned vectors whole, so
+// no shifts or selects), then one value per lane for the heads and tails.
 template <class C>
 __device__ __forceinline__ void store_staged_unaligned(const uint8_t* stg, const Params& p, int row0,
                                                        int col0, int tid) {
     constexpr int NCH = C::STG_CHUNKS;
+    constexpr int PITCH = (NCH + 1) * 16;
     const int rows = min(C::BM_, p.M - row0);
     const int ncols = min(C::BN_, p.N - col0);
     auto head_of = [&](int r) {
@@ -737,23 +746,9 @@ __device__ __forceinline__ void store_staged_unaligned(const uint8_t* stg, const
             if (q >= TOTAL || r >= rows) continue;
             const int head = head_of(r);
             if (b >= (ncols - head) / 8) continue;
-            const int sh = head * 2;                      // bytes into staged chunk b
-            const uint8_t* srow = stg + r * (NCH * 16);
-            const v4i lo = *reinterpret_cast<const v4i*>(srow + ((b + r) % NCH) * 16);
-            v4i out = lo;
-            if (sh != 0) {
-                const v4i hi = *reinterpret_cast<const v4i*>(srow + ((b + 1 + r) % NCH) * 16);
-                const uint32_t d[8] = {(uint32_t)lo[0], (uint32_t)lo[1], (uint32_t)lo[2], (uint32_t)lo[3],
-                                       (uint32_t)hi[0], (uint32_t)hi[1], (uint32_t)hi[2], (uint32_t)hi[3]};
-                const int w0 = sh >> 2;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const uint32_t a = d[(w0 + j) & 7], c = d[(w0 + j + 1) & 7];
-                    out[j] = (int)((sh & 2) ? ((a >> 16) | (c << 16)) : a);
-                }
-            }
+            const v4i v = *reinterpret_cast<const v4i_a2*>(stg + r * PITCH + head * 2 + b * 16);
             uint16_t* orow = p.out + (size_t)(row0 + r) * p.N + col0;
-            *reinterpret_cast<v4i*>(orow + head + b * 8) = out;
+            *reinterpret_cast<v4i*>(orow + head + b * 8) = v;
         }
     }
     {   // heads (items 0..7 of a row) and tails (items 8..15), one value each
@@ -768,10 +763,8 @@ __device__ __forceinline__ void store_staged_unaligned(const uint8_t* stg, const
             const int head = head_of(r);
             const int e = item < 8 ? item : head + (ncols - head) / 8 * 8 + (item - 8);
             if (item < 8 ? e >= head : e >= ncols) continue;
-            const int byte = e * 2;
-            const uint16_t v = *reinterpret_cast<const uint16_t*>(
-                stg + r * (NCH * 16) + (((byte >> 4) + r) % NCH) * 16 + (byte & 15));
-            p.out[(size_t)(row0 + r) * p.N + col0 + e] = v;
+            p.out[(size_t)(row0 + r) * p.N + col0 + e] =
+                *reinterpret_cast<const uint16_t*>(stg + r * PITCH + e * 2);
         }
     }
 }
@@ -784,22 +777,28 @@ __device__ __forceinline__ void stage_and_store(
     // As in store_tile: opaque lane id, so the addresses are not kept live
     // across the K loop.
     asm volatile("" : "+v"(lane));
-    if (p.rowwise) {
-        if (has_bias)
-            stage_tile_impl<C, true, true>(acc, stg, mbase, nbase, epi_sa, epi_sb, epi_bias, s_pt, lane);
-        else
-            stage_tile_impl<C, true, false>(acc, stg, mbase, nbase, epi_sa, epi_sb, epi_bias, s_pt, lane);
-    } else {
-        if (has_bias)
-            stage_tile_impl<C, false, true>(acc, stg, mbase, nbase, epi_sa, epi_sb, epi_bias, s_pt, lane);
-        else
-            stage_tile_impl<C, false, false>(acc, stg, mbase, nbase, epi_sa, epi_sb, epi_bias, s_pt, lane);
-    }
-    barrier_lds();
-    if (p.vec16)
+    auto stage = [&](auto pad) {
+        constexpr bool PAD = decltype(pad)::value;
+        if (p.rowwise) {
+            if (has_bias)
+                stage_tile_impl<C, true, true, PAD>(acc, stg, mbase, nbase, epi_sa, epi_sb, epi_bias, s_pt, lane);
+            else
+                stage_tile_impl<C, true, false, PAD>(acc, stg, mbase, nbase, epi_sa, epi_sb, epi_bias, s_pt, lane);
+        } else {
+            if (has_bias)
+                stage_tile_impl<C, false, true, PAD>(acc, stg, mbase, nbase, epi_sa, epi_sb, epi_bias, s_pt, lane);
+            else
+                stage_tile_impl<C, false, false, PAD>(acc, stg, mbase, nbase, epi_sa, epi_sb, epi_bias, s_pt, lane);
+        }
+        barrier_lds();
+    };
+    if (p.vec16) {
+        stage(std::false_type{});
         store_staged<C>(stg, p, row0, col0, tid);
-    else
+    } else {
+        stage(std::true_type{});
         store_staged_unaligned<C>(stg, p, row0, col0, tid);
+    }
 }
 
 // One K stage (BK bytes of K) of the software pipeline.  The fragments of

@@ -115,7 +115,7 @@ int choose_config_split(int64_t M, int64_t N, int64_t K) {
     // 128 x 128 tiles on 8 waves with split-K when they leave CUs idle.  All
     // from same-box A/B sweeps on MI355X (e.g. 512 x 12288 x 3072: 28.6 us
     // two-per-CU vs 34.2 us ping-pong; 8191 x 1000 x 4160: 44.5 vs 47.5 us;
-    // 4095 x 4097 x 96: 26.7 vs 29.0 us on 8 waves).
+    // 4095 x 4097 x 96: 19.3 vs 23.2 us on 8 waves).
     const int64_t big_tiles = cdiv(M, 256) * cdiv(N, 256);
     const int64_t tiles128 = cdiv(M, 128) * cdiv(N, 128);
     const bool pp_ok = N % 8 == 0;
