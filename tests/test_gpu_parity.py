@@ -146,6 +146,17 @@ def test_every_config_ragged(config, mode, bias, shape):
     check_full(inp, config)
 
 
+@pytest.mark.parametrize("config", _configs(), ids=_config_ids())
+@pytest.mark.parametrize("shape", [(200, 1026, 256), (140, 766, 128), (129, 4097, 32)])
+def test_every_config_unaligned_rows(config, shape):
+    # Rows that do not start on a 16-byte boundary (N % 8 = 2, 6 and odd):
+    # every row start phase N allows (2 bytes apart for odd N), heads of 0-7
+    # values, tails, and tiles narrower than 8 columns at the right edge.
+    M, N, K = shape
+    inp = wl.make_inputs(M, N, K, RW, "codes", bias=True, key=config * 31 + N)
+    check_full(inp, config)
+
+
 @pytest.mark.parametrize("recipe", ["normal", "skinny"])
 def test_normal_inputs_small(recipe):
     inp = wl.make_inputs(192, 320, 512, RW, recipe, bias=recipe == "skinny", key=77)
@@ -279,13 +290,15 @@ def test_empty_is_noop():
     torch.cuda.synchronize()
 
 
-def test_unaligned_output_rows_fall_back():
-    """N odd and an output base that is only 2-byte aligned: the kernel must
-    not use its 8-byte stores."""
-    inp = _small(RW, True, shape=(70, 131, 128))
-    M, N, _ = inp.shape
-    buf = torch.full((M * N + 1,), float("nan"), dtype=torch.bfloat16, device=DEV)
-    out = buf[1:].view(M, N)
+@pytest.mark.parametrize("offset,N", [(1, 131), (4, 136)])
+def test_unaligned_output_rows_fall_back(offset, N):
+    """An output base that is only 2- (or 8-) byte aligned: the kernel must not
+    use its 16-byte stores on rows that do not start on a 16-byte boundary,
+    even where N % 8 == 0."""
+    inp = _small(RW, True, shape=(70, N, 128))
+    M = inp.shape[0]
+    buf = torch.full((M * N + offset,), float("nan"), dtype=torch.bfloat16, device=DEV)
+    out = buf[offset:].view(M, N)
     run_gpu(inp, out=out)
     ref = oracle.scaled_mm(inp.a, inp.b, inp.scale_a, inp.scale_b, inp.bias, RW)
     nbad, worst, first = compare(out_bits(out), ref)
