@@ -109,9 +109,13 @@ int fp8_scaled_mm_with_config(const void* A, const void* B, const float* scale_a
                               int64_t M, int64_t N, int64_t K, int scaling_mode,
                               struct ihipStream_t* stream, int config_id);
 
+/* splits value that asks for a stream-K plan (see fp8_scaled_mm_with_plan). */
+#define FP8MM_SPLITS_STREAM_K (-1)
+
 /* The most general form: explicit tile configuration (config_id < 0: chosen
  * from the shape), split-K factor (splits == 0: chosen; 1: no split; at most
- * 64, clamped to the number of K slices), and workspace.  K is split only
+ * 64, clamped to the number of K slices; FP8MM_SPLITS_STREAM_K: stream-K,
+ * below), and workspace.  K is split only
  * with a non-NULL `workspace`: 256-byte aligned, at least
  * fp8_scaled_mm_workspace_size() bytes, zero-filled before its first use (its
  * first 256 KiB are arrival counters, which every call leaves at zero again;
@@ -119,7 +123,17 @@ int fp8_scaled_mm_with_config(const void* A, const void* B, const float* scale_a
  * With a NULL workspace the automatic plan does not split, and an explicit
  * splits > 1 returns FP8MM_ERR_WORKSPACE.  A workspace must not be used by
  * two calls that can run at the same time.  Results do not depend on which
- * workgroup finishes first: partial tiles are summed in split order. */
+ * workgroup finishes first: partial tiles are summed in split order.
+ *
+ * Stream-K (splits == FP8MM_SPLITS_STREAM_K; a generic configuration that can
+ * split K, else FP8MM_ERR_CONFIG; a workspace, else FP8MM_ERR_WORKSPACE):
+ * the grid fills every workgroup slot of the GPU and each workgroup takes an
+ * equal share of the tiles' (tile, K slice) iterations in tile-major order, so
+ * the work is balanced however the tile count compares with the CU count; a
+ * tile shared by several workgroups is finished through partial tiles summed
+ * in workgroup order.  Its workspace (fp8_scaled_mm_workspace_size with the
+ * same arguments) is bounded for any device; results are deterministic on a
+ * given device (the split points depend on its CU count). */
 int fp8_scaled_mm_with_plan(const void* A, const void* B, const float* scale_a,
                             const float* scale_b, const void* bias_or_null, void* out,
                             int64_t M, int64_t N, int64_t K, int scaling_mode,
@@ -160,7 +174,8 @@ int fp8_scaled_mm_noalloc(const void* A, const void* B, const float* scale_a,
                           int64_t N, int64_t K, int scaling_mode, struct ihipStream_t* stream,
                           int config_id, int splits);
 
-/* Workspace bytes the plan (config_id, splits; negative/zero = automatic)
+/* Workspace bytes the plan (config_id < 0 / splits == 0: automatic;
+ * splits == FP8MM_SPLITS_STREAM_K: stream-K, an upper bound for any device)
  * needs for this problem when the call has a workspace; 0 when it does not
  * split K, -1 for a bad mode.  Host logic only. */
 int64_t fp8_scaled_mm_workspace_size(int64_t M, int64_t N, int64_t K, int scaling_mode,

@@ -25,6 +25,9 @@ E4M3FN = 0
 E5M2 = 1
 _FORMATS = {"e4m3fn": E4M3FN, "e5m2": E5M2, E4M3FN: E4M3FN, E5M2: E5M2}
 
+# splits value of a stream-K plan (FP8MM_SPLITS_STREAM_K in include/fp8_scaled_mm.h)
+SPLITS_STREAM_K = -1
+
 # status codes from include/fp8_scaled_mm.h
 (OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_MODE, ERR_DEVICE, ERR_LAUNCH, ERR_CONFIG, ERR_WORKSPACE,
  ERR_FORMAT, ERR_SCRATCH) = range(11)
@@ -192,7 +195,8 @@ def fp8_scaled_mm(a: torch.Tensor, b: torch.Tensor, scale_a: torch.Tensor, scale
     view (stride (1, K)), which is the same memory.  Each operand is e4m3fn or
     e5m2: taken from its torch dtype, or from a_format / b_format for uint8
     codes (default e4m3fn).  `config` (-1: automatic) and `splits` (0:
-    automatic) select the plan.  When the plan splits K, its workspace is
+    automatic; SPLITS_STREAM_K: stream-K) select the plan.  When the plan
+    splits K, its workspace is
     `workspace` (a GPU byte tensor, zero-filled before first use) or, if that
     is None, one this module keeps per stream (allocated by torch)."""
     if mode not in _MODES:

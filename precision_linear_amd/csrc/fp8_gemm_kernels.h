@@ -58,6 +58,13 @@ struct Params {
     int splits, k_chunk;
     float* partials;       // num_tiles * splits * BM * BN floats (splits > 1)
     unsigned* counters;    // num_tiles arrival counters (splits > 1)
+    // Stream-K (the generic kernel's SK instantiation): the num_tiles * k_iters
+    // (tile, K slice) iterations, tile-major, are cut into gridDim.x equal
+    // ranges, workgroup w taking [w * total / G, (w + 1) * total / G); a tile
+    // is finished by the one workgroup that covers it whole, or by the
+    // segments (the workgroups whose ranges meet it) through partials and
+    // counters as in split-K, `splits` then being the room per tile for
+    // segments (an upper bound on their number).
 };
 
 typedef void (*Launch)(const Params&, dim3, hipStream_t);
@@ -66,6 +73,8 @@ struct LaunchPair {
     // The same tiles with B loaded non-temporally, for grids with a single row
     // of tiles (B is then read once); null where not compiled.
     Launch stream;
+    // The stream-K form (Cfg::STREAM_K_OK configurations only, else null).
+    Launch stream_k;
 };
 
 // Operand formats, as a kernel template parameter FMT: bit 0 set = A is e5m2,
@@ -256,6 +265,10 @@ struct Cfg {
     // partials, so it is compiled only where both fit in registers.
     static constexpr int PER_LANE_ACC = FM * FN * (MI == 32 ? 16 : 4);
     static constexpr bool SPLIT_OK = PER_LANE_ACC <= 64;
+    // A stream-K form is compiled for the 128 x 128 tiles only (a second
+    // instantiation of the kernel; the others would double the library for a
+    // plan that measured slower on every workload here).
+    static constexpr bool STREAM_K_OK = SPLIT_OK && BM == 128 && BN == 128;
     // Spread a stage's loads between MFMAs only where a K step has enough
     // MFMAs to hide them (the big, MFMA-bound tiles).
     static constexpr bool INTERLEAVE = MI == 32 && FM * FN >= 8;
@@ -880,7 +893,7 @@ __device__ __forceinline__ void run_stage(typename Mfma<C::MI_>::acc_t (&acc)[C:
 }
 
 template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int STAGES, int MI, int GROUP_M,
-          bool NT_B, int FMT>
+          bool NT_B, int FMT, bool SK = false>
 __global__ void __launch_bounds__(WAVES_M * WAVES_N * kWave,
                                   (Cfg<BM, BN, BK, WAVES_M, WAVES_N, STAGES, MI, GROUP_M>::OCCUPANCY))
 fp8_gemm_kernel(Params p) {
@@ -906,18 +919,16 @@ fp8_gemm_kernel(Params p) {
     const bool has_bias = p.bias != nullptr;
 
     __shared__ unsigned arrival;
-    const int num_units = p.num_tiles * p.splits;
-    for (int u = wg; u < num_units; u += G) {
-        const int t = u / p.splits;             // the splits of a tile are neighbours
-        const int split = u - t * p.splits;
+    // One work unit: K slices [kb, kb + k_iters) of tile t, part `part` of the
+    // tile's `nparts` (nparts > 1: its partial goes to slot t * splits + part,
+    // and the last of them to arrive finishes the tile).
+    auto unit = [&](const int t, const int kb, const int k_iters, const int part, const int nparts) {
         int pm, pn;
         tile_coords(t, p.tiles_m, p.tiles_n, GROUP_M, pm, pn);
         const int row0 = pm * BM;
         const int col0 = pn * BN;
-        // This unit's K range, as whole BK slices; the buffer resources start at
-        // its first byte so the stage code sees a K range beginning at 0.
-        const int kb = split * p.k_chunk;
-        const int k_iters = max(0, min(p.k_chunk, p.k_iters - kb));
+        // The buffer resources start at the unit's first K byte, so the stage
+        // code sees a K range beginning at 0.
         const int kskip = kb * BK;
         const int klim = p.K - kskip;
         // With a single row of tiles (the skinny shapes) every workgroup reads
@@ -1014,10 +1025,11 @@ fp8_gemm_kernel(Params p) {
             }
         }
 
-        if constexpr (C::SPLIT_OK) if (p.splits > 1) {
+        if constexpr (C::SPLIT_OK) if (nparts > 1) {
             // Publish this unit's partial tile and count the arrival; the
             // stores have completed (vmcnt 0) before the arrival is counted.
-            partial_publish<C::FN, C::FM>(acc, p.partials + (size_t)u * (BM * BN), C::THREADS, tid,
+            partial_publish<C::FN, C::FM>(acc, p.partials + ((size_t)t * p.splits + part) * (BM * BN),
+                                          C::THREADS, tid,
                                           BM * BN * 4);
             wait_vmcnt<0>();
             __syncthreads();
@@ -1027,7 +1039,7 @@ fp8_gemm_kernel(Params p) {
             __syncthreads();
             // Only the last of the tile's units goes on; it adds the partials in
             // split order (deterministic whatever the arrival order).
-            if (arrival != (unsigned)(p.splits - 1)) continue;
+            if (arrival != (unsigned)(nparts - 1)) return;
             if (tid == 0)
                 __hip_atomic_store(&p.counters[t], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 #pragma unroll
@@ -1037,7 +1049,7 @@ fp8_gemm_kernel(Params p) {
 #pragma unroll
                     for (int v = 0; v < F::NACC; ++v) acc[i][j][v] = 0.f;
             partial_accumulate_all<C::FN, C::FM>(acc, p.partials + (size_t)t * p.splits * (BM * BN),
-                                                 p.splits, BM * BN, C::THREADS, tid);
+                                                 nparts, BM * BN, C::THREADS, tid);
         }
 
         // Epilogue parameters into LDS (beside the stage buffers).
@@ -1063,6 +1075,37 @@ fp8_gemm_kernel(Params p) {
         barrier_lds();
         stage_and_store<C>(acc, smem, p, row0, col0, wm * C::WTM, wn * C::WTN, epi_sa, epi_sb,
                            epi_bias, s_pt, has_bias, lane, tid);
+    };
+
+    if constexpr (SK) {
+        // This workgroup's equal share of the tile-major (tile, K slice)
+        // iterations; each tile it meets is one unit, whose part is its rank
+        // among the workgroups meeting that tile.
+        const int64_t total = (int64_t)p.num_tiles * p.k_iters;
+        auto start_of = [&](int64_t w) { return w * total / G; };
+        auto wg_of = [&](int64_t i) {   // the workgroup whose range holds iteration i
+            int64_t w = i * G / total;
+            while (w + 1 < G && start_of(w + 1) <= i) ++w;
+            return w;
+        };
+        const int64_t end = start_of(wg + 1);
+        for (int64_t it = start_of(wg); it < end;) {
+            const int t = (int)(it / p.k_iters);
+            const int kb = (int)(it - (int64_t)t * p.k_iters);
+            const int kn = (int)min((int64_t)(p.k_iters - kb), end - it);
+            const int64_t first = wg_of((int64_t)t * p.k_iters);
+            const int64_t last = wg_of((int64_t)(t + 1) * p.k_iters - 1);
+            unit(t, kb, kn, (int)(wg - first), (int)(last - first + 1));
+            it += kn;
+        }
+    } else {
+        const int num_units = p.num_tiles * p.splits;
+        for (int u = wg; u < num_units; u += G) {
+            const int t = u / p.splits;             // the splits of a tile are neighbours
+            const int split = u - t * p.splits;
+            const int kb = split * p.k_chunk;
+            unit(t, kb, max(0, min(p.k_chunk, p.k_iters - kb)), split, p.splits);
+        }
     }
 }
 
@@ -1572,18 +1615,28 @@ void launch_pp(const Params& p, dim3 grid, hipStream_t stream) {
 }
 
 template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int STAGES, int MI, int GROUP_M,
-          bool NT_B, int FMT>
+          bool NT_B, int FMT, bool SK = false>
 void launch_cfg(const Params& p, dim3 grid, hipStream_t stream) {
     using C = Cfg<BM, BN, BK, WAVES_M, WAVES_N, STAGES, MI, GROUP_M, NT_B, FMT>;
-    hipLaunchKernelGGL((fp8_gemm_kernel<BM, BN, BK, WAVES_M, WAVES_N, STAGES, MI, GROUP_M, NT_B, FMT>),
+    hipLaunchKernelGGL((fp8_gemm_kernel<BM, BN, BK, WAVES_M, WAVES_N, STAGES, MI, GROUP_M, NT_B, FMT, SK>),
                        grid, dim3(C::THREADS), 0, stream, p);
+}
+
+// The stream-K launch of a configuration, or null where none is compiled.
+template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int STAGES, int MI, int GROUP_M, int FMT>
+constexpr Launch stream_k_launch() {
+    if constexpr (Cfg<BM, BN, BK, WAVES_M, WAVES_N, STAGES, MI, GROUP_M>::STREAM_K_OK)
+        return &launch_cfg<BM, BN, BK, WAVES_M, WAVES_N, STAGES, MI, GROUP_M, false, FMT, true>;
+    else
+        return nullptr;
 }
 
 }  // namespace
 
 #define FP8MM_LAUNCH_PAIR(FMT, name, BM, BN, BK, WMW, WNW, ST, MI, GM)                        \
     LaunchPair{&launch_cfg<BM, BN, BK, WMW, WNW, ST, MI, GM, false, FMT>,                    \
-               &launch_cfg<BM, BN, BK, WMW, WNW, ST, MI, GM, true, FMT>},
+               &launch_cfg<BM, BN, BK, WMW, WNW, ST, MI, GM, true, FMT>,                     \
+               stream_k_launch<BM, BN, BK, WMW, WNW, ST, MI, GM, FMT>()},
 #define FP8MM_PAIR_F(FMT) FP8MM_PAIR_F_##FMT
 #define FP8MM_PAIR_F_0(...) FP8MM_LAUNCH_PAIR(0, __VA_ARGS__)
 #define FP8MM_PAIR_F_1(...) FP8MM_LAUNCH_PAIR(1, __VA_ARGS__)
@@ -1596,5 +1649,5 @@ void launch_cfg(const Params& p, dim3 grid, hipStream_t stream) {
     namespace fp8mm {                                                             \
     LaunchPair NAME[kNumConfigs] = {                                              \
         FP8MM_GENERIC_CONFIGS(FP8MM_PAIR_F(FMT))                                  \
-        LaunchPair{&launch_pp<8, FMT>, nullptr}};                                 \
+        LaunchPair{&launch_pp<8, FMT>, nullptr, nullptr}};                        \
     }

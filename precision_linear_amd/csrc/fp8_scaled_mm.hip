@@ -49,19 +49,21 @@ struct ConfigInfo {
     int threads;
     int lds_bytes;
     int occupancy;   // workgroups per CU the persistent grid assumes
+    bool stream_k_ok;
 };
 
 #define FP8MM_CFG_INFO(name, BM, BN, BK, WMW, WNW, ST, MI, GM)                               \
     ConfigInfo{name, BM, BN, BK, Cfg<BM, BN, BK, WMW, WNW, ST, MI, GM>::SPLIT_OK,             \
                Cfg<BM, BN, BK, WMW, WNW, ST, MI, GM>::THREADS,                                \
                Cfg<BM, BN, BK, WMW, WNW, ST, MI, GM>::LDS_BYTES,                              \
-               Cfg<BM, BN, BK, WMW, WNW, ST, MI, GM>::OCCUPANCY},
+               Cfg<BM, BN, BK, WMW, WNW, ST, MI, GM>::OCCUPANCY,                              \
+               Cfg<BM, BN, BK, WMW, WNW, ST, MI, GM>::STREAM_K_OK},
 
 // Ids are the positions in this table (the C ABI's config_id).
 const ConfigInfo kConfigs[kNumConfigs] = {
     FP8MM_GENERIC_CONFIGS(FP8MM_CFG_INFO)
     ConfigInfo{"pp_bm256_bn256_bk128_w8_mfma16", pp::BM, pp::BN, pp::BK, true, pp::THREADS,
-               pp::LDS_BYTES, 1},
+               pp::LDS_BYTES, 1, false},
 };
 #undef FP8MM_CFG_INFO
 
@@ -264,6 +266,23 @@ int64_t workspace_bytes(int cfg, int64_t M, int64_t N, int splits) {
     return kCounterBytes + tiles * splits * (int64_t)c.bm * c.bn * 4;
 }
 
+// Stream-K: the grid's g workgroups share the tiles * k_iters (tile, K slice)
+// iterations, workgroup w from floor(w * total / g) on, so the range starts
+// inside one tile (k_iters long) number at most ceil(g / tiles), and the
+// workgroups meeting a tile at most ceil(g / tiles) + 1 (checked by brute force
+// over random tile counts, K lengths and grids): the room for partial tiles
+// per tile.  Workspace sizes use the largest grid a device can have
+// (kMaxSlots workgroups); the bound grows with g, so it covers every smaller
+// grid.
+constexpr int64_t kMaxSlots = 1024;
+
+int64_t sk_segments(int64_t tiles, int64_t k_iters, int64_t g) {
+    const int64_t total = tiles * k_iters;
+    if (g > total) g = total;
+    const int64_t m = cdiv(g, tiles) + 1;
+    return m < g ? m : g;
+}
+
 // Device scratch for fp8_scaled_mm_noalloc: its split-K counters and partial
 // tiles, for callers that cannot allocate.  Each GPU the library runs on
 // holds one copy from module load until the process ends; every call on that
@@ -298,6 +317,86 @@ __global__ void __launch_bounds__(256) clear_counters_kernel(unsigned* c, int n)
 // Where a call's split-K workspace comes from.
 enum class WsSource { kNone, kCaller, kScratch };
 
+Params base_params(const void* A, const void* B, const float* scale_a, const float* scale_b,
+                   const void* bias, void* out, int64_t M, int64_t N, int64_t K, int mode,
+                   const ConfigInfo& c) {
+    Params p;
+    p.A = static_cast<const uint8_t*>(A);
+    p.B = static_cast<const uint8_t*>(B);
+    p.scale_a = scale_a;
+    p.scale_b = scale_b;
+    p.bias = static_cast<const uint16_t*>(bias);
+    p.out = static_cast<uint16_t*>(out);
+    p.M = (int)M;
+    p.N = (int)N;
+    p.K = (int)K;
+    p.tiles_m = (int)cdiv(M, c.bm);
+    p.tiles_n = (int)cdiv(N, c.bn);
+    p.num_tiles = p.tiles_m * p.tiles_n;
+    p.k_iters = (int)cdiv(K, c.bk);
+    p.rowwise = mode == FP8MM_ROWWISE;
+    p.vec_store = (N % 4 == 0) && aligned(out, 8);
+    p.vec16 = (N % 8 == 0) && aligned(out, 16);
+    p.splits = 1;
+    p.k_chunk = p.k_iters;
+    p.counters = nullptr;
+    p.partials = nullptr;
+    return p;
+}
+
+// A stream-K plan (splits == FP8MM_SPLITS_STREAM_K): every workgroup slot of
+// the GPU takes an equal share of the (tile, K slice) iterations; the tiles
+// that several workgroups share are finished through partials and counters
+// as in split-K.  Configurations with a stream-K kernel only (the 128 x 128
+// tiles); validated arguments.
+int run_stream_k(const void* A, int fmt, const void* B, const float* scale_a, const float* scale_b,
+                 const void* bias, void* out, int64_t M, int64_t N, int64_t K, int mode,
+                 struct ihipStream_t* stream, int config_id, void* workspace, int64_t workspace_size,
+                 WsSource src) {
+    const bool can_split = src != WsSource::kNone;
+    if (!can_split) return FP8MM_ERR_WORKSPACE;
+    const int cfg = config_id >= 0 ? config_id : choose_config(M, N, K, mode, bias != nullptr, true);
+    const ConfigInfo& c = kConfigs[cfg];
+    if (!c.stream_k_ok) return FP8MM_ERR_CONFIG;
+    const int64_t tiles = cdiv(M, c.bm) * cdiv(N, c.bn);
+    const int64_t k_iters = cdiv(K, c.bk);
+    if (tiles > kMaxCounters || tiles * k_iters > INT32_MAX) return FP8MM_ERR_SHAPE;
+
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return FP8MM_ERR_DEVICE;
+    const int cus = device_cus(dev);
+    if (cus <= 0) return FP8MM_ERR_DEVICE;
+    int64_t g = (int64_t)cus * c.occupancy;
+    if (g > kMaxSlots) g = kMaxSlots;
+    if (g > tiles * k_iters) g = tiles * k_iters;
+    const int64_t segs = sk_segments(tiles, k_iters, g);
+    const int64_t ws_need = kCounterBytes + tiles * segs * (int64_t)c.bm * c.bn * 4;
+    if (src == WsSource::kCaller) {
+        if (workspace_size < ws_need) return FP8MM_ERR_WORKSPACE;
+        if ((uintptr_t)workspace & 255) return FP8MM_ERR_ALIGN;
+    } else if (ws_need > kScratchBytes) {
+        return FP8MM_ERR_SCRATCH;
+    }
+    const hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+    void* ws = workspace;
+    (void)hipGetLastError();
+    if (src == WsSource::kScratch) {
+        ws = scratch_on(dev);
+        if (!ws) return FP8MM_ERR_DEVICE;
+        const int n = (int)tiles;
+        const int blocks = (n + 255) / 256 < 256 ? (n + 255) / 256 : 256;
+        hipLaunchKernelGGL(clear_counters_kernel, dim3(blocks), dim3(256), 0, hs,
+                           static_cast<unsigned*>(ws), n);
+    }
+    Params p = base_params(A, B, scale_a, scale_b, bias, out, M, N, K, mode, c);
+    p.splits = (int)segs;
+    p.counters = static_cast<unsigned*>(ws);
+    p.partials = reinterpret_cast<float*>(static_cast<char*>(ws) + kCounterBytes);
+    kLaunch[fmt][cfg].stream_k(p, dim3((unsigned)g), hs);
+    if (hipGetLastError() != hipSuccess) return FP8MM_ERR_LAUNCH;
+    return FP8MM_OK;
+}
+
 int run_mm(const void* A, int a_format, const void* B, int b_format, const float* scale_a,
            const float* scale_b, const void* bias, void* out, int64_t M, int64_t N, int64_t K,
            int mode, struct ihipStream_t* stream, int config_id, int splits, void* workspace,
@@ -309,8 +408,11 @@ int run_mm(const void* A, int a_format, const void* B, int b_format, const float
     int st = validate(A, B, scale_a, scale_b, bias, out, M, N, K, mode);
     if (st != FP8MM_OK) return st;
     if (config_id >= kNumConfigs) return FP8MM_ERR_CONFIG;
-    if (splits < 0 || splits > 64) return FP8MM_ERR_CONFIG;
+    if (splits < FP8MM_SPLITS_STREAM_K || splits > 64) return FP8MM_ERR_CONFIG;
     if (M == 0 || N == 0) return FP8MM_OK;
+    if (splits == FP8MM_SPLITS_STREAM_K)
+        return run_stream_k(A, fmt, B, scale_a, scale_b, bias, out, M, N, K, mode, stream, config_id,
+                            workspace, workspace_size, src);
     // K is split only where the partial tiles have somewhere to go: without a
     // workspace the automatic plan does not split, and an explicit split
     // count that still splits after clamping to the K slices is refused.
@@ -352,27 +454,9 @@ int run_mm(const void* A, int a_format, const void* B, int b_format, const float
                            static_cast<unsigned*>(ws), n);
     }
 
-    Params p;
-    p.A = static_cast<const uint8_t*>(A);
-    p.B = static_cast<const uint8_t*>(B);
-    p.scale_a = scale_a;
-    p.scale_b = scale_b;
-    p.bias = static_cast<const uint16_t*>(bias);
-    p.out = static_cast<uint16_t*>(out);
-    p.M = (int)M;
-    p.N = (int)N;
-    p.K = (int)K;
-    p.tiles_m = (int)cdiv(M, c.bm);
-    p.tiles_n = (int)cdiv(N, c.bn);
-    p.num_tiles = (int)tiles;
-    p.k_iters = (int)k_iters;
-    p.rowwise = mode == FP8MM_ROWWISE;
-    p.vec_store = (N % 4 == 0) && aligned(out, 8);
-    p.vec16 = (N % 8 == 0) && aligned(out, 16);
+    Params p = base_params(A, B, scale_a, scale_b, bias, out, M, N, K, mode, c);
     p.splits = sp;
     p.k_chunk = (int)cdiv(k_iters, sp);
-    p.counters = nullptr;
-    p.partials = nullptr;
     if (sp > 1) {
         p.counters = static_cast<unsigned*>(ws);
         p.partials = reinterpret_cast<float*>(static_cast<char*>(ws) + kCounterBytes);
@@ -482,8 +566,15 @@ int64_t fp8_scaled_mm_workspace_size(int64_t M, int64_t N, int64_t K, int mode, 
                                      int config_id, int splits) {
     if (mode != FP8MM_PER_TENSOR && mode != FP8MM_ROWWISE) return -1;
     if (M <= 0 || N <= 0 || K < 16 || K % 16 != 0 || config_id >= kNumConfigs) return 0;
-    if (splits < 0 || splits > 64) return 0;
+    if (splits < FP8MM_SPLITS_STREAM_K || splits > 64) return 0;
     const int cfg = config_id >= 0 ? config_id : choose_config(M, N, K, mode, has_bias, true);
+    if (splits == FP8MM_SPLITS_STREAM_K) {
+        const ConfigInfo& c = kConfigs[cfg];
+        if (!c.stream_k_ok) return 0;
+        const int64_t tiles = cdiv(M, c.bm) * cdiv(N, c.bn);
+        const int64_t k_iters = cdiv(K, c.bk);
+        return kCounterBytes + tiles * sk_segments(tiles, k_iters, kMaxSlots) * (int64_t)c.bm * c.bn * 4;
+    }
     return workspace_bytes(cfg, M, N, plan_splits(cfg, M, N, K, splits));
 }
 

@@ -141,12 +141,41 @@ def test_workspace_and_split_host_logic(L):
     assert L.fp8_scaled_mm_select_splits(16, 16, 16, 5, 0, -1) == -1
 
 
+def test_stream_k_plan_validation(L):
+    P = 0x10000
+    f = L.fp8_scaled_mm_with_plan
+    names = binding.config_names()
+    c9 = names.index("bm128_bn128_bk128_w2x2_s2_mfma32")
+    pp = names.index("pp_bm256_bn256_bk128_w8_mfma16")
+    sk = binding.SPLITS_STREAM_K
+    # a workspace is required; the ping-pong kernel and configurations that
+    # cannot split K have no stream-K form; -2 is no plan at all
+    assert f(P, P, P, P, None, P, 512, 3072, 12288, 1, None, c9, sk, None, 0) == binding.ERR_WORKSPACE
+    assert f(P, P, P, P, None, P, 512, 3072, 12288, 1, None, pp, sk, P, 1 << 30) == binding.ERR_CONFIG
+    assert f(P, P, P, P, None, P, 512, 3072, 12288, 1, None, c9, -2, P, 1 << 30) == binding.ERR_CONFIG
+    assert L.fp8_scaled_mm_workspace_size(512, 3072, 12288, 1, 0, pp, sk) == 0
+    for cfg in range(len(names)):
+        # a configuration without a split-K form has no stream-K form either
+        if cfg != pp and L.fp8_scaled_mm_workspace_size(512, 3072, 12288, 1, 0, cfg, 2) == 0:
+            assert L.fp8_scaled_mm_workspace_size(512, 3072, 12288, 1, 0, cfg, sk) == 0
+
+
+def test_stream_k_workspace_bound(L):
+    # room for the partial tiles of every tile's segments, for any grid of up
+    # to 1024 workgroups: 96 tiles of 128 x 128, 96 K slices each
+    c9 = binding.config_names().index("bm128_bn128_bk128_w2x2_s2_mfma32")
+    ws = L.fp8_scaled_mm_workspace_size(512, 3072, 12288, 1, 0, c9, binding.SPLITS_STREAM_K)
+    tiles = 4 * 24
+    segs = -(-1024 // tiles) + 1           # workgroups that can meet one tile
+    assert ws == 256 * 1024 + tiles * segs * 128 * 128 * 4
+
+
 def test_plan_validation(L):
     P = 0x10000
     f = L.fp8_scaled_mm_with_plan
     cfg = binding.config_names().index("bm128_bn128_bk128_w2x2_s2_mfma32")
     assert f(P, P, P, P, None, P, 128, 128, 4096, 0, None, cfg, 65, None, 0) == binding.ERR_CONFIG
-    assert f(P, P, P, P, None, P, 128, 128, 4096, 0, None, cfg, -1, None, 0) == binding.ERR_CONFIG
+    assert f(P, P, P, P, None, P, 128, 128, 4096, 0, None, cfg, -2, None, 0) == binding.ERR_CONFIG
     # caller workspace too small for a 4-way split
     assert f(P, P, P, P, None, P, 128, 128, 4096, 0, None, cfg, 4, P, 1024) == binding.ERR_WORKSPACE
     need = L.fp8_scaled_mm_workspace_size(128, 128, 4096, 0, 0, cfg, 4)

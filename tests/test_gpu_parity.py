@@ -465,6 +465,45 @@ def test_split_k_changing_plans_on_one_stream():
         assert compare(got, ref)[0] == 0, (shape, splits)
 
 
+# ------------------------------------------------------------------ stream-K ---
+
+def _sk_configs():
+    # every configuration with a stream-K form (split-K capable, not ping-pong)
+    L = binding.lib()
+    return [c for c, n in enumerate(binding.config_names())
+            if L.fp8_scaled_mm_workspace_size(512, 512, 4096, 1, 0, c, binding.SPLITS_STREAM_K) > 0]
+
+
+@pytest.mark.parametrize("config", _sk_configs(),
+                         ids=[binding.config_names()[c] for c in _sk_configs()])
+@pytest.mark.parametrize("shape,mode,bias", [((300, 200, 1040), PT, True),
+                                             ((640, 768, 4096), RW, True),
+                                             ((1000, 1200, 2048), RW, False)])
+def test_stream_k_parity(config, shape, mode, bias):
+    # 6, 30 and 80 tiles of 128 x 128 over every workgroup slot of the GPU: each
+    # tile shared by several workgroups (one K slice each for the first shape),
+    # ranges that end inside tiles and start inside the next, ragged edges
+    inp = wl.make_inputs(*shape, mode, "codes", bias=bias, key=config * 7 + shape[0])
+    got = out_bits(run_gpu_plan(inp, config, binding.SPLITS_STREAM_K))
+    ref = oracle.scaled_mm(inp.a, inp.b, inp.scale_a, inp.scale_b, inp.bias, mode)
+    nbad, worst, first = compare(got, ref)
+    assert nbad == 0, (nbad, worst, first)
+
+
+def test_stream_k_deterministic_and_counters_left_zero():
+    inp = wl.make_inputs(512, 3072, 4096, RW, "normal", bias=True, key=13)
+    cfg = _cfg("bm128_bn128_bk128_w2x2_s2_mfma32")
+    need = binding.workspace_size(512, 3072, 4096, RW, True, cfg, binding.SPLITS_STREAM_K)
+    ws = torch.zeros(need, dtype=torch.uint8, device=DEV)
+    r1 = out_bits(run_gpu_plan(inp, cfg, binding.SPLITS_STREAM_K, workspace=ws))
+    r2 = out_bits(run_gpu_plan(inp, cfg, binding.SPLITS_STREAM_K, workspace=ws))
+    r3 = out_bits(run_gpu_plan(inp, cfg, binding.SPLITS_STREAM_K))
+    assert np.array_equal(r1, r2) and np.array_equal(r1, r3)
+    assert int(ws[:262144].sum()) == 0                            # counters back at zero
+    ref = oracle.scaled_mm(inp.a, inp.b, inp.scale_a, inp.scale_b, inp.bias, RW)
+    assert compare(r1, ref)[0] == 0
+
+
 def test_tensors_on_another_device_are_refused():
     # every pointer goes to a kernel on the operands' GPU: a host tensor
     # anywhere in the call must be refused before anything is launched

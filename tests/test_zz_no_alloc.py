@@ -55,6 +55,9 @@ CASES = [
      ((300, 260, 1040, RW, True, "codes"), "pp_bm256_bn256_bk128_w8_mfma16", 2)),
     (((150, 230, 1040, RW, True, "codes"), "bm128_bn32_bk256_w4x2_s3_mfma16", 4),
      ((16, 200, 1040, PT, False, "codes"), "bm16_bn32_bk512_w1x2_s6_mfma16", 2)),
+    # stream-K plans (splits -1)
+    (((640, 768, 4096, RW, True, "codes"), "bm128_bn128_bk128_w2x2_s2_mfma32", -1),
+     ((300, 200, 1040, PT, False, "codes"), "bm128_bn128_bk128_w2x4_s4_mfma32", -1)),
 ]
 
 
