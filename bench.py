@@ -454,6 +454,11 @@ def main():
                          "MALL flushed before every launch (kernel traces)")
     ap.add_argument("--profile-copy-mib", type=int, default=0, metavar="MIB",
                     help="only run one device-to-device copy of MIB MiB (counter calibration)")
+    ap.add_argument("--profile-vendor", type=int, default=0, metavar="R",
+                    help="only time the M=N=K=8192 multiplies (per-tensor, row-wise) against "
+                         "torch._scaled_mm (hipBLASLt) on the same operands: 60 settling "
+                         "launches of each, then R rounds of 40 back-to-back launches of each "
+                         "(counter runs and context)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path (the "
@@ -487,6 +492,36 @@ def main():
                 binding.fp8_quantize(x, mode, q=q, scale=s, fmt=fmt)
             torch.cuda.synchronize()
         print(json.dumps({"quantiser_launches": args.profile_quant, "shapes": len(QUANT_SHAPES)}))
+        return
+    if args.profile_vendor:
+        from precision_linear_amd import workloads as wl
+        res = {}
+        for name in ("sq8192_pt", "sq8192_rw"):
+            p = Problem(name, dev)
+            a8, b8 = p.a.view(torch.float8_e4m3fn), p.b.view(torch.float8_e4m3fn)
+            sa, sb = ((p.sa.view(-1, 1), p.sb.view(1, -1)) if p.w.mode == wl.ROWWISE
+                      else (p.sa, p.sb))
+            fns = {"ours": p.launch,
+                   "hipblaslt": lambda: torch._scaled_mm(a8, b8.t(), scale_a=sa, scale_b=sb,
+                                                         out_dtype=torch.bfloat16)}
+            for f in fns.values():
+                for _ in range(60):
+                    f()
+            torch.cuda.synchronize()
+            res[name] = {k: [] for k in fns}
+            for _ in range(args.profile_vendor):
+                for k, f in fns.items():
+                    e0 = torch.cuda.Event(enable_timing=True)
+                    e1 = torch.cuda.Event(enable_timing=True)
+                    e0.record()
+                    for _ in range(40):
+                        f()
+                    e1.record()
+                    torch.cuda.synchronize()
+                    res[name][k].append(round(e0.elapsed_time(e1) / 40 * 1e3, 1))
+            del p
+            torch.cuda.empty_cache()
+        print(json.dumps({"us_per_launch": res}))
         return
     if args.profile_gemm:
         p = Problem(args.profile_workload, dev)
