@@ -13,8 +13,11 @@ settles; the timed steps measure the settled rate.
 
 The JSON line also carries
   roofline      the GEMM kernel's own throughput (algorithmic flops per launch
-                over its average launch time, from HIP events on the launch
-                stream) against the dense-FP8 MFMA peak of MI355X;
+                over its average launch time: the GPU time between two HIP
+                events around the timed steps, on the launch stream, divided
+                by the launches) against the dense-FP8 MFMA peak of MI355X;
+                config.kernel_us gives the spread of single launches (one
+                event pair each, a pass after the timed steps);
   protocol      the gist "matmul_fp8.py" timing protocol (function
                 `benchmark`: one untimed call, 8 warm-ups, then 32 runs, each
                 timed on its own, reported as p50 with p20 / p80) for both
@@ -34,7 +37,10 @@ The JSON line also carries
                 their 8-way column shards, with the MALL flushed before every
                 launch, reported in HBM GB/s; the gist's mid-size shape sweep,
                 the ragged shapes and the e5m2 / mixed-format 8192^3 multiplies
-                in TFLOP/s; the quantisers in HBM GB/s.
+                in TFLOP/s, operands resident (us_p50 from an event pair per
+                launch; us_batch per launch of 20 back to back, which leaves
+                out the few microseconds each event pair adds to a short
+                launch); the quantisers in HBM GB/s.
 """
 import argparse
 import hashlib
@@ -163,6 +169,23 @@ def time_launches(problem, n, flush=None):
     return [s.elapsed_time(e) for s, e in evs]
 
 
+def batch_launches(problem, n=20, reps=3):
+    """Mean time per launch (ms) of n launches back to back between two HIP
+    events, median over reps batches: the kernel's rate without the gaps that
+    an event pair around every launch adds."""
+    import torch
+    ts = []
+    for _ in range(reps):
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(n):
+            problem.launch()
+        e.record()
+        torch.cuda.synchronize()
+        ts.append(s.elapsed_time(e) / n)
+    return sorted(ts)[len(ts) // 2]
+
+
 def quantiles(ts):
     q = np.quantile(np.asarray(ts, dtype=np.float64), [0.2, 0.5, 0.8])
     return {"p20_us": round(q[0] * 1e3, 2), "p50_us": round(q[1] * 1e3, 2),
@@ -230,6 +253,7 @@ def resident_results(dev, names, reps=20, keep=None):
         warm_up(p)
         ts = sorted(time_launches(p, reps))
         t50 = ts[len(ts) // 2] * 1e-3
+        tb = batch_launches(p) * 1e-3
         tf = p.w.flops / t50 / 1e12
         t_mfma = p.w.flops / (PEAK_FP8_TFLOPS * 1e12)
         t_hbm = p.w.algorithmic_bytes / (PEAK_HBM_GBS * 1e9)
@@ -239,6 +263,8 @@ def resident_results(dev, names, reps=20, keep=None):
                     "frac_mfma": round(tf / PEAK_FP8_TFLOPS, 4),
                     "bound": "mfma" if t_mfma >= t_hbm else "hbm",
                     "frac_roofline": round(max(t_mfma, t_hbm) / t50, 4),
+                    "us_batch": round(tb * 1e6, 2),
+                    "frac_roofline_batch": round(max(t_mfma, t_hbm) / tb, 4),
                     "inputs_sha256": p.inp.sha256()})
         if keep is not None:
             keep.append((name, p.inp, p.sample))
@@ -559,23 +585,33 @@ def main():
             p.launch()
     torch.cuda.synchronize()
 
-    durations = {p.name: [] for p in probs}
+    # The timed steps: launches back to back, with one HIP event pair around
+    # all of them on the launch stream (events between launches would add
+    # their own gaps to the step time).
     torch.cuda.synchronize()
+    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
+    g0.record()
+    for _ in range(args.steps):
+        for p in probs:
+            p.launch()
+    g1.record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    elapsed = t1 - t0
+    kernel_avg_s = g0.elapsed_time(g1) * 1e-3 / (args.steps * len(probs))
+    achieved = probs[0].w.flops / kernel_avg_s / 1e12
+    # Per-launch spread, from one event pair per launch in a pass of its own.
+    pairs = {p.name: [] for p in probs}
     for _ in range(args.steps):
         for p in probs:
             s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             s.record()
             p.launch()
             e.record()
-            durations[p.name].append((s, e))
+            pairs[p.name].append((s, e))
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    elapsed = t1 - t0
-    per_kernel = {k: [s.elapsed_time(e) for s, e in v] for k, v in durations.items()}
-    all_ms = [x for v in per_kernel.values() for x in v]
-    kernel_avg_s = sum(all_ms) / len(all_ms) * 1e-3
-    achieved = probs[0].w.flops / kernel_avg_s / 1e12
+    per_kernel = {k: [s.elapsed_time(e) for s, e in v] for k, v in pairs.items()}
 
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
