@@ -363,14 +363,14 @@ quant_tensor_kernel(const uint16_t* __restrict__ x, uint8_t* __restrict__ q, int
 // count as the grid is that, but not when other kernels hold CUs (another
 // stream, another process).  So the wait is bounded: a workgroup that has
 // waited 1 ms of the constant-rate wall clock (or the limit set by
-// fp8_quantize_set_wait_limit_us) tries to claim its word with a
-// compare-and-swap (0 -> kGaveUp); if that succeeds it leaves, freeing its
-// CU for the workgroups not yet started, and its share is left to the last
-// to arrive, whose exchange of that word returns kGaveUp: after its own pass 2
-// it converts every share so left (re-reading x).  If the claim fails, the
-// scale has just arrived and the workgroup goes on.  Each word thus has one
-// owner at every moment, and the result never depends on which path a share
-// took.
+// fp8_quantize_set_wait_limit_us) claims its word by exchanging kGaveUp into
+// it.  If the exchange returns 0 it leaves, freeing its CU for the workgroups
+// not yet started, and its share is left to the last to arrive, whose own
+// exchange of that word returns kGaveUp: after its own pass 2 it converts
+// every share so left (re-reading x).  If the exchange returns the scale, the
+// scale had just arrived: the workgroup sets the word back to 0 and goes on.
+// Each word thus has one owner at every moment, and the result never depends
+// on which path a share took.
 //
 // Workspace (32-bit words; zero-filled before its first use, and every call
 // sets them back to zero: the last to arrive resets the counter, the maxima
