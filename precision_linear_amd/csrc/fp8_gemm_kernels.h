@@ -490,6 +490,16 @@ __device__ __forceinline__ void partial_accumulate(A (&acc)[FN][FM], const float
     }
 }
 
+template <int FN, int FM, class A>
+__device__ __forceinline__ void acc_add(A (&acc)[FN][FM], const A (&x)[FN][FM]) {
+#pragma unroll
+    for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int j = 0; j < FM; ++j)
+#pragma unroll
+            for (int e = 0; e < (int)(sizeof(A) / 4); ++e) acc[i][j][e] += x[i][j][e];
+}
+
 // acc += the partial tiles 0 .. splits-1 of one tile (stored one after the
 // other, tile_floats apart, each in the layout above), added in split order.
 // With few chunks per partial (small tiles) the loads of several partials go
@@ -527,6 +537,30 @@ __device__ __forceinline__ void partial_accumulate_all(A (&acc)[FN][FM], const f
                     for (int c = 0; c < NC; ++c)
                         acc_chunk_add<FN, FM>(acc, c, __builtin_bit_cast(v4f, x[k][c]));
         }
+    }
+}
+
+// acc = the sum of the partial tiles 0 .. splits-1 of one tile, added in split
+// order into zeroed accumulators; partial own_q is `own` (this unit's, still
+// in registers), the others are read from memory (stored one after the
+// other, tile_floats apart, each in the layout above).  For partials of more
+// than 8 chunks per thread, which go out one partial per batch: not reading
+// its own back saves one memory latency.
+template <int FN, int FM, class A>
+__device__ __forceinline__ void partial_sum_in_order(A (&acc)[FN][FM], const A (&own)[FN][FM],
+                                                     int own_q, const float* tile_parts, int splits,
+                                                     int tile_floats, int stride, int idx) {
+    static_assert(FN * FM * (int)(sizeof(A) / 16) > 8, "one partial per batch");
+#pragma unroll
+    for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int j = 0; j < FM; ++j) acc[i][j] = A{};
+    for (int q = 0; q < splits; ++q) {
+        if (q == own_q)
+            acc_add<FN, FM>(acc, own);
+        else
+            partial_accumulate<FN, FM>(acc, tile_parts + (size_t)q * tile_floats, stride, idx,
+                                       (uint32_t)tile_floats * 4);
     }
 }
 
@@ -1028,8 +1062,8 @@ fp8_gemm_kernel(Params p) {
         if constexpr (C::SPLIT_OK) if (nparts > 1) {
             // Publish this unit's partial tile and count the arrival; the
             // stores have completed (vmcnt 0) before the arrival is counted.
-            partial_publish<C::FN, C::FM>(acc, p.partials + ((size_t)t * p.splits + part) * (BM * BN),
-                                          C::THREADS, tid,
+            float* parts = p.partials + (size_t)t * p.splits * (BM * BN);
+            partial_publish<C::FN, C::FM>(acc, parts + (size_t)part * (BM * BN), C::THREADS, tid,
                                           BM * BN * 4);
             wait_vmcnt<0>();
             __syncthreads();
@@ -1038,18 +1072,34 @@ fp8_gemm_kernel(Params p) {
                                                  __HIP_MEMORY_SCOPE_AGENT);
             __syncthreads();
             // Only the last of the tile's units goes on; it adds the partials in
-            // split order (deterministic whatever the arrival order).
+            // split order (deterministic whatever the arrival order), its own
+            // from registers where the partials are large.
             if (arrival != (unsigned)(nparts - 1)) return;
             if (tid == 0)
                 __hip_atomic_store(&p.counters[t], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if constexpr (C::FN * C::FM * (F::NACC / 4) <= 8) {
+                // Small partials: all of them go out in one batch, so reading
+                // this unit's own back costs no extra latency.
 #pragma unroll
-            for (int i = 0; i < C::FN; ++i)
+                for (int i = 0; i < C::FN; ++i)
 #pragma unroll
-                for (int j = 0; j < C::FM; ++j)
+                    for (int j = 0; j < C::FM; ++j) acc[i][j] = typename F::acc_t{};
+                partial_accumulate_all<C::FN, C::FM>(acc, parts, nparts, BM * BN, C::THREADS, tid);
+            } else if (nparts == 2) {
+                // P0 + P1 in place: fp32 addition commutes, so the sum is the
+                // same whichever unit is last.
+                partial_accumulate<C::FN, C::FM>(acc, parts + (size_t)(1 - part) * (BM * BN), C::THREADS,
+                                                 tid, BM * BN * 4);
+            } else {
+                const typename F::acc_t(&own)[C::FN][C::FM] = acc;
+                typename F::acc_t sum[C::FN][C::FM];
+                partial_sum_in_order<C::FN, C::FM>(sum, own, part, parts, nparts, BM * BN, C::THREADS,
+                                                   tid);
 #pragma unroll
-                    for (int v = 0; v < F::NACC; ++v) acc[i][j][v] = 0.f;
-            partial_accumulate_all<C::FN, C::FM>(acc, p.partials + (size_t)t * p.splits * (BM * BN),
-                                                 nparts, BM * BN, C::THREADS, tid);
+                for (int i = 0; i < C::FN; ++i)
+#pragma unroll
+                    for (int j = 0; j < C::FM; ++j) acc[i][j] = sum[i][j];
+            }
         }
 
         // Epilogue parameters into LDS (beside the stage buffers).
