@@ -91,7 +91,9 @@ constexpr int kFormats = 4;
 //     smaller tiles make that fix-up cheaper) or, without a workspace, enough
 //     of them to fill the CUs;
 //   * 128 x 128 on 8 waves (mid-size grids) and on 4 waves with two
-//     workgroups per CU (one's output stores overlap the other's loads).
+//     workgroups per CU (one's output stores overlap the other's loads);
+//   * 64 x 128 on 4 waves, three workgroups per CU: output-write-bound grids
+//     (K of one slice) whose rows are not 16-byte aligned.
 #define FP8MM_GENERIC_CONFIGS(X)                                                   \
     X("bm16_bn32_bk512_w1x2_s6_mfma16", 16, 32, 512, 1, 2, 6, 16, 8)               \
     X("bm16_bn64_bk256_w1x4_s4_mfma16", 16, 64, 256, 1, 4, 4, 16, 8)               \
@@ -102,8 +104,9 @@ constexpr int kFormats = 4;
     X("bm128_bn32_bk256_w4x2_s3_mfma16", 128, 32, 256, 4, 2, 3, 16, 8)             \
     X("bm128_bn64_bk256_w4x2_s3_mfma16", 128, 64, 256, 4, 2, 3, 16, 8)             \
     X("bm128_bn128_bk128_w2x4_s4_mfma32", 128, 128, 128, 2, 4, 4, 32, 8)           \
-    X("bm128_bn128_bk128_w2x2_s2_mfma32", 128, 128, 128, 2, 2, 2, 32, 8)
-constexpr int kNumGenericConfigs = 10;
+    X("bm128_bn128_bk128_w2x2_s2_mfma32", 128, 128, 128, 2, 2, 2, 32, 8)           \
+    X("bm64_bn128_bk128_w2x2_s2_mfma32", 64, 128, 128, 2, 2, 2, 32, 8)
+constexpr int kNumGenericConfigs = 11;
 constexpr int kPingPongId = kNumGenericConfigs;
 constexpr int kNumConfigs = kNumGenericConfigs + 1;
 
@@ -285,10 +288,12 @@ struct Cfg {
     static_assert(CPR == 4 || CPR == 8 || CPR == 16 || CPR == 32, "BK must be 64..512");
     static_assert(A_BYTES % 1024 == 0 && B_BYTES % 1024 == 0, "stages are whole 1 KiB blocks");
     static_assert(LDS_BYTES <= 160 * 1024, "gfx950 LDS is 160 KiB per workgroup");
-    // Workgroups per CU the persistent grid is sized for: two where two fit
-    // in the 160 KiB of LDS (small-K tiles: one workgroup's output stores then
-    // overlap the other's loads), else one.
-    static constexpr int OCCUPANCY = LDS_BYTES * 2 <= 160 * 1024 ? 2 : 1;
+    // Workgroups per CU the persistent grid is sized for: as many as fit in
+    // the 160 KiB of LDS, up to three (small tiles: one workgroup's output
+    // stores then overlap another's loads).
+    static constexpr int OCCUPANCY = LDS_BYTES * 3 <= 160 * 1024   ? 3
+                                     : LDS_BYTES * 2 <= 160 * 1024 ? 2
+                                                                   : 1;
     static_assert(STAGES >= 2, "at least double buffering");
     static_assert(BN % 8 == 0 && BM * (BN * 2 + 16) <= MAIN_BYTES,
                   "the output tile (with its padded rows) fits the stage buffers");

@@ -80,11 +80,22 @@ constexpr int kNarrow128x64 = 7;      // "bm128_bn64_bk256_w4x2_s3_mfma16"
 constexpr int kMidConfig = 8;         // "bm128_bn128_bk128_w2x4_s4_mfma32"
 constexpr int kSkinny128x128 = kMidConfig;
 constexpr int kTwoPerCuConfig = 9;    // "bm128_bn128_bk128_w2x2_s2_mfma32", two workgroups per CU
+constexpr int kThreePerCuConfig = 10; // "bm64_bn128_bk128_w2x2_s2_mfma32", three workgroups per CU
 constexpr int kPingPongConfig = kPingPongId;   // "pp_bm256_bn256_bk128_w8_mfma16"
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 int choose_splits(int cfg, int64_t M, int64_t N, int64_t K);
+
+// A grid of at least 384 tiles of 128 x 128 whose K is one slice (the output
+// write is the bound) and whose rows are not 16-byte aligned (N % 8 != 0):
+// 64 x 128 tiles three per CU keep more output stores overlapping other
+// workgroups' loads (MI355X: 4095 x 4097 x 96 18.3 us against 20.2 us with
+// 128 x 128 tiles two per CU; 16.9 against 18.4 us back to back).  With
+// aligned rows the 256 x 256 or two-per-CU tiles are faster.
+bool write_bound_unaligned(int64_t M, int64_t N, int64_t K) {
+    return N % 8 != 0 && K <= 128 && cdiv(M, 128) * cdiv(N, 128) >= 384;
+}
 
 // The tile configuration for a call that may split K.
 int choose_config_split(int64_t M, int64_t N, int64_t K) {
@@ -124,6 +135,7 @@ int choose_config_split(int64_t M, int64_t N, int64_t K) {
     if (pp_ok && big_tiles >= 192) return kPingPongConfig;
     if (pp_ok && big_tiles >= 96 && choose_splits(kPingPongConfig, M, N, K) > 1)
         return kPingPongConfig;
+    if (write_bound_unaligned(M, N, K)) return kThreePerCuConfig;
     if (tiles128 >= 384) return kTwoPerCuConfig;
     if (pp_ok && big_tiles >= 96) return kPingPongConfig;
     // Fewer tiles with a long K: two workgroups per CU, split over K until
@@ -142,7 +154,6 @@ int choose_config_split(int64_t M, int64_t N, int64_t K) {
 // tiles 18 us; 512 x 3072 x 12288: 128 x 64 tiles 44 us against 76 us with
 // 128 x 128 two per CU.
 int choose_config_nosplit(int64_t M, int64_t N, int64_t K) {
-    (void)K;
     auto tiles = [&](int cfg) { return cdiv(M, kConfigs[cfg].bm) * cdiv(N, kConfigs[cfg].bn); };
     if (M <= 128) {
         const int order[] = {kNarrow128x32, kNarrow64x32, kSkinny16x64, kNarrow16x32};
@@ -152,6 +163,7 @@ int choose_config_nosplit(int64_t M, int64_t N, int64_t K) {
         return kNarrow16x32;
     }
     const int64_t tiles128 = cdiv(M, 128) * cdiv(N, 128);
+    if (write_bound_unaligned(M, N, K)) return kThreePerCuConfig;
     if (tiles128 >= 384) return kTwoPerCuConfig;
     if (tiles128 >= 160) return kMidConfig;
     return tiles(kNarrow128x64) > tiles128 ? kNarrow128x64 : kMidConfig;
