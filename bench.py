@@ -643,6 +643,7 @@ def main():
                    "tile_config": binding.config_names()[binding.select_config(8192, 8192, 8192, 0)],
                    "frac_of_peak": round(value / PEAK_FP8_TFLOPS, 4),
                    "settle_ms_before_warmup": round(settle_ms, 1),
+                   "settle_steps_before_warmup": settle_steps,
                    "kernel_us": {k: quantiles(v) for k, v in per_kernel.items()},
                    "inputs_sha256": {p.name: p.inp.sha256() for p in probs}},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP8_TFLOPS,
