@@ -506,20 +506,17 @@ __device__ __forceinline__ void acc_add(A (&acc)[FN][FM], const A (&x)[FN][FM]) 
 }
 
 // acc += the partial tiles 0 .. splits-1 of one tile (stored one after the
-// other, tile_floats apart, each in the layout above), added in split order.
-// With few chunks per partial (small tiles) the loads of several partials go
-// out together, up to 16 chunks per batch: the sum is the same, and the
-// fix-up costs one memory latency per batch instead of one per partial.
+// other, tile_floats apart, each in the layout above), added in split order,
+// for partials of at most 8 chunks per thread (small tiles): the loads of
+// several partials go out together, up to 16 chunks per batch, so the fix-up
+// costs one memory latency per batch instead of one per partial.
 template <int FN, int FM, class A>
 __device__ __forceinline__ void partial_accumulate_all(A (&acc)[FN][FM], const float* tile_parts,
                                                        int splits, int tile_floats, int stride,
                                                        int idx) {
     constexpr int NC = FN * FM * (int)(sizeof(A) / 16);
-    if constexpr (NC > 8) {
-        for (int q = 0; q < splits; ++q)
-            partial_accumulate<FN, FM>(acc, tile_parts + (size_t)q * tile_floats, stride, idx,
-                                       (uint32_t)tile_floats * 4);
-    } else {
+    static_assert(NC <= 8, "several partials per batch");
+    {
         constexpr int QB = 16 / NC;    // partials per batch
         const __amdgpu_buffer_rsrc_t r =
             make_rsrc(tile_parts, (uint32_t)splits * (uint32_t)tile_floats * 4);
