@@ -192,8 +192,9 @@ def scaled_mm(a, b, scale_a, scale_b, bias=None, mode=PER_TENSOR, rows=None, col
     With an e5m2 operand that argument fails (e5m2 spans 2^-16 .. 57344, so a
     sum can need more than 53 bits); acc is then the exact integer sum of
     `_exact_integer_acc` rounded once to fp64 (relative error <= 2^-53), for
-    finite codes and K <= 32768, and mag is the fp64 matrix product of the
-    magnitudes (a tolerance term, relative error below K * 2^-53).
+    K <= 32768, and mag is the fp64 matrix product of the magnitudes (a
+    tolerance term, relative error below K * 2^-53).  Non-finite codes are
+    taken out of both sums and decide acc by the IEEE 754 rules below.
     """
     a = np.asarray(a, dtype=np.uint8)
     b = np.asarray(b, dtype=np.uint8)
@@ -208,21 +209,37 @@ def scaled_mm(a, b, scale_a, scale_b, bias=None, mode=PER_TENSOR, rows=None, col
 
     da = decode(a[rows], a_format)           # [m, K]
     db = decode(b[cols], b_format)           # [n, K]
-    # NaN codes (e4m3fn 0x7F / 0xFF) follow IEEE 754 arithmetic, written out
-    # here rather than left to the matrix-product library: a NaN operand makes
-    # its product NaN whatever the other factor (0 included), and a NaN term
-    # makes the sum NaN, so acc[m, n] is NaN exactly when row m of A or row n
-    # of B holds a NaN code.  The sums themselves are formed over the other
-    # values with the NaNs replaced by 0.
-    if (a_format != E4M3FN or b_format != E4M3FN) and not (
-            np.all(np.isfinite(da)) and np.all(np.isfinite(db))):
-        raise ValueError("e5m2 operands must be finite (no inf or NaN codes)")
-    nan_rows = np.isnan(da).any(axis=1)
-    nan_cols = np.isnan(db).any(axis=1)
-    if nan_rows.any() or nan_cols.any():
-        da = np.where(np.isnan(da), 0.0, da)
-        db = np.where(np.isnan(db), 0.0, db)
-    nan_mask = nan_rows[:, None] | nan_cols[None, :]
+    # Non-finite codes (NaN in both formats: e4m3fn 0x7F / 0xFF, e5m2
+    # 0x7D..0x7F / 0xFD..0xFF; +-infinity in e5m2 only: 0x7C / 0xFC) follow
+    # IEEE 754 arithmetic, written out here rather than left to the
+    # matrix-product library:
+    #   a product is NaN if a factor is NaN, or one factor is infinite and the
+    #   other zero; it is infinite, with the sign of the factors' signs'
+    #   product, if a factor is infinite and the other non-zero;
+    #   a sum is NaN if a term is NaN or it has both a +inf and a -inf term,
+    #   else +-inf if it has an infinite term, else the finite sum.
+    # Which of these holds for (m, n) is an "any over k" of elementwise
+    # conditions on row m of A and row n of B; the finite sums are formed over
+    # the other values, with every non-finite value replaced by 0.
+    fa, fb = np.isfinite(da), np.isfinite(db)
+    special = not (fa.all() and fb.all())
+    if special:
+        def any_k(x, y):   # [m, n]: some k with x[m, k] and y[n, k]
+            return (x.astype(np.int64) @ y.astype(np.int64).T) > 0
+        nan_a, nan_b = np.isnan(da), np.isnan(db)
+        inf_a, inf_b = np.isinf(da), np.isinf(db)
+        zero_a, zero_b = da == 0, db == 0
+        pos_a, pos_b = ~nan_a & (da > 0), ~nan_b & (db > 0)
+        neg_a, neg_b = ~nan_a & (da < 0), ~nan_b & (db < 0)
+        nan_mask = (nan_a.any(axis=1)[:, None] | nan_b.any(axis=1)[None, :]
+                    | any_k(inf_a, zero_b) | any_k(zero_a, inf_b))
+        pinf = (any_k(inf_a & pos_a, pos_b) | any_k(inf_a & neg_a, neg_b)
+                | any_k(pos_a, inf_b & pos_b) | any_k(neg_a, inf_b & neg_b))
+        ninf = (any_k(inf_a & pos_a, neg_b) | any_k(inf_a & neg_a, pos_b)
+                | any_k(pos_a, inf_b & neg_b) | any_k(neg_a, inf_b & pos_b))
+        nan_mask |= pinf & ninf
+        da = np.where(fa, da, 0.0)
+        db = np.where(fb, db, 0.0)
     if a_format == E4M3FN and b_format == E4M3FN:
         acc = da @ db.T
     else:
@@ -230,7 +247,9 @@ def scaled_mm(a, b, scale_a, scale_b, bias=None, mode=PER_TENSOR, rows=None, col
             raise ValueError("the integer accumulation is only argued for K <= 32768")
         acc = _exact_integer_acc(da, db, UNIT_EXP[a_format], UNIT_EXP[b_format])
     mag = np.abs(da) @ np.abs(db).T
-    if nan_mask.any():
+    if special:
+        acc = np.where(pinf, np.inf, acc)
+        acc = np.where(ninf, -np.inf, acc)
         acc = np.where(nan_mask, np.nan, acc)
 
     sa = np.asarray(scale_a, dtype=np.float32).astype(np.float64).reshape(-1)
@@ -247,7 +266,8 @@ def scaled_mm(a, b, scale_a, scale_b, bias=None, mode=PER_TENSOR, rows=None, col
     else:
         raise ValueError(f"unknown scaling mode {mode}")
 
-    y = s * acc
-    if bias is not None:
-        y = y + bf16_bits_to_f64(np.asarray(bias, dtype=np.uint16)[cols])[None, :]
+    with np.errstate(invalid="ignore"):      # 0 * inf and inf - inf are NaN, as IEEE 754 has them
+        y = s * acc
+        if bias is not None:
+            y = y + bf16_bits_to_f64(np.asarray(bias, dtype=np.uint16)[cols])[None, :]
     return {"bits": f64_to_bf16_rne(y), "y": y, "acc": acc, "mag": mag, "s": s}

@@ -5,7 +5,8 @@
 evaluated in fp64.  ulp_bf16(x) for x > 0 is 2^(max(floor(log2 x), -126) - 7)
 (the spacing of bf16 numbers at x; subnormal spacing below 2^-126) and
 2^-133 at x = 0.  A NaN reference requires a NaN result, and a NaN result
-requires a NaN reference.
+requires a NaN reference; an infinite reference requires the same infinity,
+and an infinite result the same infinite reference.
 """
 import numpy as np
 
@@ -30,9 +31,10 @@ def compare(gpu_bits, ref):
     r = bf16_bits_to_f64(ref["bits"])
     tol = 2.0 * ulp_bf16(r) + 1e-3 * ref["s"] * ref["mag"]
     rn, gn = np.isnan(r), np.isnan(g)
+    ri, gi = np.isinf(r), np.isinf(g)
     with np.errstate(invalid="ignore"):
         err = np.abs(g - r)
-        bad = np.where(rn | gn, rn != gn, err > tol)
-        ratio = np.where(rn | gn, 0.0, err / tol)
+        bad = np.where(rn | gn, rn != gn, np.where(ri | gi, r != g, err > tol))
+        ratio = np.where(rn | gn | ri | gi, 0.0, err / tol)
     idx = np.argwhere(bad)
     return int(bad.sum()), float(np.max(ratio)) if ratio.size else 0.0, (tuple(idx[0]) if len(idx) else None)

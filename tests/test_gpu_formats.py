@@ -8,7 +8,8 @@ import oracle
 from precision_linear_amd import binding
 from precision_linear_amd import workloads as wl
 from parity import compare
-from test_gpu_parity import OFMT, _config_ids, _configs, _to_dev, out_bits, ref_mm, run_gpu
+from test_gpu_parity import (OFMT, _cfg, _config_ids, _configs, _to_dev, out_bits, ref_mm, run_gpu,
+                             run_gpu_plan)
 
 pytestmark = pytest.mark.gpu
 PT, RW = wl.PER_TENSOR, wl.ROWWISE
@@ -122,3 +123,39 @@ def test_torch_float8_dtypes_carry_the_format():
     assert nbad == 0, (nbad, worst, first)
     with pytest.raises(ValueError):
         binding.fp8_scaled_mm(a, b, _to_dev(inp.scale_a), _to_dev(inp.scale_b), a_format="e4m3fn")
+
+
+# e5m2 infinities and NaNs in the operands (+inf 0x7C, -inf 0xFC, NaN 0x7E,
+# 0x7F): the oracle applies IEEE 754 (inf * 0 = NaN, inf - inf = NaN, a lone
+# infinity keeps its sign); the comparison demands the same NaN positions and
+# the same infinities.  A row of A with one +inf (its outputs are +-inf, or
+# NaN where B has a zero at that k), a row with +inf and -inf (NaN), a NaN
+# row; in B a -inf column and a NaN column.  The "codes" recipe draws 1% zero
+# codes, so inf * 0 occurs too.  Plans: the main tile families and split-K.
+NONFINITE_PLANS = [("bm16_bn64_bk256_w1x4_s4_mfma16", 1), ("bm128_bn128_bk128_w2x4_s4_mfma32", 1),
+                   ("bm128_bn128_bk128_w2x2_s2_mfma32", 1), ("bm64_bn128_bk128_w2x2_s2_mfma32", 1),
+                   ("pp_bm256_bn256_bk128_w8_mfma16", 1), ("bm128_bn128_bk128_w2x4_s4_mfma32", 3),
+                   ("pp_bm256_bn256_bk128_w8_mfma16", 2)]
+
+
+@pytest.mark.parametrize("pair", PAIRS, ids=PAIR_IDS)
+@pytest.mark.parametrize("config,splits", NONFINITE_PLANS)
+def test_nonfinite_e5m2_codes_follow_ieee(pair, config, splits):
+    fa, fb = pair
+    inp = _inputs(300, 520, 1024, RW, fa, fb, bias=True, key=splits * 7 + len(config))
+    a, b = inp.a.copy(), inp.b.copy()
+    if fa == "e5m2":
+        a[5, 17] = 0x7C
+        a[40, 3], a[40, 9] = 0x7C, 0xFC
+        a[77, 100] = 0x7E
+    if fb == "e5m2":
+        b[33, 0] = 0xFC
+        b[200, 5] = 0x7F
+    inp = wl.Inputs(a, b, inp.scale_a, inp.scale_b, inp.bias, RW, fa, fb)
+    print(f"[formats] non-finite {fa}x{fb} config={config} splits={splits}", flush=True)
+    got = out_bits(run_gpu_plan(inp, _cfg(config), splits))
+    ref = ref_mm(inp)
+    nbad, worst, first = compare(got, ref)
+    assert nbad == 0, (nbad, worst, first)
+    r = ref["bits"]
+    assert (r == 0x7FC0).any() and ((r & 0x7FFF) == 0x7F80).any()    # both kinds occur

@@ -306,10 +306,109 @@ def test_extreme_span_at_largest_k():
     assert r2["acc"][0, 0] == 2.0 ** -32
 
 
-def test_nonfinite_e5m2_inputs_rejected():
-    a = np.array([[0x7C] + [0] * 15], np.uint8)
-    with pytest.raises(ValueError):
-        oracle.scaled_mm(a, a.copy(), np.ones(1, np.float32), np.ones(1, np.float32), a_format=E5, b_format=E5)
+# Non-finite e5m2 codes: +inf 0x7C, -inf 0xFC, NaN 0x7D..0x7F and 0xFD..0xFF.
+# Each case is one row of A against one row of B (K = 16, the rest zeros),
+# with the IEEE 754 result written out by hand: inf times zero is NaN, a NaN
+# factor or term gives NaN, +inf and -inf terms together give NaN, and a lone
+# infinity keeps the sign of its factors' signs' product.
+INF, NINF, NAN, ONE, TWO, MONE, MTWO, ZERO, MZERO = 0x7C, 0xFC, 0x7D, 0x3C, 0x40, 0xBC, 0xC0, 0x00, 0x80
+NONFINITE_CASES = [
+    ([INF, ONE], [ONE, ONE], 0x7F80),        # inf + 1 = inf
+    ([INF, ONE], [MONE, ONE], 0xFF80),       # -inf + 1 = -inf
+    ([NINF], [MTWO], 0x7F80),                # (-inf)(-2) = inf
+    ([INF, INF], [ONE, TWO], 0x7F80),        # inf + inf = inf
+    ([INF, ONE], [ZERO, ONE], None),         # inf * 0 = NaN
+    ([INF, ONE], [MZERO, ONE], None),        # inf * -0 = NaN
+    ([ZERO, TWO], [NINF, ONE], None),        # 0 * -inf = NaN
+    ([INF, NINF], [ONE, ONE], None),         # inf - inf = NaN
+    ([INF, ONE], [ONE, NINF], None),         # inf + (-inf) = NaN
+    ([0x7F, ONE], [ZERO, ONE], None),        # NaN * 0 = NaN
+    ([ONE, ONE], [0xFE, ONE], None),         # NaN term
+    ([ONE, TWO], [ONE, ONE], 0x4040),        # finite: 1 + 2 = 3 (bf16 0x4040)
+]
+
+
+@pytest.mark.parametrize("ca,cb,want", NONFINITE_CASES)
+def test_nonfinite_e5m2_follow_ieee(ca, cb, want):
+    a = np.zeros((1, 16), np.uint8)
+    b = np.zeros((1, 16), np.uint8)
+    a[0, :len(ca)] = ca
+    b[0, :len(cb)] = cb
+    r = oracle.scaled_mm(a, b, np.ones(1, np.float32), np.ones(1, np.float32), a_format=E5, b_format=E5)
+    got = int(r["bits"][0, 0])
+    if want is None:
+        assert np.isnan(r["acc"][0, 0]) and got == 0x7FC0
+    else:
+        assert got == want, hex(got)
+
+
+@pytest.mark.parametrize("cb,want", [([0x38, 0x38], 0x7F80),     # e4m3fn 1, 1: inf + 1
+                                     ([0x00, 0x38], None),       # e4m3fn 0: inf * 0
+                                     ([0xB8, 0x38], 0xFF80),     # e4m3fn -1: -inf + 1
+                                     ([0x7F, 0x38], None)])      # e4m3fn NaN
+def test_nonfinite_e5m2_times_e4m3fn(cb, want):
+    a = np.array([[INF, ONE] + [0] * 14], np.uint8)
+    b = np.array([cb + [0] * 14], np.uint8)
+    r = oracle.scaled_mm(a, b, np.ones(1, np.float32), np.ones(1, np.float32), a_format=E5, b_format=E4)
+    got = int(r["bits"][0, 0])
+    if want is None:
+        assert got == 0x7FC0
+    else:
+        assert got == want, hex(got)
+
+
+def test_nonfinite_e5m2_scale_zero_and_bias():
+    # 0 * inf = NaN after the scale; inf + bias = inf
+    a = np.array([[INF] + [0] * 15], np.uint8)
+    b = np.array([[ONE] + [0] * 15], np.uint8)
+    r0 = oracle.scaled_mm(a, b, np.zeros(1, np.float32), np.ones(1, np.float32), a_format=E5, b_format=E5)
+    assert r0["bits"][0, 0] == 0x7FC0
+    bias = np.array([0xC2C8], np.uint16)            # bf16 -100
+    r1 = oracle.scaled_mm(a, b, np.full(1, 0.5, np.float32), np.ones(1, np.float32), bias,
+                          a_format=E5, b_format=E5)
+    assert r1["bits"][0, 0] == 0x7F80
+
+
+def _binary16_value(code):
+    """An e5m2 code is the top byte of an IEEE binary16 pattern."""
+    return float(np.array([int(code) << 8], np.uint16).view(np.float16)[0])
+
+
+def test_nonfinite_e5m2_against_python_floats():
+    """Random small matrices with sparse inf / NaN codes and zeros: the
+    oracle's acc against a plain Python loop in IEEE doubles over values
+    decoded as binary16 (infinities and NaNs propagate by the hardware's own
+    IEEE rules there).  Non-finite results must agree exactly (NaN, or the
+    same infinity); finite ones equal the exact sum of the products
+    (fractions.Fraction) rounded once to double."""
+    rng = np.random.default_rng(17)
+    M, N, K = 9, 7, 32
+    pool = np.array([c for c in range(256) if (c & 0x7F) < 0x7C], np.uint8)     # finite codes
+
+    def draw(rows):
+        x = pool[rng.integers(0, pool.size, (rows, K))]
+        x[rng.random((rows, K)) < 0.15] = 0
+        special = rng.random((rows, K)) < 0.05
+        x[special] = rng.choice(np.array([0x7C, 0xFC, 0x7D, 0xFF], np.uint8), special.sum())
+        return x
+
+    for trial in range(6):
+        a, b = draw(M), draw(N)
+        r = oracle.scaled_mm(a, b, np.ones(1, np.float32), np.ones(1, np.float32), a_format=E5, b_format=E5)
+        for m in range(M):
+            for n in range(N):
+                acc = 0.0
+                for k in range(K):
+                    acc += _binary16_value(a[m, k]) * _binary16_value(b[n, k])
+                got = r["acc"][m, n]
+                if np.isnan(acc):
+                    assert np.isnan(got), (trial, m, n)
+                elif np.isinf(acc):
+                    assert got == acc, (trial, m, n, got, acc)
+                else:
+                    exact = sum(Fraction(_binary16_value(a[m, k])) * Fraction(_binary16_value(b[n, k]))
+                                for k in range(K))
+                    assert got == float(exact), (trial, m, n)
 
 
 # ---------------------------------------------------------------- invariants ---
