@@ -7,6 +7,7 @@ fallback path).
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 
@@ -165,16 +166,19 @@ _TORCH_FORMATS = {torch.float8_e4m3fn: E4M3FN, torch.float8_e5m2: E5M2}
 def _as_codes(t: torch.Tensor, name: str, fmt) -> tuple:
     """(uint8 view, format id).  A float8 tensor carries its format; uint8
     codes take `fmt` (default e4m3fn)."""
+    dt = t.dtype
+    if fmt is None and dt == torch.uint8:
+        return t, E4M3FN
     if fmt is not None and fmt not in _FORMATS:
         raise ValueError(f"{name}_format must be 'e4m3fn' or 'e5m2', got {fmt!r}")
-    if t.dtype in _TORCH_FORMATS:
-        f = _TORCH_FORMATS[t.dtype]
+    if dt in _TORCH_FORMATS:
+        f = _TORCH_FORMATS[dt]
         if fmt is not None and _FORMATS[fmt] != f:
-            raise ValueError(f"{name} is {t.dtype} but {name}_format={fmt!r}")
+            raise ValueError(f"{name} is {dt} but {name}_format={fmt!r}")
         return t.view(torch.uint8), f
-    if t.dtype == torch.uint8:
-        return t, E4M3FN if fmt is None else _FORMATS[fmt]
-    raise ValueError(f"{name} must be float8_e4m3fn, float8_e5m2 or uint8 codes, got {t.dtype}")
+    if dt == torch.uint8:
+        return t, _FORMATS[fmt]
+    raise ValueError(f"{name} must be float8_e4m3fn, float8_e5m2 or uint8 codes, got {dt}")
 
 
 def _same_device(ref: torch.Tensor, **tensors) -> None:
@@ -183,6 +187,11 @@ def _same_device(ref: torch.Tensor, **tensors) -> None:
     for name, t in tensors.items():
         if t is not None and t.device != ref.device:
             raise ValueError(f"{name} is on {t.device}, expected {ref.device}")
+
+
+# Workspace bytes of automatic plans, per (device, M, N, K, mode, bias, config,
+# splits): the plan depends on nothing else, so the size is asked once.
+_ws_sizes: dict = {}
 
 
 def fp8_scaled_mm(a: torch.Tensor, b: torch.Tensor, scale_a: torch.Tensor, scale_b: torch.Tensor,
@@ -199,9 +208,9 @@ def fp8_scaled_mm(a: torch.Tensor, b: torch.Tensor, scale_a: torch.Tensor, scale
     splits K, its workspace is
     `workspace` (a GPU byte tensor, zero-filled before first use) or, if that
     is None, one this module keeps per stream (allocated by torch)."""
-    if mode not in _MODES:
+    m = _MODES.get(mode) if isinstance(mode, (str, int)) else None
+    if m is None:
         raise ValueError(f"mode must be 'per_tensor' or 'rowwise', got {mode!r}")
-    m = _MODES[mode]
     a, fa = _as_codes(a, "a", a_format)
     b, fb = _as_codes(b, "b", b_format)
     if a.dim() != 2 or b.dim() != 2:
@@ -228,27 +237,37 @@ def fp8_scaled_mm(a: torch.Tensor, b: torch.Tensor, scale_a: torch.Tensor, scale
         raise ValueError(f"{'per-tensor' if m == PER_TENSOR else 'row-wise'} scales need "
                          f"{want_a} and {want_b} elements, got {scale_a.numel()} and {scale_b.numel()}")
     if bias is not None:
-        if bias.dtype != torch.bfloat16 or bias.numel() != N or not bias.is_contiguous() or not bias.is_cuda:
+        if bias.dtype != torch.bfloat16 or bias.numel() != N or not bias.is_contiguous():
             raise ValueError("bias must be a contiguous bf16 GPU vector of length N")
+    dev = a.get_device()
     if out is None:
         out = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
-    elif out.dtype != torch.bfloat16 or tuple(out.shape) != (M, N) or not out.is_contiguous():
+    elif out.dtype != torch.bfloat16 or out.shape != (M, N) or not out.is_contiguous():
         raise ValueError("out must be a contiguous bf16 M x N tensor")
-    stream = torch.cuda.current_stream(a.device).cuda_stream
-    ws_ptr, ws_bytes = None, 0
-    if workspace is not None:
-        if not workspace.is_cuda or not workspace.is_contiguous():
-            raise ValueError("workspace must be a contiguous GPU tensor")
-        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
-    elif splits != 1:
-        need = int(lib().fp8_scaled_mm_workspace_size(M, N, K, m, int(bias is not None),
-                                                      int(config), int(splits)))
-        if need > 0:
-            with torch.cuda.device(a.device):
+    L = lib()
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    # The library launches on the current HIP device: make it a's (calls
+    # from that device, the usual case, skip the switch).
+    switch = torch.cuda.current_device() != dev
+    with torch.cuda.device(dev) if switch else contextlib.nullcontext():
+        ws_ptr, ws_bytes = None, 0
+        if workspace is not None:
+            if not workspace.is_contiguous():
+                raise ValueError("workspace must be a contiguous GPU tensor")
+            ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+        elif splits != 1:
+            key = (dev, M, N, K, m, bias is not None, config, splits)
+            need = _ws_sizes.get(key)
+            if need is None:
+                need = int(L.fp8_scaled_mm_workspace_size(M, N, K, m, int(bias is not None),
+                                                          int(config), int(splits)))
+                if len(_ws_sizes) >= 4096:      # many distinct shapes: start over
+                    _ws_sizes.clear()
+                _ws_sizes[key] = need
+            if need > 0:
                 ws = _workspace(a.device, stream, need)
-            ws_ptr, ws_bytes = ws.data_ptr(), ws.numel()
-    with torch.cuda.device(a.device):
-        st = lib().fp8_scaled_mm_typed(
+                ws_ptr, ws_bytes = ws.data_ptr(), ws.numel()
+        st = L.fp8_scaled_mm_typed(
             a.data_ptr(), fa, b.data_ptr(), fb, scale_a.data_ptr(), scale_b.data_ptr(),
             bias.data_ptr() if bias is not None else None, out.data_ptr(),
             M, N, K, m, stream, int(config), int(splits), ws_ptr, ws_bytes)
