@@ -37,6 +37,7 @@
 
 #include "../../include/fp8_scaled_mm.h"
 #include "fp8_gemm_kernels.h"
+#include "plan_cost_table.h"
 
 namespace {
 
@@ -85,7 +86,7 @@ constexpr int kPingPongConfig = kPingPongId;   // "pp_bm256_bn256_bk128_w8_mfma1
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-int choose_splits(int cfg, int64_t M, int64_t N, int64_t K);
+int fixed_rule_splits(int cfg, int64_t M, int64_t N, int64_t K);
 
 // A grid of at least 384 tiles of 128 x 128 whose K is one slice (the output
 // write is the bound) and whose rows are not 16-byte aligned (N % 8 != 0):
@@ -102,7 +103,7 @@ int choose_config_split(int64_t M, int64_t N, int64_t K) {
     // Skinny problems (M <= 128) are HBM-bound on B: tiles as tall as M and
     // 112 columns wide when that gives about one tile per CU (N = 28672 is
     // 256 x 112), else narrower tiles whose K reduction is split until the
-    // work units fill the CUs (choose_splits).  Chosen from measurements on
+    // work units fill the CUs (fixed_rule_splits).  Chosen from measurements on
     // MI355X of the six skinny inference shapes.
     // Few columns as well (under 2048, or under 8192 for 128 rows: the
     // column shards of those shapes over 8 GPUs) take narrower tiles, split
@@ -133,7 +134,7 @@ int choose_config_split(int64_t M, int64_t N, int64_t K) {
     const int64_t tiles128 = cdiv(M, 128) * cdiv(N, 128);
     const bool pp_ok = N % 8 == 0;
     if (pp_ok && big_tiles >= 192) return kPingPongConfig;
-    if (pp_ok && big_tiles >= 96 && choose_splits(kPingPongConfig, M, N, K) > 1)
+    if (pp_ok && big_tiles >= 96 && fixed_rule_splits(kPingPongConfig, M, N, K) > 1)
         return kPingPongConfig;
     if (write_bound_unaligned(M, N, K)) return kThreePerCuConfig;
     if (tiles128 >= 384) return kTwoPerCuConfig;
@@ -169,14 +170,125 @@ int choose_config_nosplit(int64_t M, int64_t N, int64_t K) {
     return tiles(kNarrow128x64) > tiles128 ? kNarrow128x64 : kMidConfig;
 }
 
+// ---------------------------------------------------------- plan model ---
+//
+// Grids that the 256 x 256 tiles fill (at least 192 of them, N % 8 == 0) or
+// that have more than 1536 tiles of 128 x 128 take the fixed rules above.
+// So do grids whose K is one slice and whose rows are not 16-byte aligned
+// (write_bound_unaligned: the measurements behind the model have aligned
+// rows).  Every other grid takes the plan -- tile configuration and split
+// count -- of least predicted time under a cost model fitted to
+// measurements on MI355X of every plan on a few hundred shapes (M from 16 to
+// 8192, N from 256 to 28672, K from 128 to 28672; plan_sweep.py,
+// plan_fit.py): a linear function, per configuration, of the features below.  Two coefficient
+// tables: M <= 128 (fitted on launches whose operands come from HBM, as a
+// decode step's weights do) and M > 128 (operands left in the caches).  On
+// held-out shapes the chosen plan ran within 2% of the fastest measured one
+// (geometric mean), where the fixed rules alone were 17% off.
+bool plan_modelled(int64_t M, int64_t N, int64_t K) {
+    const bool pp_fills = N % 8 == 0 && cdiv(M, 256) * cdiv(N, 256) >= 192;
+    return !pp_fills && cdiv(M, 128) * cdiv(N, 128) <= 1536 && !write_bound_unaligned(M, N, K);
+}
+
+// The split count a plan with `s` requested runs: at most the K slices, then
+// the smallest count with the same slices per unit (as plan_splits).
+int64_t normalised_splits(int64_t s, int64_t k_iters) {
+    if (s > k_iters) s = k_iters;
+    return s > 1 ? cdiv(k_iters, cdiv(k_iters, s)) : 1;
+}
+
+// Predicted time (us) of configuration cfg with s splits: T tiles, U = T * s
+// units, S = 256 * occupancy workgroup slots, R = ceil(U / S) rounds of
+// units per slot, Lc = ceil(U / 256) units per CU, kk K slices per unit, act
+// = min(U, S) / S the busy fraction of the slots, a = BM * BN / 16384.
+double plan_cost(const PlanCostRow& row, const ConfigInfo& c, int64_t M, int64_t N, int64_t K,
+                 int64_t s) {
+    const int64_t S = 256 * (int64_t)c.occupancy;
+    const int64_t T = cdiv(M, c.bm) * cdiv(N, c.bn);
+    const int64_t U = T * s;
+    const int64_t R = cdiv(U, S);
+    const int64_t kk = cdiv(cdiv(K, c.bk), s);
+    const double act = (double)(U < S ? U : S) / (double)S;
+    const int64_t Lc = cdiv(U, 256);
+    const double sp = s > 1 ? 1.0 : 0.0;
+    const double a = (double)(c.bm * c.bn) / 16384.0;
+    const double f[kPlanFeatures] = {
+        1.0, (double)(R * kk), (double)(R * kk) * act, (double)R, sp, sp * (double)s * a,
+        sp * (double)R * a, sp * (double)T * (double)s * (double)c.bm * (double)c.bn / 1e6,
+        (double)((M + N) * K) / 1e6, sp * (double)s * (double)R * a, (double)(Lc * kk), (double)Lc,
+        (double)(Lc * kk) * act};
+    double t = 0.0;
+    for (int i = 0; i < kPlanFeatures; ++i) t += row.c[i] * f[i];
+    return t;
+}
+
+struct Plan {
+    int cfg;       // -1: no configuration is modelled here
+    int splits;
+};
+
+constexpr int kSplitCandidates[] = {2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15, 16, 24, 32};
+
+// The modelled plan of least predicted time, over every configuration or
+// only `only_cfg` (>= 0).  Candidates: configurations fitted for this M, the
+// ping-pong kernel only with N % 8 == 0, tile grids of at most 6 rounds of
+// slots; split counts (with can_split) leaving at least 2 K slices per unit
+// and at most 3 rounds of units, the ping-pong kernel at most 3 ways and
+// only into units of at least 40 slices.  Ties keep the earlier candidate.
+Plan model_plan(int64_t M, int64_t N, int64_t K, bool can_split, int only_cfg) {
+    const PlanCostRow* table = M <= 128 ? kPlanCost_streamed : kPlanCost_resident;
+    Plan best{-1, 1};
+    double best_t = 0.0;
+    auto consider = [&](int cfg, int64_t s) {
+        const double t = plan_cost(table[cfg], kConfigs[cfg], M, N, K, s);
+        if (best.cfg < 0 || t < best_t) {
+            best = Plan{cfg, (int)s};
+            best_t = t;
+        }
+    };
+    for (int cfg = 0; cfg < kNumConfigs; ++cfg) {
+        if (only_cfg >= 0 && cfg != only_cfg) continue;
+        const ConfigInfo& c = kConfigs[cfg];
+        if (!table[cfg].usable) continue;
+        const bool pp = cfg == kPingPongConfig;
+        if (pp && N % 8 != 0) continue;
+        const int64_t S = 256 * (int64_t)c.occupancy;
+        const int64_t T = cdiv(M, c.bm) * cdiv(N, c.bn);
+        if (T > 6 * S) continue;
+        consider(cfg, 1);
+        if (!can_split || !c.split_ok || !table[cfg].split_usable) continue;
+        const int64_t k_iters = cdiv(K, c.bk);
+        for (int s : kSplitCandidates) {
+            if (2 * s > k_iters || T * s > 3 * S) continue;
+            if (pp && (s > 3 || k_iters / s < 40)) continue;
+            consider(cfg, normalised_splits(s, k_iters));
+        }
+    }
+    return best;
+}
+
 // The automatic tile configuration.  can_split: the call has a workspace for
 // split-K partials; without one, K is never split, and where the plan with a
 // workspace would split, narrower tiles take its place.
 int choose_config(int64_t M, int64_t N, int64_t K, int mode, int has_bias, bool can_split) {
     (void)mode; (void)has_bias;
+    if (plan_modelled(M, N, K)) {
+        const Plan p = model_plan(M, N, K, can_split, -1);
+        if (p.cfg >= 0) return p.cfg;
+    }
     const int cfg = choose_config_split(M, N, K);
-    if (can_split || choose_splits(cfg, M, N, K) <= 1) return cfg;
+    if (can_split || fixed_rule_splits(cfg, M, N, K) <= 1) return cfg;
     return choose_config_nosplit(M, N, K);
+}
+
+// The automatic split count of a configuration: the modelled plan's for
+// that configuration, else the fixed rule.
+int choose_splits(int cfg, int64_t M, int64_t N, int64_t K) {
+    if (plan_modelled(M, N, K)) {
+        const Plan p = model_plan(M, N, K, true, cfg);
+        if (p.cfg >= 0) return p.splits;
+    }
+    return fixed_rule_splits(cfg, M, N, K);
 }
 
 // Per-device facts, read once per device: the compute-unit count and whether
@@ -215,7 +327,8 @@ int validate(const void* A, const void* B, const float* sa, const float* sb, con
     return FP8MM_OK;
 }
 
-// Split-K factor for a configuration: only when the tile grid leaves most of
+// Split-K factor of the fixed rules (grids the plan model leaves out, see
+// plan_modelled): only when the tile grid leaves most of
 // the workgroup slots (256 CUs times the configuration's workgroups per CU)
 // idle, and never below 8 K slices per split.  The ping-pong
 // kernel's 256 x 256 fp32 partials (256 KiB per unit, written and read back
@@ -223,7 +336,7 @@ int validate(const void* A, const void* B, const float* sa, const float* sb, con
 // at most 3 ways and only into units of at least 40 slices (measured on
 // MI355X: 2304 x 3072 x 12288 goes from 112 to 88 us with 2 units of 48
 // slices, while 8191 x 1000 x 4160 gets slower with 2 units of 17).
-int choose_splits(int cfg, int64_t M, int64_t N, int64_t K) {
+int fixed_rule_splits(int cfg, int64_t M, int64_t N, int64_t K) {
     const ConfigInfo& c = kConfigs[cfg];
     if (!c.split_ok) return 1;
     const int64_t tiles = cdiv(M, c.bm) * cdiv(N, c.bn);
