@@ -267,13 +267,36 @@ Plan model_plan(int64_t M, int64_t N, int64_t K, bool can_split, int only_cfg) {
     return best;
 }
 
+// model_plan's results, per thread and direct-mapped (64 entries): weighing
+// every candidate plan takes a few microseconds of host time, and a caller
+// usually repeats a few shapes (a network's layers), each then planned once.
+// `key` is 1 + 2 * (only_cfg + 1) + can_split, so a zeroed entry matches no
+// query.
+struct PlanMemo {
+    int64_t M, N, K;
+    int key;
+    Plan plan;
+};
+thread_local PlanMemo t_plan_memo[64];
+
+Plan model_plan_memo(int64_t M, int64_t N, int64_t K, bool can_split, int only_cfg) {
+    const int key = 1 + 2 * (only_cfg + 1) + (can_split ? 1 : 0);
+    const uint64_t h = (uint64_t)M * 0x9E3779B97F4A7C15ull ^ (uint64_t)N * 0xC2B2AE3D27D4EB4Full ^
+                       (uint64_t)K * 0x165667B19E3779F9ull ^ (uint64_t)key * 0xD6E8FEB86659FD93ull;
+    PlanMemo& e = t_plan_memo[h >> 58];
+    if (e.key == key && e.M == M && e.N == N && e.K == K) return e.plan;
+    const Plan p = model_plan(M, N, K, can_split, only_cfg);
+    e = PlanMemo{M, N, K, key, p};
+    return p;
+}
+
 // The automatic tile configuration.  can_split: the call has a workspace for
 // split-K partials; without one, K is never split, and where the plan with a
 // workspace would split, narrower tiles take its place.
 int choose_config(int64_t M, int64_t N, int64_t K, int mode, int has_bias, bool can_split) {
     (void)mode; (void)has_bias;
     if (plan_modelled(M, N, K)) {
-        const Plan p = model_plan(M, N, K, can_split, -1);
+        const Plan p = model_plan_memo(M, N, K, can_split, -1);
         if (p.cfg >= 0) return p.cfg;
     }
     const int cfg = choose_config_split(M, N, K);
@@ -285,7 +308,7 @@ int choose_config(int64_t M, int64_t N, int64_t K, int mode, int has_bias, bool 
 // that configuration, else the fixed rule.
 int choose_splits(int cfg, int64_t M, int64_t N, int64_t K) {
     if (plan_modelled(M, N, K)) {
-        const Plan p = model_plan(M, N, K, true, cfg);
+        const Plan p = model_plan_memo(M, N, K, true, cfg);
         if (p.cfg >= 0) return p.splits;
     }
     return fixed_rule_splits(cfg, M, N, K);
