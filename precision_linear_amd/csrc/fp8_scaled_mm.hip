@@ -180,11 +180,12 @@ int choose_config_nosplit(int64_t M, int64_t N, int64_t K) {
 // count -- of least predicted time under a cost model fitted to
 // measurements on MI355X of every plan on a few hundred shapes (M from 16 to
 // 8192, N from 256 to 28672, K from 128 to 28672; plan_sweep.py,
-// plan_fit.py): a linear function, per configuration, of the features below.  Two coefficient
-// tables: M <= 128 (fitted on launches whose operands come from HBM, as a
-// decode step's weights do) and M > 128 (operands left in the caches).  On
-// held-out shapes the chosen plan ran within 2% of the fastest measured one
-// (geometric mean), where the fixed rules alone were 17% off.
+// plan_fit.py): a linear function, per configuration, of the features below.
+// Two coefficient tables: M <= 128 (fitted on launches whose operands come
+// from HBM, as a decode step's weights do) and M > 128 (operands left in the
+// caches).  On held-out shapes the chosen plan ran within 1.4% of the
+// fastest measured one (geometric mean), where the fixed rules alone were
+// 14-17% off.
 bool plan_modelled(int64_t M, int64_t N, int64_t K) {
     const bool pp_fills = N % 8 == 0 && cdiv(M, 256) * cdiv(N, 256) >= 192;
     return !pp_fills && cdiv(M, 128) * cdiv(N, 128) <= 1536 && !write_bound_unaligned(M, N, K);
