@@ -108,3 +108,30 @@ def test_model_plans_are_valid(L):
         assert not (names[c].startswith("pp") and N % 8)
         ws = L.fp8_scaled_mm_workspace_size(M, N, K, 0, 1, -1, 0)
         assert (ws == 0) == (s == 1)
+
+
+def test_plans_from_several_host_threads_agree(L):
+    """The plan memo is per thread: calls from several threads at once (ctypes
+    releases the GIL around each call) give the single-thread answers."""
+    import threading
+    shapes = _shapes(400, 5)
+    want = [(L.fp8_scaled_mm_select_config(M, N, K, 1, 0, 1),
+             L.fp8_scaled_mm_select_splits(M, N, K, 1, 0, -1)) for M, N, K in shapes]
+    errors = []
+
+    def worker(offset):
+        for r in range(3):
+            for i in range(len(shapes)):
+                j = (i * 7 + offset + r) % len(shapes)
+                M, N, K = shapes[j]
+                got = (L.fp8_scaled_mm_select_config(M, N, K, 1, 0, 1),
+                       L.fp8_scaled_mm_select_splits(M, N, K, 1, 0, -1))
+                if got != want[j]:
+                    errors.append((shapes[j], got, want[j]))
+
+    threads = [threading.Thread(target=worker, args=(k,)) for k in range(6)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors[:3]
