@@ -2,7 +2,6 @@
 states it: the coefficient tables in csrc/plan_cost_table.h, the features of
 plan_fit.features and the candidate plans of plan_fit.Table.candidates, on
 random shapes of the grids the model covers.  No GPU needed."""
-import os
 import re
 
 import numpy as np
