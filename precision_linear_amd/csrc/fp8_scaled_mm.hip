@@ -183,7 +183,7 @@ int choose_config_nosplit(int64_t M, int64_t N, int64_t K) {
 // plan_fit.py): a linear function, per configuration, of the features below.
 // Two coefficient tables: M <= 128 (fitted on launches whose operands come
 // from HBM, as a decode step's weights do) and M > 128 (operands left in the
-// caches).  On held-out shapes the chosen plan ran within 1.4% of the
+// caches).  On held-out shapes the chosen plan ran within 1.2-1.4% of the
 // fastest measured one (geometric mean), where the fixed rules alone were
 // 14-17% off.
 static_assert(sizeof(kPlanCost_streamed) / sizeof(PlanCostRow) == kNumConfigs &&
@@ -205,7 +205,8 @@ int64_t normalised_splits(int64_t s, int64_t k_iters) {
 // Predicted time (us) of configuration cfg with s splits: T tiles, U = T * s
 // units, S = 256 * occupancy workgroup slots, R = ceil(U / S) rounds of
 // units per slot, Lc = ceil(U / 256) units per CU, kk K slices per unit, act
-// = min(U, S) / S the busy fraction of the slots, a = BM * BN / 16384.
+// = min(U, S) / S the busy fraction of the slots, a = BM * BN / 16384, and
+// Lc - U / 256 the busiest CUs' extra load.
 double plan_cost(const PlanCostRow& row, const ConfigInfo& c, int64_t M, int64_t N, int64_t K,
                  int64_t s) {
     const int64_t S = 256 * (int64_t)c.occupancy;
@@ -221,7 +222,7 @@ double plan_cost(const PlanCostRow& row, const ConfigInfo& c, int64_t M, int64_t
         1.0, (double)(R * kk), (double)(R * kk) * act, (double)R, sp, sp * (double)s * a,
         sp * (double)R * a, sp * (double)T * (double)s * (double)c.bm * (double)c.bn / 1e6,
         (double)((M + N) * K) / 1e6, sp * (double)s * (double)R * a, (double)(Lc * kk), (double)Lc,
-        (double)(Lc * kk) * act};
+        (double)(Lc * kk) * act, ((double)Lc - (double)U / 256.0) * (double)kk};
     double t = 0.0;
     for (int i = 0; i < kPlanFeatures; ++i) t += row.c[i] * f[i];
     return t;

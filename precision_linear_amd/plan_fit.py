@@ -30,7 +30,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 HEADER = os.path.join(HERE, "csrc", "plan_cost_table.h")
 CUS = 256                  # MI355X compute units; the slot counts below assume it
 FEATURES = ["1", "R*kk", "R*kk*act", "R", "split", "split*s*a", "split*R*a",
-            "split*T*s*BM*BN/1e6", "(M+N)*K/1e6", "split*s*R*a", "Lc*kk", "Lc", "Lc*kk*act"]
+            "split*T*s*BM*BN/1e6", "(M+N)*K/1e6", "split*s*R*a", "Lc*kk", "Lc", "Lc*kk*act",
+            "(Lc-U/256)*kk"]
 MIN_ROWS = 60              # a configuration with fewer measurements in a regime is not used
 SPLIT_CANDIDATES = list(range(2, 17)) + [24, 32]
 
@@ -51,7 +52,9 @@ def features(bm, bn, bk, occ, M, N, K, s):
     T tiles, U = T * s units, S = CUS * occ workgroup slots, R = ceil(U / S)
     rounds of units per slot, Lc = ceil(U / CUS) units per CU, kk K slices
     per unit, act = min(U, S) / S the busy fraction of the slots, a = BM * BN
-    / 16384 the partial tile's size in 128 x 128 tiles."""
+    / 16384 the partial tile's size in 128 x 128 tiles; Lc - U / CUS is the
+    busiest CUs' extra load (a third unit on a few CUs of a grid of just
+    over two units per CU costs the whole launch a unit's time)."""
     S = CUS * occ
     T = cdiv(M, bm) * cdiv(N, bn)
     U = T * s
@@ -63,7 +66,7 @@ def features(bm, bn, bk, occ, M, N, K, s):
     sp = 1.0 if s > 1 else 0.0
     a = bm * bn / 16384
     return [1.0, R * kk, R * kk * act, R, sp, sp * s * a, sp * R * a, sp * T * s * bm * bn / 1e6,
-            (M + N) * K / 1e6, sp * s * R * a, Lc * kk, Lc, Lc * kk * act]
+            (M + N) * K / 1e6, sp * s * R * a, Lc * kk, Lc, Lc * kk * act, (Lc - U / CUS) * kk]
 
 
 def tile_dims(name):

@@ -304,7 +304,7 @@ PLANS = {
     (128, 3584, 8192): ("bm128_bn64_bk256_w4x2_s3_mfma16", 4),
     (16, 1024, 28672): ("bm16_bn32_bk512_w1x2_s6_mfma16", 8),
     (64, 1024, 28672): ("bm64_bn32_bk256_w4x2_s4_mfma16", 8),
-    (128, 1024, 28672): ("bm128_bn32_bk256_w4x2_s3_mfma16", 8),
+    (128, 1024, 28672): ("bm64_bn64_bk256_w1x4_s4_mfma16", 8),
     (512, 12288, 3072): ("bm128_bn128_bk128_w2x2_s2_mfma32", 1),
     (512, 3072, 12288): ("bm128_bn128_bk128_w2x4_s4_mfma32", 2),
     (1152, 3072, 12288): ("bm128_bn128_bk128_w2x4_s4_mfma32", 1),
