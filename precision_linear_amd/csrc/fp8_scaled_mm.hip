@@ -171,6 +171,10 @@ int choose_config_nosplit(int64_t M, int64_t N, int64_t K) {
 }
 
 // ---------------------------------------------------------- plan model ---
+
+static_assert(sizeof(kPlanCost_streamed) / sizeof(PlanCostRow) == kNumConfigs &&
+                  sizeof(kPlanCost_resident) / sizeof(PlanCostRow) == kNumConfigs,
+              "plan cost tables need one row per configuration (re-run plan_fit.py)");
 //
 // Grids that the 256 x 256 tiles fill (at least 192 of them, N % 8 == 0) or
 // that have more than 1536 tiles of 128 x 128 take the fixed rules above.
@@ -186,10 +190,6 @@ int choose_config_nosplit(int64_t M, int64_t N, int64_t K) {
 // caches).  On held-out shapes the chosen plan ran within 1.2-1.4% of the
 // fastest measured one (geometric mean), where the fixed rules alone were
 // 14-17% off.
-static_assert(sizeof(kPlanCost_streamed) / sizeof(PlanCostRow) == kNumConfigs &&
-                  sizeof(kPlanCost_resident) / sizeof(PlanCostRow) == kNumConfigs,
-              "plan cost tables need one row per configuration (re-run plan_fit.py)");
-
 bool plan_modelled(int64_t M, int64_t N, int64_t K) {
     const bool pp_fills = N % 8 == 0 && cdiv(M, 256) * cdiv(N, 256) >= 192;
     return !pp_fills && cdiv(M, 128) * cdiv(N, 128) <= 1536 && !write_bound_unaligned(M, N, K);
