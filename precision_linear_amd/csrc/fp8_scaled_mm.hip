@@ -175,7 +175,7 @@ int choose_config_nosplit(int64_t M, int64_t N, int64_t K) {
 static_assert(sizeof(kPlanCost_streamed) / sizeof(PlanCostRow) == kNumConfigs &&
                   sizeof(kPlanCost_resident) / sizeof(PlanCostRow) == kNumConfigs,
               "plan cost tables need one row per configuration (re-run plan_fit.py)");
-//
+
 // Grids that the 256 x 256 tiles fill (at least 192 of them, N % 8 == 0) or
 // that have more than 1536 tiles of 128 x 128 take the fixed rules above.
 // So do grids whose K is one slice and whose rows are not 16-byte aligned
