@@ -134,3 +134,23 @@ def test_plans_from_several_host_threads_agree(L):
     for t in threads:
         t.join()
     assert not errors, errors[:3]
+
+
+def test_features_of_one_plan_by_hand():
+    """plan_fit.features on one plan, worked out by hand from the stated
+    definitions: 128 x 128 x 128 tiles two per CU (S = 512 slots), M = 1000,
+    N = 11008, K = 4096, 3 splits.  T = 8 * 86 = 688 tiles, U = 2064 units,
+    R = ceil(2064 / 512) = 5, k_iters = 32, kk = ceil(32 / 3) = 11,
+    act = 1, Lc = ceil(2064 / 256) = 9, a = 1."""
+    f = plan_fit.features(128, 128, 128, 2, 1000, 11008, 4096, 3)
+    want = [1.0, 5 * 11, 5 * 11 * 1.0, 5, 1.0, 3 * 1.0, 5 * 1.0, 688 * 3 * 128 * 128 / 1e6,
+            (1000 + 11008) * 4096 / 1e6, 3 * 5 * 1.0, 9 * 11, 9, 9 * 11 * 1.0,
+            (9 - 2064 / 256) * 11]
+    assert len(f) == len(plan_fit.FEATURES) == len(want)
+    assert f == pytest.approx(want, rel=1e-15, abs=0)
+    # unsplit, a partly busy grid: 16 x 64 tiles, M = 16, N = 3584, K = 8192
+    # (T = 56, U = 56, R = 1, kk = 32, act = 56 / 256, Lc = 1): no split terms
+    g = plan_fit.features(16, 64, 256, 1, 16, 3584, 8192, 1)
+    act = 56 / 256
+    assert g == pytest.approx([1.0, 32, 32 * act, 1, 0, 0, 0, 0, (16 + 3584) * 8192 / 1e6, 0,
+                               32, 1, 32 * act, (1 - 56 / 256) * 32], rel=1e-15, abs=0)
