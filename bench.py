@@ -40,7 +40,8 @@ The JSON line also carries
                 in TFLOP/s, operands resident (us_p50 from an event pair per
                 launch; us_batch per launch of 20 back to back, which leaves
                 out the few microseconds each event pair adds to a short
-                launch); the quantisers in HBM GB/s.
+                launch); the quantisers in HBM GB/s.  Each multiply names
+                the automatic plan it ran ("plan": configuration / splits).
 """
 import argparse
 import hashlib
@@ -145,6 +146,14 @@ class Problem:
                        "g_cols": bits(self.out.index_select(1, torch.from_numpy(cols).to(self.out.device)))}
 
 
+def plan_of(w):
+    """The automatic plan the binding runs for a workload: "configuration
+    name / split count" (the binding supplies a workspace, so K may split)."""
+    from precision_linear_amd import binding
+    c = binding.select_config(w.M, w.N, w.K, w.mode, w.bias, True)
+    return f"{binding.config_names()[c]} / {binding.select_splits(w.M, w.N, w.K, w.mode, w.bias)}"
+
+
 def evict_caches(flush):
     """Read a buffer larger than the 256 MB MALL, so that the next launch finds
     none of its operands in the caches.  (Reading, not writing: dirty lines
@@ -229,7 +238,8 @@ def skinny_results(dev, reps=20, keep=None):
         res.append({"workload": name, "M": p.w.M, "N": p.w.N, "K": p.w.K,
                     "us_p50": round(t50 * 1e6, 2), "hbm_gbs": round(gbs, 1),
                     "frac_hbm": round(gbs / PEAK_HBM_GBS, 4),
-                    "tflops": round(p.w.flops / t50 / 1e12, 1), "inputs_sha256": p.inp.sha256()})
+                    "tflops": round(p.w.flops / t50 / 1e12, 1), "plan": plan_of(p.w),
+                    "inputs_sha256": p.inp.sha256()})
         if keep is not None:
             keep.append((name, p.inp, p.sample))
         del p
@@ -265,7 +275,7 @@ def resident_results(dev, names, reps=20, keep=None):
                     "frac_roofline": round(max(t_mfma, t_hbm) / t50, 4),
                     "us_batch": round(tb * 1e6, 2),
                     "frac_roofline_batch": round(max(t_mfma, t_hbm) / tb, 4),
-                    "inputs_sha256": p.inp.sha256()})
+                    "plan": plan_of(p.w), "inputs_sha256": p.inp.sha256()})
         if keep is not None:
             keep.append((name, p.inp, p.sample))
         del p
