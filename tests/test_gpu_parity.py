@@ -437,6 +437,22 @@ def test_split_k_more_splits_than_slices():
     assert compare(got, ref)[0] == 0
 
 
+@pytest.mark.parametrize("config,splits", [("bm16_bn32_bk512_w1x2_s6_mfma16", 32),
+                                           ("bm16_bn64_bk256_w1x4_s4_mfma16", 24),
+                                           ("bm64_bn32_bk256_w4x2_s4_mfma16", 16),
+                                           ("bm128_bn128_bk128_w2x4_s4_mfma32", 32),
+                                           ("bm128_bn128_bk128_w2x2_s2_mfma32", 24)])
+@pytest.mark.parametrize("mode", [PT, RW])
+def test_split_k_many_splits(config, splits, mode):
+    # The automatic plan splits up to 32 ways: K = 16400 (33 slices of 512,
+    # 65 of 256, 129 of 128, the last one ragged), so units have 1-6 slices
+    # and the last unit of a tile sums up to 32 partials in split order.
+    inp = wl.make_inputs(40, 200, 16400, mode, "codes", bias=mode == RW, key=splits + 5 * mode)
+    got = out_bits(run_gpu_plan(inp, _cfg(config), splits))
+    nbad, worst, first = compare(got, ref_mm(inp))
+    assert nbad == 0, (nbad, worst, first)
+
+
 def test_split_k_deterministic_and_workspace_equivalent():
     inp = wl.make_inputs(128, 512, 8192, RW, "normal", bias=True, key=11)
     cfg = _cfg("bm128_bn128_bk128_w2x2_s2_mfma32")
