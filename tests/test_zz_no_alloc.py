@@ -92,3 +92,29 @@ def test_noalloc_plan_beyond_the_scratch_is_refused():
     st = L.fp8_scaled_mm_noalloc(P, P, P, P, None, P, 8192, 8192, 8192, 0, None, pp, 3)
     assert st == binding.ERR_SCRATCH
     assert "scratch" in binding.status_string(st)
+
+
+def test_noalloc_automatic_plan_shrinks_to_the_scratch():
+    # 2048 x 4096 x 14336: the automatic plan is 256 x 256 tiles with 2
+    # splits, whose counters and partial tiles (64 MiB + 256 KiB) do not fit
+    # the 64 MiB scratch, so the no-alloc call runs the same tiles unsplit:
+    # bit-identical to the workspace form with splits = 1, and within the
+    # oracle's tolerance.
+    L = binding.lib()
+    M, N, K = 2048, 4096, 14336
+    pp = binding.config_names().index("pp_bm256_bn256_bk128_w8_mfma16")
+    assert binding.select_config(M, N, K, RW, False) == pp
+    assert binding.select_splits(M, N, K, RW) == 2
+    assert binding.workspace_size(M, N, K, RW) > 64 << 20
+    inp = wl.make_inputs(M, N, K, RW, "normal", key=577)
+    print(f"[noalloc] automatic plan beyond the scratch: shape={inp.shape}", flush=True)
+    args = _args(inp)
+    out_n = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+    out_w = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+    assert _noalloc(L, args, out_n, inp, -1, 0) == binding.OK
+    st, _ = _with_plan(L, args, out_w, inp, pp, 1)
+    assert st == binding.OK
+    torch.cuda.synchronize()
+    assert torch.equal(out_n.view(torch.int16), out_w.view(torch.int16))
+    nbad, worst, first = compare(out_bits(out_n), ref_mm(inp))
+    assert nbad == 0, (nbad, worst, first)
