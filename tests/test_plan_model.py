@@ -154,3 +154,13 @@ def test_features_of_one_plan_by_hand():
     act = 56 / 256
     assert g == pytest.approx([1.0, 32, 32 * act, 1, 0, 0, 0, 0, (16 + 3584) * 8192 / 1e6, 0,
                                32, 1, 32 * act, (1 - 56 / 256) * 32], rel=1e-15, abs=0)
+
+
+def test_sweep_draws_are_seeded_and_inside_the_modelled_sizes():
+    from precision_linear_amd import plan_sweep
+    a = plan_sweep.sample_shapes(2024, 50)
+    assert a == plan_sweep.sample_shapes(2024, 50) and len(a) == 50
+    assert a != plan_sweep.sample_shapes(77, 50)
+    for M, N, K in a:
+        assert M in plan_sweep.M_GRID and N in plan_sweep.N_GRID and K in plan_sweep.K_GRID
+        assert M * N <= 16_000_000 and M * N * K <= 6e10
