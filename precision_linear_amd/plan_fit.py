@@ -201,7 +201,7 @@ def cross_validate(hdr, rows, folds=5, can_split=True):
     return math.exp(float(np.mean(np.log(ratios)))), max(ratios)
 
 
-def emit(tables, path=HEADER):
+def emit(tables, sources, path=HEADER):
     names = tables["resident"].names
     lines = [
         "// Plan cost model of the automatic plan: per tile configuration, the",
@@ -209,6 +209,11 @@ def emit(tables, path=HEADER):
         "// the plan's features (plan_fit.py: features()), for operands streamed from",
         "// HBM (M <= 128) and left in the caches (M > 128).  Fitted on MI355X by",
         "// plan_fit.py from plan_sweep.py measurements; written by plan_fit.py.",
+    ]
+    for regime in ("streamed", "resident"):
+        n, files = sources[regime]
+        lines.append(f"// {regime}: {n} shapes from " + ", ".join(files))
+    lines += [
         "#pragma once",
         "",
         f"constexpr int kPlanFeatures = {len(FEATURES)};",
@@ -245,7 +250,7 @@ def main(argv):
     for a in argv:
         regime, _, path = a.partition(":")
         groups[regime].append(path)
-    tables = {}
+    tables, sources = {}, {}
     for regime, paths in groups.items():
         hdr, rows = load(paths)
         rows = [d for d in rows if (d["shape"][0] <= 128) == (regime == "streamed")]
@@ -257,7 +262,8 @@ def main(argv):
               f"plan in use when measured: geomean "
               f"{math.exp(float(np.mean(np.log(auto)))):.3f}, worst {max(auto):.2f}")
         tables[regime] = Table(hdr).fit(rows)
-    emit(tables)
+        sources[regime] = (len(rows), [os.path.basename(p) for p in paths])
+    emit(tables, sources)
     print(HEADER)
 
 
