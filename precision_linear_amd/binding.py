@@ -189,6 +189,25 @@ def _same_device(ref: torch.Tensor, **tensors) -> None:
             raise ValueError(f"{name} is on {t.device}, expected {ref.device}")
 
 
+def _check_devices(dev: int, tensors) -> None:
+    """_same_device for a (name, tensor) sequence against device index dev,
+    comparing indices (a CPU tensor's is -1)."""
+    for name, t in tensors:
+        if t is not None and t.get_device() != dev:
+            raise ValueError(f"{name} is on {t.device}, expected cuda:{dev}")
+
+
+# The current stream's raw handle for a device index: torch's direct accessor
+# where it has one (no Stream object built per call), else the public API.
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
+def _stream_of(dev: int) -> int:
+    if _raw_stream is not None:
+        return _raw_stream(dev)
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
 # Workspace bytes of automatic plans, per (device, M, N, K, mode, bias, config,
 # splits): the plan depends on nothing else, so the size is asked once.
 _ws_sizes: dict = {}
@@ -228,7 +247,9 @@ def fp8_scaled_mm(a: torch.Tensor, b: torch.Tensor, scale_a: torch.Tensor, scale
         raise ValueError("a must be contiguous (row-major M x K)")
     if not (a.is_cuda and b.is_cuda and scale_a.is_cuda and scale_b.is_cuda):
         raise ValueError("all tensors must be on the GPU")
-    _same_device(a, b=b, scale_a=scale_a, scale_b=scale_b, bias=bias, out=out, workspace=workspace)
+    dev = a.get_device()
+    _check_devices(dev, (("b", b), ("scale_a", scale_a), ("scale_b", scale_b), ("bias", bias),
+                         ("out", out), ("workspace", workspace)))
     for name, s in (("scale_a", scale_a), ("scale_b", scale_b)):
         if s.dtype != torch.float32 or not s.is_contiguous():
             raise ValueError(f"{name} must be contiguous float32")
@@ -239,13 +260,12 @@ def fp8_scaled_mm(a: torch.Tensor, b: torch.Tensor, scale_a: torch.Tensor, scale
     if bias is not None:
         if bias.dtype != torch.bfloat16 or bias.numel() != N or not bias.is_contiguous():
             raise ValueError("bias must be a contiguous bf16 GPU vector of length N")
-    dev = a.get_device()
     if out is None:
         out = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
     elif out.dtype != torch.bfloat16 or out.shape != (M, N) or not out.is_contiguous():
         raise ValueError("out must be a contiguous bf16 M x N tensor")
     L = lib()
-    stream = torch.cuda.current_stream(dev).cuda_stream
+    stream = _stream_of(dev)
     # The library launches on the current HIP device: make it a's (calls
     # from that device, the usual case, skip the switch).
     switch = torch.cuda.current_device() != dev
