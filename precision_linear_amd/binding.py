@@ -181,17 +181,10 @@ def _as_codes(t: torch.Tensor, name: str, fmt) -> tuple:
     raise ValueError(f"{name} must be float8_e4m3fn, float8_e5m2 or uint8 codes, got {dt}")
 
 
-def _same_device(ref: torch.Tensor, **tensors) -> None:
-    """Every given tensor (None skipped) must live on ref's GPU: the library
-    passes their pointers to kernels on that device."""
-    for name, t in tensors.items():
-        if t is not None and t.device != ref.device:
-            raise ValueError(f"{name} is on {t.device}, expected {ref.device}")
-
-
 def _check_devices(dev: int, tensors) -> None:
-    """_same_device for a (name, tensor) sequence against device index dev,
-    comparing indices (a CPU tensor's is -1)."""
+    """Every (name, tensor) given (None skipped) must live on GPU `dev`: the
+    library passes their pointers to kernels on that device.  Compares
+    device indices (a CPU tensor's is -1)."""
     for name, t in tensors:
         if t is not None and t.get_device() != dev:
             raise ValueError(f"{name} is on {t.device}, expected cuda:{dev}")
@@ -317,7 +310,8 @@ def fp8_quantize(x: torch.Tensor, mode="rowwise", q: torch.Tensor | None = None,
         raise ValueError("x must be a contiguous 2-D bf16 GPU tensor")
     rows, cols = x.shape
     n_scale = 1 if m == PER_TENSOR else rows
-    _same_device(x, q=q, scale=scale)
+    dev = x.get_device()
+    _check_devices(dev, (("q", q), ("scale", scale)))
     if q is None:
         q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
     elif q.dtype not in (torch.uint8, torch.float8_e4m3fn if f == E4M3FN else torch.float8_e5m2) \
@@ -327,8 +321,8 @@ def fp8_quantize(x: torch.Tensor, mode="rowwise", q: torch.Tensor | None = None,
         scale = torch.empty(n_scale, dtype=torch.float32, device=x.device)
     elif scale.dtype != torch.float32 or scale.numel() != n_scale or not scale.is_contiguous():
         raise ValueError(f"scale must be a contiguous float32 tensor of {n_scale} elements")
-    stream = torch.cuda.current_stream(x.device).cuda_stream
-    with torch.cuda.device(x.device):
+    stream = _stream_of(dev)
+    with torch.cuda.device(dev) if torch.cuda.current_device() != dev else contextlib.nullcontext():
         need = int(lib().fp8_quantize_workspace_size(rows, cols, m)) if workspace else 0
         ws = _workspace(x.device, stream, need, "quantize") if need > 0 else None
         st = getattr(lib(), fn_name)(x.data_ptr() if x.numel() else None,
